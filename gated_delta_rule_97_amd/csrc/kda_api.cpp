@@ -1,0 +1,312 @@
+// C ABI of the KDA library: host-side validation, workspace carve-up,
+// dispatch to the gfx950 kernels, and launch timing.  No device memory is
+// ever allocated here; every buffer belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, size_t elem_bytes) {
+    PrefillLayout L;
+    const size_t slots = size_t(nc_max) * size_t(H);
+    size_t off = 0;
+    L.coff = off;
+    off = align_up(off + sizeof(int32_t) * size_t(N + 1), 256);
+    L.W = off;
+    off = align_up(off + slots * C * dk * elem_bytes, 256);
+    L.Qp = off;
+    off = align_up(off + slots * C * dk * elem_bytes, 256);
+    L.KtT = off;
+    off = align_up(off + slots * C * dk * elem_bytes, 256);
+    L.Ut = off;
+    off = align_up(off + slots * C * dv * elem_bytes, 256);
+    L.Oi = off;
+    off = align_up(off + slots * C * dv * elem_bytes, 256);
+    L.D = off;
+    off = align_up(off + slots * dk * sizeof(float), 256);
+    L.total = off;
+    return L;
+}
+
+bool prefill_supported(int dtype, int dk, int dv, int C) {
+    auto okd = [](int d) { return d == 32 || d == 64 || d == 128; };
+    if (!okd(dk) || !okd(dv) || (C != 16 && C != 64)) return false;
+    if (dtype == KDA_DTYPE_F32 && C == 64 && (dk > 64 || dv > 64)) return false;
+    return dtype == KDA_DTYPE_F32 || dtype == KDA_DTYPE_BF16;
+}
+
+// ------------------------------------------------------------------ timing
+namespace {
+struct ProfRec {
+    hipEvent_t start, stop;
+    std::string name;
+};
+struct Profiler {
+    bool active = false;
+    int cap = 0;
+    int used = 0;
+    std::vector<hipEvent_t> evs;  // 2 * cap events, created up front
+    std::vector<std::string> names;
+} g_prof;
+}  // namespace
+
+void prof_begin(hipStream_t s) {
+    if (!g_prof.active || g_prof.used >= g_prof.cap) return;
+    (void)hipEventRecord(g_prof.evs[2 * g_prof.used], s);
+}
+
+void prof_end(hipStream_t s, const char *name) {
+    if (!g_prof.active || g_prof.used >= g_prof.cap) return;
+    (void)hipEventRecord(g_prof.evs[2 * g_prof.used + 1], s);
+    g_prof.names[g_prof.used] = name;
+    ++g_prof.used;
+}
+
+}  // namespace kda
+
+using namespace kda;
+
+static bool misaligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+static bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+static size_t dtype_bytes(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
+
+extern "C" {
+
+const char *kda_status_string(int status) {
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "unsupported dk/dv/chunk/dtype combination";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case KDA_ERR_ALIAS: return "buffers overlap in a way that is not allowed";
+    case KDA_ERR_LAUNCH: return "the HIP runtime reported an error";
+    case KDA_ERR_DECAY_BOUND: return "a log-decay value is outside [-5, 0]";
+    default: return "unknown status";
+    }
+}
+
+// Shared shape checks; fills nc_max and N (number of sequences).
+static int prefill_shape(int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size, kda_dtype dt,
+                         bool packed, int *nc_max, int *N) {
+    if (dt != KDA_DTYPE_F32 && dt != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+    if (!prefill_supported(dt, dk, dv, chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (packed) {
+        if (B != 1) return KDA_ERR_SHAPE;
+        *N = num_seqs;
+        const int64_t slots = (int64_t(T) + chunk_size - 1) / chunk_size + num_seqs;
+        if (slots > INT32_MAX / 2) return KDA_ERR_SHAPE;
+        *nc_max = int(slots);
+    } else {
+        if (num_seqs != B) return KDA_ERR_SHAPE;
+        *N = B;
+        const int64_t slots = int64_t(B) * ((int64_t(T) + chunk_size - 1) / chunk_size);
+        if (slots > INT32_MAX / 2) return KDA_ERR_SHAPE;
+        *nc_max = int(slots);
+    }
+    // element offsets are computed in 64 bits; per-dimension products in 32
+    if (int64_t(B) * T * H > INT32_MAX || int64_t(*N) * H > INT32_MAX) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                                     kda_dtype dtype, size_t *bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    // the size must not depend on whether cu_seqlens is given: take the
+    // larger of the two slot counts
+    int nc_a = 0, nc_b = 0, N = 0, st;
+    if (B == 1) {
+        st = prefill_shape(B, T, H, dk, dv, num_seqs, chunk_size, dtype, true, &nc_a, &N);
+        if (st != KDA_OK) return st;
+    }
+    if (num_seqs == B) {
+        st = prefill_shape(B, T, H, dk, dv, num_seqs, chunk_size, dtype, false, &nc_b, &N);
+        if (st != KDA_OK) return st;
+    } else if (B != 1) {
+        return KDA_ERR_SHAPE;
+    }
+    const int nc = std::max(nc_a, nc_b);
+    *bytes = prefill_layout(nc, H, num_seqs, dk, dv, chunk_size, dtype_bytes(dtype)).total;
+    return KDA_OK;
+}
+
+int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const float *h0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                      int num_seqs, int chunk_size, kda_dtype dtype, unsigned flags, void *o, float *ht,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const bool packed = cu_seqlens != nullptr;
+    int nc_max = 0, N = 0;
+    int st = prefill_shape(B, T, H, dk, dv, num_seqs, chunk_size, dtype, packed, &nc_max, &N);
+    if (st != KDA_OK) return st;
+    const size_t rows = size_t(B) * size_t(T);
+    const size_t eb = dtype_bytes(dtype);
+    const bool any_tokens = rows > 0;
+    if (any_tokens && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (!workspace && N > 0) return KDA_ERR_WORKSPACE;
+
+    size_t need = 0;
+    st = kda_chunk_prefill_workspace_size(B, T, H, dk, dv, num_seqs, chunk_size, dtype, &need);
+    if (st != KDA_OK) return st;
+    if (N > 0 && workspace_bytes < need) return KDA_ERR_WORKSPACE;
+
+    for (const void *p : {q, k, v, (const void *)g, (const void *)beta, (const void *)h0, (const void *)o,
+                          (const void *)ht, (const void *)cu_seqlens})
+        if (misaligned(p, 16)) return KDA_ERR_ALIGN;
+    if (misaligned(workspace, 256)) return KDA_ERR_ALIGN;
+
+    const size_t nq = rows * H * dk * eb, nv = rows * H * dv * eb, ng = rows * H * dk * 4, nb = rows * H * 4;
+    const size_t ns = size_t(N) * H * dk * dv * 4;
+    const size_t ncu = packed ? sizeof(int32_t) * size_t(N + 1) : 0;
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {g, ng}, {beta, nb}, {h0, ns}, {cu_seqlens, ncu}};
+    const Buf outs[] = {{o, nv}, {ht, ns}, {workspace, need}};
+    for (int i = 0; i < 3; ++i) {
+        for (const Buf &b : ins) {
+            if (i == 1 && b.p == h0) {  // ht == h0 exactly is an in-place resume
+                if (ht && h0 && ht != h0 && overlap(ht, ns, h0, ns)) return KDA_ERR_ALIAS;
+                continue;
+            }
+            if (overlap(outs[i].p, outs[i].n, b.p, b.n)) return KDA_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return KDA_ERR_ALIAS;
+    }
+
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        unsigned flag = 0;
+        if (run_checks(g, rows * H * dk, cu_seqlens, N, T, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (flag & 2u) return KDA_ERR_SHAPE;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    if (N == 0) return KDA_OK;
+
+    const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0;
+    a.cu = cu_seqlens;
+    a.coff = reinterpret_cast<int32_t *>(ws + L.coff);
+    a.T = T; a.H = H; a.N = N;
+    a.nc_max = nc_max;
+    a.nc_seq = (T + chunk_size - 1) / chunk_size;
+    a.o = o; a.ht = ht;
+    a.W = ws + L.W; a.Qp = ws + L.Qp; a.KtT = ws + L.KtT; a.Ut = ws + L.Ut; a.Oi = ws + L.Oi;
+    a.D = reinterpret_cast<float *>(ws + L.D);
+
+    if (!any_tokens) a.nc_max = 0;  // only the state copy h0 -> ht remains
+    if (packed && a.nc_max > 0) {
+        if (launch_chunk_offsets(cu_seqlens, N, T, chunk_size, nc_max, a.coff, stream) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+    }
+    if (packed && a.nc_max == 0) {
+        // no tokens at all: every sequence is empty; the state kernel still
+        // runs (with zero chunks) to write ht = h0
+        a.cu = nullptr;
+        a.nc_seq = 0;
+        a.T = 0;
+    }
+    // value-column block: narrow blocks when few (sequence, head) chains
+    // would leave compute units idle
+    const int bv = (int64_t(N) * H * (dv / 32) < 512) ? 16 : 32;
+    hipError_t e = (dtype == KDA_DTYPE_BF16) ? launch_prefill_bf16(a, dk, dv, chunk_size, bv, stream)
+                                             : launch_prefill_f32(a, dk, dv, chunk_size, bv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    float *state, void *o, int N, int H, int dk, int dv, kda_dtype dtype, unsigned flags,
+                    hipStream_t stream) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
+    auto okd = [](int d) { return d == 32 || d == 64 || d == 128; };
+    if (!okd(dk) || !okd(dv)) return KDA_ERR_UNSUPPORTED;
+    if (int64_t(N) * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    for (const void *p : {q, k, v, (const void *)g, (const void *)beta, (const void *)state, (const void *)o})
+        if (misaligned(p, 16)) return KDA_ERR_ALIGN;
+    const size_t nh = size_t(N) * H, eb = dtype_bytes(dtype);
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{q, nh * dk * eb}, {k, nh * dk * eb}, {v, nh * dv * eb}, {g, nh * dk * 4}, {beta, nh * 4}};
+    const size_t nstate = nh * dk * dv * 4, no = nh * dv * eb;
+    for (const Buf &b : ins) {
+        if (overlap(state, nstate, b.p, b.n) || overlap(o, no, b.p, b.n)) return KDA_ERR_ALIAS;
+    }
+    if (overlap(state, nstate, o, no)) return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        unsigned flag = 0;
+        if (run_checks(g, nh * dk, nullptr, 0, 0, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    hipError_t e = launch_decode(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, N, H, dk, dv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_profile_start(int max_launches) {
+    if (max_launches <= 0) return KDA_ERR_SHAPE;
+    if (g_prof.active) return KDA_ERR_SHAPE;
+    for (hipEvent_t e : g_prof.evs) (void)hipEventDestroy(e);
+    g_prof.evs.assign(2 * size_t(max_launches), nullptr);
+    for (auto &e : g_prof.evs)
+        if (hipEventCreate(&e) != hipSuccess) return KDA_ERR_LAUNCH;
+    g_prof.names.assign(size_t(max_launches), std::string());
+    g_prof.cap = max_launches;
+    g_prof.used = 0;
+    g_prof.active = true;
+    return KDA_OK;
+}
+
+int kda_profile_stop(kda_kernel_time *out, int max_entries, int *n_entries) {
+    if (!g_prof.active) return KDA_ERR_SHAPE;
+    g_prof.active = false;
+    std::vector<kda_kernel_time> agg;
+    int status = KDA_OK;
+    for (int i = 0; i < g_prof.used; ++i) {
+        if (hipEventSynchronize(g_prof.evs[2 * i + 1]) != hipSuccess) { status = KDA_ERR_LAUNCH; break; }
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_prof.evs[2 * i], g_prof.evs[2 * i + 1]) != hipSuccess) {
+            status = KDA_ERR_LAUNCH;
+            break;
+        }
+        auto it = std::find_if(agg.begin(), agg.end(),
+                               [&](const kda_kernel_time &t) { return g_prof.names[i] == t.name; });
+        if (it == agg.end()) {
+            kda_kernel_time t;
+            memset(&t, 0, sizeof(t));
+            strncpy(t.name, g_prof.names[i].c_str(), sizeof(t.name) - 1);
+            agg.push_back(t);
+            it = agg.end() - 1;
+        }
+        it->launches += 1;
+        it->total_ms += ms;
+    }
+    for (hipEvent_t e : g_prof.evs) (void)hipEventDestroy(e);
+    g_prof.evs.clear();
+    g_prof.used = 0;
+    g_prof.cap = 0;
+    const int n = std::min<int>(int(agg.size()), std::max(max_entries, 0));
+    for (int i = 0; i < n; ++i) out[i] = agg[i];
+    if (n_entries) *n_entries = int(agg.size());
+    return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Small support kernels: the packed-batch chunk map and the debug checks.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+// coff[n] = first chunk slot of sequence n = sum over m < n of
+// ceil(len_m / C), clamped to the workspace's nc_max slots.  Lengths come
+// from cu_seqlens clamped to [0, T], so malformed offsets can never produce
+// an out-of-range slot.  One workgroup; sequences in tiles of 1024.
+__global__ __launch_bounds__(1024) void kda_chunk_offsets_kernel(const int32_t *__restrict__ cu, int N, int T,
+                                                                 int C, int nc_max, int32_t *__restrict__ coff) {
+    __shared__ int32_t scan[1024];
+    __shared__ int32_t carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        carry = 0;
+        coff[0] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < N; base += 1024) {
+        const int n = base + tid;
+        int cnt = 0;
+        if (n < N) {
+            int s = cu[n], e = cu[n + 1];
+            s = s < 0 ? 0 : (s > T ? T : s);
+            e = e < s ? s : (e > T ? T : e);
+            cnt = (e - s + C - 1) / C;
+        }
+        scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int x = (tid >= off) ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += x;
+            __syncthreads();
+        }
+        if (n < N) coff[n + 1] = min(carry + scan[tid], nc_max);
+        __syncthreads();
+        if (tid == 1023) carry = min(carry + scan[1023], nc_max);
+        __syncthreads();
+    }
+}
+
+hipError_t launch_chunk_offsets(const int32_t *cu, int N, int T, int C, int nc_max, int32_t *coff,
+                                hipStream_t s) {
+    prof_begin(s);
+    hipLaunchKernelGGL(kda_chunk_offsets_kernel, dim3(1), dim3(1024), 0, s, cu, N, T, C, nc_max, coff);
+    prof_end(s, "kda_chunk_offsets");
+    return hipGetLastError();
+}
+
+// ---- debug checks (KDA_FLAG_CHECK_DECAY) ----
+__device__ unsigned int g_kda_check_flag;
+
+__global__ void kda_flag_reset_kernel() { g_kda_check_flag = 0u; }
+
+__global__ void kda_check_decay_kernel(const float *__restrict__ g, size_t n) {
+    unsigned bad = 0;
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = g[i];
+        if (!(x >= -5.f && x <= 0.f)) bad = 1u;  // NaN fails both comparisons
+    }
+    if (bad) atomicOr(&g_kda_check_flag, 1u);
+}
+
+__global__ void kda_check_cu_kernel(const int32_t *__restrict__ cu, int N, int T) {
+    unsigned bad = 0;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < N; i += gridDim.x * blockDim.x)
+        if (cu[i + 1] < cu[i]) bad = 2u;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (cu[0] != 0 || cu[N] != T)) bad = 2u;
+    if (bad) atomicOr(&g_kda_check_flag, bad);
+}
+
+hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N, int T, hipStream_t s,
+                      unsigned *flag_out) {
+    hipLaunchKernelGGL(kda_flag_reset_kernel, dim3(1), dim3(1), 0, s);
+    if (n > 0) {
+        size_t blocks = (n + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(kda_check_decay_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, g, n);
+    }
+    if (cu) {
+        const int blocks = N / 256 + 1 > 1024 ? 1024 : N / 256 + 1;
+        hipLaunchKernelGGL(kda_check_cu_kernel, dim3(blocks), dim3(256), 0, s, cu, N, T);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return e;
+    unsigned flag = 0;
+    e = hipMemcpyFromSymbol(&flag, HIP_SYMBOL(g_kda_check_flag), sizeof(flag), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    *flag_out = flag;
+    return hipSuccess;
+}
+
+}  // namespace kda

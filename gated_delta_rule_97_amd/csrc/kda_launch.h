@@ -1,0 +1,65 @@
+// Internal interface between the C ABI (kda_api.cpp) and the kernel
+// translation units.  Not installed; no torch or Python types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Everything the prefill kernels need, by value.
+struct PrefillArgs {
+    const void *q, *k, *v;     // [rows][H][dk|dv] in the compute dtype
+    const float *g, *beta;     // [rows][H][dk], [rows][H]
+    const float *h0;           // [N][H][dk][dv] or null
+    const int32_t *cu;         // packed sequence offsets [N+1] or null
+    int32_t *coff;             // per-sequence first chunk slot [N+1] (packed only)
+    int T;                     // tokens per sequence (fixed) or in total (packed)
+    int H, N;
+    int nc_max;                // chunk slots in the workspace
+    int nc_seq;                // chunks per sequence (fixed-length batches)
+    void *o;                   // [rows][H][dv]
+    float *ht;                 // [N][H][dk][dv] or null
+    // workspace, per (chunk slot, head):
+    void *W;                   // [C][dk]  WY factor  (I+A)^-1 (beta k e^Gam)
+    void *Qp;                  // [C][dk]  q e^Gam - P W
+    void *KtT;                 // [dk][C]  (k e^{Gam_last - Gam})^T
+    void *Ut;                  // [C][dv]  (I+A)^-1 (beta v)
+    void *Oi;                  // [C][dv]  P (I+A)^-1 (beta v)
+    float *D;                  // [dk]     e^{Gam_last}
+};
+
+// Workspace carve-up shared by the size query and the prefill call.
+struct PrefillLayout {
+    size_t coff, W, Qp, KtT, Ut, Oi, D, total;
+};
+PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
+                             size_t elem_bytes);
+
+// Launch-time profiling hooks (no-ops unless a profiling session is open).
+void prof_begin(hipStream_t s);
+void prof_end(hipStream_t s, const char *name);
+
+// Kernel launchers.  They return hipSuccess or the launch error.  Shapes have
+// been validated by the caller.
+hipError_t launch_chunk_offsets(const int32_t *cu, int N, int T, int C,
+                                int nc_max, int32_t *coff, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int dk, int dv, int C,
+                               int bv, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, int dk, int dv, int C,
+                              int bv, hipStream_t s);
+hipError_t launch_decode(int dtype, const void *q, const void *k,
+                         const void *v, const float *g, const float *beta,
+                         float *state, void *o, int N, int H, int dk, int dv,
+                         hipStream_t s);
+// Debug checks: set a device flag when g leaves [-5, 0] (bit 0) or when
+// cu_seqlens is malformed (bit 1), then read it back synchronously.
+hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N,
+                      int T, hipStream_t s, unsigned *flag_out);
+
+// Whether a dtype / size combination has kernels built (fp32 with chunk 64
+// needs dk, dv <= 64 to fit the intra-chunk kernel in LDS).
+bool prefill_supported(int dtype, int dk, int dv, int C);
+
+}  // namespace kda

@@ -1,0 +1,153 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * KDA is the gated delta rule with a per-channel decay (Kimi K3 architecture
+ * blog post: "Sequence" section -- three of every four layers keep a
+ * fixed-size recurrent state instead of rereading the prefix; section on the
+ * lower bound on the log-decay -- the state forgets as it goes, and computing
+ * it chunk by chunk divides by the accumulated decay).  For one head of one
+ * sequence, state S (dk x dv, fp32), per token t:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * Conventions for every entry point
+ *   - All device pointers are caller-owned; the library never allocates device
+ *     memory.  Work is enqueued on the caller's stream and the call returns
+ *     without waiting, except where a flag below says otherwise.
+ *   - Tensors are contiguous row-major with the shapes given below; every
+ *     pointer must be 16-byte aligned (the workspace 256-byte aligned).
+ *   - dk and dv are each one of 32, 64, 128.
+ *   - g is the natural-log decay per channel; the method requires
+ *     -5 <= g <= 0 (keep at least e^-5 = 0.67% per step, the blog post's
+ *     bound, so a 16-token tile's accumulated log-decay stays in [-80, 0]).
+ *     Values outside that range are undefined behaviour (they may overflow
+ *     to Inf/NaN) unless KDA_FLAG_CHECK_DECAY is set.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is launched and a negative status is returned.
+ *   - q, k, v and o share one dtype (kda_dtype); g, beta and the states are
+ *     always float32.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_dtype {
+    KDA_DTYPE_F32 = 0,  /* IEEE float32 */
+    KDA_DTYPE_BF16 = 1  /* bfloat16 (outputs rounded to nearest even) */
+} kda_dtype;
+
+enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL                     */
+    KDA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent         */
+    KDA_ERR_UNSUPPORTED = -3, /* dk/dv/chunk/dtype combination not built        */
+    KDA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required     */
+    KDA_ERR_ALIGN = -5,       /* a pointer is not suitably aligned              */
+    KDA_ERR_ALIAS = -6,       /* buffers overlap in a way that is not allowed   */
+    KDA_ERR_LAUNCH = -7,      /* the HIP runtime reported an error              */
+    KDA_ERR_DECAY_BOUND = -8  /* KDA_FLAG_CHECK_DECAY found g outside [-5, 0]   */
+};
+
+/* Debug flag: before computing, scan g on the device, synchronize the stream
+ * and return KDA_ERR_DECAY_BOUND (launching nothing else) if any g is
+ * outside [-5, 0] or NaN.  For a packed batch it also checks that cu_seqlens
+ * starts at 0, never decreases and ends at T (KDA_ERR_SHAPE otherwise).
+ * This breaks the no-host-sync rule on purpose. */
+#define KDA_FLAG_CHECK_DECAY 1u
+
+/* Bytes of device workspace kda_chunk_prefill needs for these sizes
+ * (written to *bytes).  Same arguments as kda_chunk_prefill.  The figure
+ * depends only on the sizes, never on the contents of cu_seqlens. */
+int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv,
+                                     int num_seqs, int chunk_size,
+                                     kda_dtype dtype, size_t *bytes);
+
+/*
+ * Chunked KDA prefill (the blog post's chunk-wise evaluation with the decay
+ * bound: every 16-token tile, the diagonal ones included, is an ordinary
+ * dense matrix product).
+ *
+ *   q, k       [B, T, H, dk]  dtype
+ *   v          [B, T, H, dv]  dtype
+ *   g          [B, T, H, dk]  float32, natural-log decay in [-5, 0]
+ *   beta       [B, T, H]      float32
+ *   h0         [N, H, dk, dv] float32 initial state per sequence, or NULL
+ *              for a zero start (prefix-cache resume: the serving-stack
+ *              section restores a cached recurrent state at a boundary)
+ *   cu_seqlens device int32 [N+1] or NULL.  NULL: N = B sequences of T
+ *              tokens each.  Non-NULL: packed variable-length batch, B must
+ *              be 1, sequence n owns rows [cu[n], cu[n+1]), cu[0] = 0 and
+ *              cu[N] = T.  Malformed contents give unspecified results but
+ *              never an out-of-bounds access (checked with the flag above).
+ *   num_seqs   N (B when cu_seqlens is NULL)
+ *   chunk_size 16 or 64 (a multiple of the 16-token tile); results are the
+ *              same up to rounding.  float32 with chunk 64 needs dk, dv <= 64.
+ *   o          [B, T, H, dv]  dtype, written
+ *   ht         [N, H, dk, dv] float32 final state per sequence, or NULL.
+ *              ht may be exactly h0 (in-place resume); partial overlap of ht
+ *              and h0, and any overlap of o/ht/workspace with an input or
+ *              with each other, is KDA_ERR_ALIAS.
+ *   workspace  device scratch of at least kda_chunk_prefill_workspace_size
+ *              bytes, 256-byte aligned; its contents on entry do not matter.
+ *              Two calls in flight on different streams need two workspaces.
+ *   stream     HIP stream the kernels are enqueued on.
+ * A sequence of length 0 gives ht = h0 (or zeros).
+ */
+int kda_chunk_prefill(const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, const float *h0,
+                      const int32_t *cu_seqlens, int B, int T, int H, int dk,
+                      int dv, int num_seqs, int chunk_size, kda_dtype dtype,
+                      unsigned flags, void *o, float *ht, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step for N independent sequences, one token each, updating the
+ * state in place (the serving-stack section: the recurrent state is updated
+ * in place).  Per (n, h): S' = Diag(exp(g)) S; u = beta (v - S'^T k);
+ * S = S' + k u^T; o = S^T q.  The state is read once and written once.
+ *
+ *   q, k  [N, H, dk] dtype      v [N, H, dv] dtype
+ *   g     [N, H, dk] float32    beta [N, H] float32
+ *   state [N, H, dk, dv] float32, read and overwritten
+ *   o     [N, H, dv] dtype, written; must not overlap any other argument
+ */
+int kda_decode_step(const void *q, const void *k, const void *v,
+                    const float *g, const float *beta, float *state, void *o,
+                    int N, int H, int dk, int dv, kda_dtype dtype,
+                    unsigned flags, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *kda_status_string(int status);
+
+/* ---------------------------------------------------------------------
+ * Launch timing (measurement plumbing).  Between kda_profile_start and
+ * kda_profile_stop every kernel the library enqueues is bracketed by a pair
+ * of HIP events recorded on the same stream (no host synchronisation).
+ * kda_profile_stop synchronizes on the recorded events and reports, per
+ * kernel name, the number of launches and their summed duration.  Launches
+ * beyond max_launches are not timed.  Not thread-safe; one session at a
+ * time per process.
+ * --------------------------------------------------------------------- */
+typedef struct kda_kernel_time {
+    char name[48];
+    int launches;
+    double total_ms;
+} kda_kernel_time;
+
+int kda_profile_start(int max_launches);
+int kda_profile_stop(kda_kernel_time *out, int max_entries, int *n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+No call here reaches a kernel (every case fails validation, or has N = 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_97_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+BF16, F32 = kda.KDA_DTYPE_BF16, kda.KDA_DTYPE_F32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"kda_chunk_prefill", "kda_decode_step", "kda_chunk_prefill_workspace_size",
+            "kda_status_string"} <= set(names)
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
+
+
+def test_status_strings():
+    for code in range(0, -9, -1):
+        s = kda.kda_status_string(code)
+        assert s and s != "unknown status"
+    assert kda.kda_status_string(-99) == "unknown status"
+
+
+def test_workspace_size():
+    w1 = kda.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 1, 64, BF16)
+    # W, Q', K~^T, Ut, Oi (bf16) + decay (fp32) per (chunk, head), plus the chunk map
+    slots = (8192 // 64 + 1) * 32
+    assert w1 >= slots * (5 * 64 * 128 * 2 + 128 * 4)
+    assert w1 % 256 == 0
+    w2 = kda.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64, 64, BF16)
+    assert w2 > w1
+    assert kda.kda_chunk_prefill_workspace_size(4, 100, 2, 32, 32, 4, 16, F32) > 0
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_workspace_size(1, 100, 2, 48, 32, 1, 64, BF16)
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_workspace_size(1, 100, 2, 128, 128, 1, 64, F32)
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_workspace_size(1, 100, 2, 64, 64, 1, 32, BF16)
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_workspace_size(2, 100, 2, 64, 64, 3, 64, BF16)
+    assert e.value.status == kda.KDA_ERR_SHAPE
+
+
+# fake, never-dereferenced device addresses (validation fails before use)
+A = 1 << 32
+
+
+def _prefill(**kw):
+    args = dict(q=A, k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24), h0=0,
+                cu_seqlens=0, B=1, T=64, H=2, dk=32, dv=32, num_seqs=1, chunk_size=16, dtype=F32,
+                flags=0, o=A + (5 << 24), ht=A + (6 << 24), workspace=A + (7 << 24), workspace_bytes=1 << 20,
+                stream=0)
+    args.update(kw)
+    return kda.kda_chunk_prefill(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk_size=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=7), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=128, chunk_size=64), kda.KDA_ERR_UNSUPPORTED),   # fp32 chunk 64 needs d <= 64
+    (dict(H=0), kda.KDA_ERR_SHAPE),
+    (dict(T=-1), kda.KDA_ERR_SHAPE),
+    (dict(num_seqs=2), kda.KDA_ERR_SHAPE),                            # N must equal B without cu_seqlens
+    (dict(B=2, num_seqs=2, cu_seqlens=A + (8 << 24)), kda.KDA_ERR_SHAPE),  # packed needs B = 1
+    (dict(q=0), kda.KDA_ERR_NULL),
+    (dict(g=0), kda.KDA_ERR_NULL),
+    (dict(o=0), kda.KDA_ERR_NULL),
+    (dict(workspace=0), kda.KDA_ERR_WORKSPACE),
+    (dict(workspace_bytes=1024), kda.KDA_ERR_WORKSPACE),
+    (dict(k=A + (1 << 24) + 8), kda.KDA_ERR_ALIGN),
+    (dict(workspace=A + (7 << 24) + 16), kda.KDA_ERR_ALIGN),
+    (dict(o=A + 256), kda.KDA_ERR_ALIAS),                             # o overlaps q
+    (dict(h0=A + (9 << 24), ht=A + (9 << 24) + 4096), kda.KDA_ERR_ALIAS),  # partial h0/ht overlap
+    (dict(workspace=A + (6 << 24)), kda.KDA_ERR_ALIAS),               # workspace overlaps ht
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+
+
+def test_prefill_nothing_to_do():
+    # no sequences: nothing is launched, nothing is touched
+    assert _prefill(B=0, num_seqs=0, T=0, q=0, k=0, v=0, g=0, beta=0, o=0, ht=0, workspace=0) == kda.KDA_OK
+
+
+def _decode(**kw):
+    args = dict(q=A, k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24),
+                state=A + (5 << 24), o=A + (6 << 24), N=4, H=2, dk=128, dv=128, dtype=BF16, flags=0, stream=0)
+    args.update(kw)
+    return kda.kda_decode_step(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=3), kda.KDA_ERR_UNSUPPORTED),
+    (dict(H=0), kda.KDA_ERR_SHAPE),
+    (dict(N=-1), kda.KDA_ERR_SHAPE),
+    (dict(state=0), kda.KDA_ERR_NULL),
+    (dict(o=A + (6 << 24) + 2), kda.KDA_ERR_ALIGN),
+    (dict(o=A + (5 << 24) + 1024), kda.KDA_ERR_ALIAS),                # o inside the state
+    (dict(state=A + 64), kda.KDA_ERR_ALIAS),                          # state overlaps q
+])
+def test_decode_validation(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_decode_empty_batch():
+    assert _decode(N=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK

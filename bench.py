@@ -1,0 +1,252 @@
+"""Benchmark: KDA chunked prefill (headline) and decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: prefill B=1, H=32, T=8192, dk=dv=128, bf16 q/k/v, fp32 g,
+beta and states, chunk 64, h0 ~ N(0, 0.02).  One step = one kda_chunk_prefill
+call over the whole batch (all of its kernels), inputs resident in HBM.
+value = tokens/s = B*T / (time per call).
+
+Also measured and reported in the same JSON line: decode (256 sequences x 32
+heads, d = 128, 128 consecutive in-place steps), per-kernel durations from
+HIP events recorded around every launch on the launch stream, roofline
+fractions against MI355X peaks (HBM 8 TB/s; bf16 MFMA 2.5 PFLOP/s), and the
+fp64 oracle timed on the host cores on the same inputs (a reported baseline,
+with a parity check of the benchmarked output).
+
+Progress goes to stderr; stdout carries exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=32,d=128,T=8192 bf16) + decode steps/s; % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+# Algorithmic accounting (per token-head, d = 128): q, k, v bf16 (768 B),
+# g fp32 (512 B), beta fp32 (4 B), o bf16 (256 B); plus the fp32 state read
+# (h0) and written (ht) once per (sequence, head).  Flops: 141,013 per
+# token-head at chunk 64 (exact lower triangles, inversion, three state
+# products).  Per kernel: the intra-chunk kernel must read q, k, v, g, beta;
+# the state kernel must read h0 and write o and ht.
+BYTES_PER_TOKEN_HEAD = 1540
+INTRA_BYTES_PER_TOKEN_HEAD = 1284
+INTER_BYTES_PER_TOKEN_HEAD = 256
+FLOPS_PER_TOKEN_HEAD = 141013
+DECODE_BYTES_PER_SEQ_HEAD = 132612  # 2 x 64 KiB fp32 state + 1540 B of vectors
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_97_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(kernel)
+    if not rec or rec.get("workload") != workload or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-passes", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_97_amd as kda
+    import workloads
+
+    dev = torch.device("cuda:0")
+    spec = workloads.CONFIGS[1]
+    B, T, H, dk, dv, C = spec.B, spec.T, spec.H, spec.dk, spec.dv, spec.chunk
+    log(f"generating {spec.name}")
+    x = workloads.make_prefill(spec)
+    d = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.workspace_bytes(B, T, H, dk, dv, B, C, kda.KDA_DTYPE_BF16), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=C, o=o, ht=ht,
+                          workspace=ws)
+
+    log(f"prefill warmup x{args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"prefill timed x{args.steps}")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kda.kda_profile_start(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kt = kda.kda_profile_stop()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    log(f"prefill {ms_step * 1e3:.1f} us/call -> {value / 1e6:.2f} M tokens/s (wall {wall * 1e3 / args.steps:.1f} us)")
+
+    per_kernel_us = {name: 1e3 * tot / n for name, (n, tot) in kt.items()}
+    th = B * T * H
+    state_bytes = 2 * B * H * dk * dv * 4
+    kernel_bytes = {"kda_intra": INTRA_BYTES_PER_TOKEN_HEAD * th,
+                    "kda_inter": INTER_BYTES_PER_TOKEN_HEAD * th + state_bytes}
+    dom = max(per_kernel_us, key=per_kernel_us.get)
+    dom_us = per_kernel_us[dom]
+    achieved = kernel_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
+    workload = "prefill B=1 H=32 T=8192 d=128 bf16 chunk=64"
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(dom, workload),
+                "avg_launch_us": round(dom_us, 2),
+                "algorithmic_bytes_per_launch": kernel_bytes.get(dom, 0)}
+    path_bytes = BYTES_PER_TOKEN_HEAD * th + state_bytes
+    path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
+    path_tflops = FLOPS_PER_TOKEN_HEAD * th / (ms_step * 1e-3) / 1e12
+    path_roofline = {"bound": "hbm", "algorithmic_bytes": path_bytes,
+                     "achieved_GBps": round(path_gbs, 1), "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_flops": FLOPS_PER_TOKEN_HEAD * th,
+                     "achieved_TFLOPs": round(path_tflops, 2),
+                     "mfma_frac": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "hbm_floor_us": round(path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
+
+    # ---------------------------------------------------------------- decode
+    dspec = workloads.DECODE
+    log(f"decode inputs: {dspec.name}")
+    state0 = workloads.make_decode_state(dspec, device=dev)
+    state = state0.clone()
+    steps_in = [workloads.make_decode_step(dspec, s, device=dev) for s in range(dspec.steps)]
+    od = torch.empty((dspec.N, dspec.H, dspec.dv), dtype=torch.bfloat16, device=dev)
+
+    def decode_pass():
+        for s in range(dspec.steps):
+            xi = steps_in[s]
+            kda.decode_step(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], state, o=od)
+
+    decode_pass()  # warmup
+    torch.cuda.synchronize()
+    times = []
+    dec_kt = {}
+    for p in range(args.decode_passes):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        if p == args.decode_passes - 1:
+            kda.kda_profile_start(dspec.steps + 4)
+        ev0.record(stream)
+        decode_pass()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        if p == args.decode_passes - 1:
+            dec_kt = kda.kda_profile_stop()
+        times.append(ev0.elapsed_time(ev1))
+    t_pass = min(times) * 1e-3
+    dec_steps_s = dspec.steps / t_pass
+    dec_launch_us = 1e3 * dec_kt["kda_decode"][1] / dec_kt["kda_decode"][0]
+    dec_bytes = DECODE_BYTES_PER_SEQ_HEAD * dspec.N * dspec.H
+    dec_gbs = dec_bytes / (dec_launch_us * 1e-6) / 1e9
+    log(f"decode {t_pass * 1e3:.2f} ms / {dspec.steps} steps -> {dec_steps_s:.0f} steps/s, "
+        f"{dec_launch_us:.1f} us/launch, {dec_gbs:.0f} GB/s")
+    decode = {"workload": "decode N=256 H=32 d=128 bf16, 128 in-place steps",
+              "steps_per_s": round(dec_steps_s, 1), "tokens_per_s": round(dec_steps_s * dspec.N, 1),
+              "ms_per_step": round(1e3 * t_pass / dspec.steps, 4),
+              "roofline": {"kernel": "kda_decode", "bound": "hbm", "achieved": round(dec_gbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": load_traffic("kda_decode", "decode N=256 H=32 d=128 bf16"),
+                           "avg_launch_us": round(dec_launch_us, 2),
+                           "algorithmic_bytes_per_launch": dec_bytes}}
+
+    # -------------------------------------------- oracle on the host cores
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: workloads.to_numpy_f32(t)[0]
+        q, k, v, g, b = (f(x[n]) for n in ("q", "k", "v", "g", "beta"))
+        h0 = x["h0"].numpy().astype(np.float64)
+        threads = oracle.max_threads()
+        log(f"oracle on the host: full workload, {threads} threads")
+        t0 = time.perf_counter()
+        o_ref, ht_ref = oracle.prefill(q, k, v, g, b, h0)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(tokens / t_cpu, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the full headline workload ({T} tokens x {H} heads), fp64 token loop, "
+                         f"{t_cpu:.2f} s wall",
+               "host_cpus": os.cpu_count()}
+        step()
+        torch.cuda.synchronize()
+        on = o[0].double().cpu().numpy()
+        hn = ht.double().cpu().numpy()
+        rel = lambda a, r: float(np.linalg.norm(a - r) / np.linalg.norm(r))
+        parity = {"o_rel_l2": rel(on, o_ref), "ht_rel_l2": rel(hn, ht_ref), "tol": 2e-2}
+        log(f"oracle {t_cpu:.2f} s; parity o {parity['o_rel_l2']:.2e} ht {parity['ht_rel_l2']:.2e}")
+
+        # decode baseline: the first 4 steps of the decode workload
+        ref_state = state0.double().cpu().numpy()
+        t0 = time.perf_counter()
+        for s in range(4):
+            xi = steps_in[s]
+            oracle.decode_step(*(workloads.to_numpy_f32(xi[n]) for n in ("q", "k", "v", "g", "beta")),
+                               ref_state)
+        t_dec_cpu = (time.perf_counter() - t0) / 4
+        decode["cpu_baseline"] = {"value": round(1.0 / t_dec_cpu, 3), "unit": "steps/s", "cores": threads,
+                                  "kind": "oracle", "sample": "first 4 of the 128 decode steps"}
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded generators: unit-norm q/k, N(0,1) v, sigmoid beta, g=-5*sigmoid(N(0,1)))",
+           "config": {"workload": workload, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
+                      "h0": "N(0,0.02)"},
+           "roofline": roofline, "path_roofline": path_roofline,
+           "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+           "cpu_baseline": cpu, "parity": parity, "decode": decode,
+           "source_digest": source_digest()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,7 +11,7 @@ raw integer device addresses.  ``chunk_prefill`` and ``decode_step`` wrap
 them for torch tensors.
 
 Importing this package raises if the library has not been built
-(``python -m gated_delta_rule_97_amd.build``): there is no fallback path.
+(``python gated_delta_rule_97_amd/build.py``): there is no fallback path.
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m gated_delta_rule_97_amd.build` (no CPU fallback exists)")
+                      "`python gated_delta_rule_97_amd/build.py` (no CPU fallback exists)")
 
 # A process must hold a single HIP runtime.  torch carries its own copy of
 # libamdhip64 (same SONAME as the system one); loading torch before libkda.so

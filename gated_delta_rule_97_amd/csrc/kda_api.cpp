@@ -28,13 +28,15 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
     L.Qp = off;
     off = align_up(off + slots * C * dk * elem_bytes, 256);
     L.KtT = off;
-    off = align_up(off + slots * C * dk * elem_bytes, 256);
+    off = align_up(off + slots * chunk_pad(C, elem_bytes) * dk * elem_bytes, 256);
     L.Ut = off;
     off = align_up(off + slots * C * dv * elem_bytes, 256);
     L.Oi = off;
     off = align_up(off + slots * C * dv * elem_bytes, 256);
     L.D = off;
     off = align_up(off + slots * dk * sizeof(float), 256);
+    L.dummy = off;
+    off += 1024;
     L.total = off;
     return L;
 }
@@ -76,6 +78,18 @@ void prof_end(hipStream_t s, const char *name) {
 }  // namespace kda
 
 using namespace kda;
+
+// Compute units of the current device, queried once per device.
+static int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
 
 static bool misaligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
@@ -208,9 +222,12 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
     a.T = T; a.H = H; a.N = N;
     a.nc_max = nc_max;
     a.nc_seq = (T + chunk_size - 1) / chunk_size;
+    a.num_cu = device_cu_count();
+    if (a.num_cu <= 0) return KDA_ERR_LAUNCH;
     a.o = o; a.ht = ht;
     a.W = ws + L.W; a.Qp = ws + L.Qp; a.KtT = ws + L.KtT; a.Ut = ws + L.Ut; a.Oi = ws + L.Oi;
     a.D = reinterpret_cast<float *>(ws + L.D);
+    a.dummy = ws + L.dummy;
 
     if (!any_tokens) a.nc_max = 0;  // only the state copy h0 -> ht remains
     if (packed && a.nc_max > 0) {

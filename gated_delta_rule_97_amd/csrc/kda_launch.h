@@ -19,23 +19,31 @@ struct PrefillArgs {
     int H, N;
     int nc_max;                // chunk slots in the workspace
     int nc_seq;                // chunks per sequence (fixed-length batches)
+    int num_cu;                // compute units of the device (persistent grids)
     void *o;                   // [rows][H][dv]
     float *ht;                 // [N][H][dk][dv] or null
-    // workspace, per (chunk slot, head):
-    void *W;                   // [C][dk]  WY factor  (I+A)^-1 (beta k e^Gam)
-    void *Qp;                  // [C][dk]  q e^Gam - P W
-    void *KtT;                 // [dk][C]  (k e^{Gam_last - Gam})^T
-    void *Ut;                  // [C][dv]  (I+A)^-1 (beta v)
-    void *Oi;                  // [C][dv]  P (I+A)^-1 (beta v)
+    // workspace, per (chunk slot, head); "operand" / "quad" order are the
+    // wave-read orders defined in kda_prefill_impl.h:
+    void *W;                   // [C][dk]  (I+A)^-1 (beta k e^Gam), operand order
+    void *Qp;                  // [C][dk]  q e^Gam - P W, operand order
+    void *KtT;                 // [dk][Cp] (k e^{Gam_last - Gam})^T, operand order
+    void *Ut;                  // [C][dv]  (I+A)^-1 (beta v), quad order
+    void *Oi;                  // [C][dv]  P (I+A)^-1 (beta v), quad order
     float *D;                  // [dk]     e^{Gam_last}
+    void *dummy;               // 1 KiB sink for the o rows past a sequence's end
 };
 
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {
-    size_t coff, W, Qp, KtT, Ut, Oi, D, total;
+    size_t coff, W, Qp, KtT, Ut, Oi, D, dummy, total;
 };
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
                              size_t elem_bytes);
+// chunk length rounded up to the MFMA contraction of the dtype (K~^T pad)
+inline int chunk_pad(int C, size_t elem_bytes) {
+    const int k = elem_bytes == 2 ? 32 : 4;
+    return (C + k - 1) / k * k;
+}
 
 // Launch-time profiling hooks (no-ops unless a profiling session is open).
 void prof_begin(hipStream_t s);

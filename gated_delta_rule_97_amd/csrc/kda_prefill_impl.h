@@ -72,16 +72,69 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: intra-chunk work.  LDS layout (byte offsets), padded rows.
+// Workspace layouts.  Every intermediate is stored in the exact order its
+// consumer's wavefront reads it, so that one wave-wide load instruction is
+// one contiguous, fully used span (1 KiB for a bf16 operand fragment).
+//
+// Operand order of an [R][K] matrix used as an MFMA A (or B) operand:
+// blocks of 16 rows x Mma::K columns, block (rb, kb) at index rb*(Kp/K)+kb,
+// inside a block lane (row % 16) + 16 * ((k % K) / KPL) holds KPL
+// consecutive k.  Kp = K rounded up to Mma::K (the pad stays unread).
+// Quad order of an [R][N] matrix read elementwise at MFMA output positions:
+// 16x16 tiles, tile (r/16, n/16) at index (r/16)*(N/16) + n/16, inside a
+// tile lane (n % 16) + 16 * ((r % 16) / 4) holds 4 consecutive rows.
+// ---------------------------------------------------------------------------
+template <class T> __host__ __device__ constexpr int kpad(int K) {
+    return (K + Mma<T>::K - 1) / Mma<T>::K * Mma<T>::K;
+}
+
+template <class T, int K>
+__device__ __forceinline__ size_t frag_off(int r, int k) {
+    using M = Mma<T>;
+    constexpr int KP = kpad<T>(K);
+    const int blk = (r >> 4) * (KP / M::K) + k / M::K;
+    const int ln = (r & 15) + 16 * ((k % M::K) / M::KPL);
+    return size_t(blk) * (16 * M::K) + ln * M::KPL + (k % M::KPL);
+}
+
+// four consecutive k of row r (k0 % 4 == 0) into operand order
+template <class T, int K>
+__device__ __forceinline__ void store_frag4(T *base, int r, int k0, float a, float b, float c, float d) {
+    if constexpr (Mma<T>::KPL >= 4) {
+        store4(base + frag_off<T, K>(r, k0), a, b, c, d);
+    } else {
+        base[frag_off<T, K>(r, k0)] = from_f32<T>(a);
+        base[frag_off<T, K>(r, k0 + 1)] = from_f32<T>(b);
+        base[frag_off<T, K>(r, k0 + 2)] = from_f32<T>(c);
+        base[frag_off<T, K>(r, k0 + 3)] = from_f32<T>(d);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ size_t quad_off(int tile_r, int tile_n, int lane) {
+    return (size_t(tile_r) * (N / 16) + tile_n) * 256 + lane * 4;
+}
+
+constexpr int kIThreads = 1024;  // kernel 1
+constexpr int kIWaves = kIThreads / kWave;
+
+// ---------------------------------------------------------------------------
+// Kernel 1: intra-chunk work, persistent.  Its LDS footprint allows one
+// workgroup per compute unit, so the workgroup is 16 wavefronts (four per
+// SIMD) to overlap the latencies of its many short dependent steps.  Each workgroup walks (chunk, head)
+// items in chunk-major order; while it computes one item, the raw inputs of
+// its next item are already in flight into registers.  LDS row pitches are
+// chosen so that 16 lanes reading 16 bytes from 16 consecutive rows hit 64
+// distinct banks.
 // ---------------------------------------------------------------------------
 template <class T, int DK, int DV, int C>
 struct IntraLds {
     static constexpr int PT = 16 / sizeof(T);  // 16-byte row pad, in elements
-    static constexpr int G_LD = DK + 4;        // fp32 Gam       [C][DK]
-    static constexpr int K_LD = DK + PT;       // k, q           [C][DK]
-    static constexpr int KT_LD = C + PT;       // transposed ops [DK|DV][C]
-    static constexpr int A_LD = C + 4;         // fp32 A, L      [C][C]
-    static constexpr int P_LD = C + PT;        // P              [C][C]
+    static constexpr int G_LD = DK + 4;        // fp32 Gam        [C][DK]
+    static constexpr int K_LD = DK + PT;       // k, q (q e^Gam)  [C][DK]
+    static constexpr int KT_LD = C + PT;       // transposed ops  [DK|DV][C]
+    static constexpr int A_LD = C + 4;         // fp32 A, L       [C][C]
+    static constexpr int P_LD = C + PT;        // P               [C][C]
     static constexpr int Y_LD = 20;            // fp32 16x16 scratch
     static constexpr size_t oG = 0;
     static constexpr size_t oK = oG + size_t(C) * G_LD * 4;
@@ -89,344 +142,654 @@ struct IntraLds {
     static constexpr size_t oB = oQ + size_t(C) * K_LD * sizeof(T);
     static constexpr size_t oKT = oB + size_t(C) * 4;
     static constexpr size_t oVT = oKT + size_t(DK) * KT_LD * sizeof(T);
+    // one region holds, in turn: natural v and the K~^T staging, then A and L
+    static constexpr int V_LD = DV + PT;                               // natural v [C][DV]
     static constexpr size_t oA = oVT + size_t(DV) * KT_LD * sizeof(T);
     static constexpr size_t oL = oA + size_t(C) * A_LD * 4;
-    static constexpr size_t oP = oL + size_t(C) * A_LD * 4;
+    static constexpr size_t oV = oA;
+    static constexpr size_t oKtT = oV + size_t(C) * V_LD * sizeof(T);
+    static constexpr size_t kAL = size_t(2) * C * A_LD * 4;
+    static constexpr size_t kVK = size_t(C) * V_LD * sizeof(T) + size_t(DK) * KT_LD * sizeof(T);
+    static constexpr size_t oP = oA + (kAL > kVK ? kAL : kVK);
     static constexpr size_t oY = oP + size_t(C) * P_LD * sizeof(T);
-    static constexpr size_t bytes = oY + size_t(3) * 16 * Y_LD * 4;
+    static constexpr size_t oT = oY + size_t(3) * 16 * Y_LD * 4;      // cumsum segment totals
+    static constexpr size_t bytes = oT + size_t(8) * (DK / 4) * 16;
+};
+
+// Raw inputs of one (chunk, head) item as held by one thread.
+template <class T, int DK, int DV, int C>
+struct IntraIn {
+    static constexpr int EV = 16 / sizeof(T);
+    static constexpr int NKV = (C * DK / EV + kIThreads - 1) / kIThreads;  // k, q vectors per thread
+    static constexpr int NVV = (C * DV / EV + kIThreads - 1) / kIThreads;  // v vectors per thread
+    static constexpr int NGV = (C * DK / 4 + kIThreads - 1) / kIThreads;   // g float4 per thread
+    uint4 k[NKV], q[NKV], v[NVV];
+    float4 g[NGV];
+    float bv[NVV];  // beta of each v row
 };
 
 template <class T, int DK, int DV, int C>
-__global__ __launch_bounds__(kThreads) void kda_intra_kernel(PrefillArgs a) {
+__device__ __forceinline__ void intra_fetch(IntraIn<T, DK, DV, C> &in, const PrefillArgs &a, const ChunkLoc &loc,
+                                            int h, int tid) {
+    using In = IntraIn<T, DK, DV, C>;
+    constexpr int EV = In::EV, KV = DK / EV, VV = DV / EV, GV = DK / 4;
+    const T *kg = static_cast<const T *>(a.k);
+    const T *qg = static_cast<const T *>(a.q);
+    const T *vg = static_cast<const T *>(a.v);
+    const int H = a.H;
+#pragma unroll
+    for (int u = 0; u < In::NKV; ++u) {
+        const int idx = tid + kIThreads * u, t = idx / KV, cv = idx % KV;
+        in.k[u] = in.q[u] = make_uint4(0, 0, 0, 0);
+        if (idx < C * KV && t < loc.len) {
+            const size_t off = (size_t(loc.tok0 + t) * H + h) * DK + cv * EV;
+            in.k[u] = *reinterpret_cast<const uint4 *>(kg + off);
+            in.q[u] = *reinterpret_cast<const uint4 *>(qg + off);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < In::NVV; ++u) {
+        const int idx = tid + kIThreads * u, t = idx / VV, cv = idx % VV;
+        in.v[u] = make_uint4(0, 0, 0, 0);
+        in.bv[u] = 0.f;
+        if (idx < C * VV && t < loc.len) {
+            in.v[u] = *reinterpret_cast<const uint4 *>(vg + (size_t(loc.tok0 + t) * H + h) * DV + cv * EV);
+            in.bv[u] = a.beta[size_t(loc.tok0 + t) * H + h];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < In::NGV; ++u) {
+        const int idx = tid + kIThreads * u, t = idx / GV, cv = idx % GV;
+        in.g[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (idx < C * GV && t < loc.len)
+            in.g[u] = *reinterpret_cast<const float4 *>(a.g + (size_t(loc.tok0 + t) * H + h) * DK + cv * 4);
+    }
+}
+
+// A value the compiler must treat as unknown at this point.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// 8 consecutive fp32 values from LDS
+__device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <class T, int DK, int DV, int C>
+__global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     using Ly = IntraLds<T, DK, DV, C>;
+    using In = IntraIn<T, DK, DV, C>;
     using M = Mma<T>;
     typedef typename M::Frag Frag;
     constexpr int NT = C / kTile;
     constexpr int G_LD = Ly::G_LD, K_LD = Ly::K_LD, KT_LD = Ly::KT_LD;
     constexpr int A_LD = Ly::A_LD, P_LD = Ly::P_LD, Y_LD = Ly::Y_LD;
-    constexpr int EV = 16 / sizeof(T);  // elements per 16-byte vector
+    constexpr int EV = In::EV, KV = DK / EV, VV = DV / EV, GV = DK / 4;
 
     extern __shared__ __align__(16) unsigned char smem[];
     float *sG = reinterpret_cast<float *>(smem + Ly::oG);
     T *sK = reinterpret_cast<T *>(smem + Ly::oK);
-    T *sQ = reinterpret_cast<T *>(smem + Ly::oQ);
+    T *sQ = reinterpret_cast<T *>(smem + Ly::oQ);   // q, later q e^Gam
     float *sB = reinterpret_cast<float *>(smem + Ly::oB);
-    T *sKT = reinterpret_cast<T *>(smem + Ly::oKT);  // beta k e^Gam ^T, later W^T
-    T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);  // beta v ^T,       later Ut^T
+    T *sKT = reinterpret_cast<T *>(smem + Ly::oKT);  // (beta k e^Gam)^T, later W^T
+    T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);  // (beta v)^T,       later Ut^T
+    T *sKtT = reinterpret_cast<T *>(smem + Ly::oKtT);  // (k e^{Gam_last-Gam})^T staging
+    T *sV = reinterpret_cast<T *>(smem + Ly::oV);      // natural v staging
     float *sA = reinterpret_cast<float *>(smem + Ly::oA);
     float *sL = reinterpret_cast<float *>(smem + Ly::oL);
     T *sP = reinterpret_cast<T *>(smem + Ly::oP);
     float *sY = reinterpret_cast<float *>(smem + Ly::oY);
+    float4 *sTot = reinterpret_cast<float4 *>(smem + Ly::oT);
 
-    const int gc = blockIdx.x, h = blockIdx.y;
-    ChunkLoc loc;
-    if (!locate_chunk(a, gc, C, loc)) return;  // uniform over the workgroup
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int grp = lane >> 4, l16 = lane & 15;
     const int H = a.H;
-    const T *qg = static_cast<const T *>(a.q);
-    const T *kg = static_cast<const T *>(a.k);
-    const T *vg = static_cast<const T *>(a.v);
-    const size_t slot = size_t(gc) * H + h;
+    const int nitems = a.nc_max * H;
 
-    // ---- phase 0: stage g, k, q, beta (tail rows are neutral: zeros) ----
-    for (int t = tid; t < C; t += kThreads)
-        sB[t] = (t < loc.len) ? a.beta[size_t(loc.tok0 + t) * H + h] : 0.f;
-    constexpr int GV = DK / 4;
-    for (int i = tid; i < C * GV; i += kThreads) {
-        const int t = i / GV, cv = i - t * GV;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t < loc.len)
-            x = *reinterpret_cast<const float4 *>(a.g + (size_t(loc.tok0 + t) * H + h) * DK + cv * 4);
-        *reinterpret_cast<float4 *>(sG + t * G_LD + cv * 4) = x;
-    }
-    constexpr int KV = DK / EV;
-    for (int i = tid; i < C * KV; i += kThreads) {
-        const int t = i / KV, cv = i - t * KV;
-        uint4 xk = make_uint4(0, 0, 0, 0), xq = make_uint4(0, 0, 0, 0);
-        if (t < loc.len) {
-            const size_t off = (size_t(loc.tok0 + t) * H + h) * DK + cv * EV;
-            xk = *reinterpret_cast<const uint4 *>(kg + off);
-            xq = *reinterpret_cast<const uint4 *>(qg + off);
-        }
-        *reinterpret_cast<uint4 *>(sK + t * K_LD + cv * EV) = xk;
-        *reinterpret_cast<uint4 *>(sQ + t * K_LD + cv * EV) = xq;
-    }
-    for (int i = tid; i < C * A_LD; i += kThreads) sL[i] = 0.f;
-    __syncthreads();
+    // first item of this workgroup with a valid chunk
+    int item = blockIdx.x;
+    ChunkLoc loc;
+    while (item < nitems && !locate_chunk(a, item / H, C, loc)) item += gridDim.x;
+    if (item >= nitems) return;
+    In in;
+    intra_fetch(in, a, loc, item % H, int(threadIdx.x));
 
-    // ---- phase 1: Gam = cumulative log-decay along the chunk, per channel --
-    {
-        constexpr int TPC = kThreads / DK;  // threads per channel
-        constexpr int SL = C / TPC;         // rows per thread
-        static_assert(TPC * DK == kThreads && SL >= 1, "cumsum split");
-        const int c = tid % DK, seg = tid / DK;
-        float run = 0.f;
-#pragma unroll
-        for (int r = 0; r < SL; ++r) {
-            float *p = sG + (seg * SL + r) * G_LD + c;
-            run += *p;
-            *p = run;
-        }
-        float *sTot = sA;  // scratch until phase 3
-        sTot[seg * DK + c] = run;
-        __syncthreads();
-        float off = 0.f;
-        for (int s = 0; s < seg; ++s) off += sTot[s * DK + c];
-        if (seg > 0) {
-#pragma unroll
-            for (int r = 0; r < SL; ++r) sG[(seg * SL + r) * G_LD + c] += off;
-        }
-        __syncthreads();
-    }
+    while (item < nitems) {
+        // thread coordinates pass through an opaque copy each iteration, so
+        // that the many per-stage LDS addresses are recomputed here instead
+        // of being hoisted out of the loop and held in registers throughout
+        const int tid = opaque(int(threadIdx.x)), lane = tid & 63, wid = tid >> 6;
+        const int grp = lane >> 4, l16 = lane & 15;
+        const int gc = item / H, h = item % H;
+        const size_t slot = size_t(gc) * H + h;
+        const ChunkLoc cur = loc;
 
-    // ---- phase 2: elementwise operands ----
-    // beta_s k_s e^{Gam_s}, transposed: B operand of W = L (beta k e^Gam)
-    for (int i = tid; i < C * DK; i += kThreads) {
-        const int s = i % C, c = i / C;
-        const float x = sB[s] * to_f32(sK[s * K_LD + c]) * exp_e(sG[s * G_LD + c]);
-        sKT[c * KT_LD + s] = from_f32<T>(x);
-    }
-    // beta_s v_s, transposed: B operand of Ut = L (beta v)
-    constexpr int VV = DV / EV;
-    for (int i = tid; i < C * VV; i += kThreads) {
-        const int s = i / VV, jv = i - s * VV;
-        Vec16<T> x;
-        x.raw = make_uint4(0, 0, 0, 0);
-        if (s < loc.len)
-            x.raw = *reinterpret_cast<const uint4 *>(vg + (size_t(loc.tok0 + s) * H + h) * DV + jv * EV);
-        const float bs = sB[s];
+        // ---- stage the raw inputs (tail rows are neutral zeros) ----
 #pragma unroll
-        for (int e = 0; e < EV; ++e) sVT[(jv * EV + e) * KT_LD + s] = from_f32<T>(bs * x.get(e));
-    }
-    // (k e^{Gam_last - Gam})^T and e^{Gam_last} for the state update
-    {
-        T *KtT = static_cast<T *>(a.KtT) + slot * DK * C;
-        constexpr int TV = C / EV;
-        for (int i = tid; i < DK * TV; i += kThreads) {
-            const int c = i / TV, tv = i - c * TV;
-            const float glast = sG[(C - 1) * G_LD + c];
-            Vec16<T> out;
-            T *po = reinterpret_cast<T *>(&out.raw);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                const int t = tv * EV + e;
-                po[e] = from_f32<T>(to_f32(sK[t * K_LD + c]) * exp_e(glast - sG[t * G_LD + c]));
+        for (int u = 0; u < In::NKV; ++u) {
+            const int idx = tid + kIThreads * u, t = idx / KV, cv = idx % KV;
+            if (idx < C * KV) {
+                *reinterpret_cast<uint4 *>(sK + t * K_LD + cv * EV) = in.k[u];
+                *reinterpret_cast<uint4 *>(sQ + t * K_LD + cv * EV) = in.q[u];
             }
-            *reinterpret_cast<uint4 *>(KtT + size_t(c) * C + tv * EV) = out.raw;
         }
-        if (tid < DK) a.D[slot * DK + tid] = exp_e(sG[(C - 1) * G_LD + tid]);
-    }
+#pragma unroll
+        for (int u = 0; u < In::NGV; ++u) {
+            const int idx = tid + kIThreads * u, t = idx / GV, cv = idx % GV;
+            if (idx < C * GV) *reinterpret_cast<float4 *>(sG + t * G_LD + cv * 4) = in.g[u];
+        }
+#pragma unroll
+        for (int u = 0; u < In::NVV; ++u) {
+            const int idx = tid + kIThreads * u, t = idx / VV, jv = idx % VV;
+            if (idx < C * VV) {
+                *reinterpret_cast<uint4 *>(sV + t * Ly::V_LD + jv * EV) = in.v[u];
+                if (jv == 0) sB[t] = in.bv[u];
+            }
+        }
+        // ---- prefetch the next item's inputs while this one computes ----
+        int nxt = item + gridDim.x;
+        while (nxt < nitems && !locate_chunk(a, nxt / H, C, loc)) nxt += gridDim.x;
+        if (nxt < nitems) intra_fetch(in, a, loc, nxt % H, tid);
+        __syncthreads();
 
-    // ---- phase 3: A (strictly lower, row-scaled by beta) and P (lower incl.)
-    //      on MFMA, one 16x16 tile pair (I, J <= I) at a time ----
-    constexpr int NPAIR = NT * (NT + 1) / 2;
-    for (int item = wid; item < NPAIR; item += kWaves) {
-        int I = 0, rem = item;
-        while (rem > I) { rem -= I + 1; ++I; }
-        const int J = rem;
-        const int row = kTile * I + l16;  // token t of the A fragment
-        const int col = kTile * J + l16;  // token s of the B fragment
-        const float *gref = sG + (I > 0 ? kTile * I - 1 : 0) * G_LD;  // r_I: row before tile I
+        // ---- Gam = cumulative log-decay along the chunk, per channel ----
+        {
+            constexpr int NCG = DK / 4;                                   // float4 channel groups
+            constexpr int NSEG0 = (kIThreads / NCG) < 8 ? (kIThreads / NCG) : 8;  // segments per channel
+            constexpr int NSEG = NSEG0 < C ? NSEG0 : C;
+            constexpr int SL = C / NSEG;
+            const int cg = tid % NCG, seg = tid / NCG;
+            float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (seg < NSEG) {
+#pragma unroll
+                for (int r = 0; r < SL; ++r) {
+                    float4 *p = reinterpret_cast<float4 *>(sG + (seg * SL + r) * G_LD + cg * 4);
+                    const float4 x = *p;
+                    run.x += x.x; run.y += x.y; run.z += x.z; run.w += x.w;
+                    *p = run;
+                }
+                sTot[seg * NCG + cg] = run;
+            }
+            __syncthreads();
+            if (seg < NSEG && seg > 0) {
+                float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int s2 = 0; s2 < seg; ++s2) {
+                    const float4 x = sTot[s2 * NCG + cg];
+                    off.x += x.x; off.y += x.y; off.z += x.z; off.w += x.w;
+                }
+#pragma unroll
+                for (int r = 0; r < SL; ++r) {
+                    float4 *p = reinterpret_cast<float4 *>(sG + (seg * SL + r) * G_LD + cg * 4);
+                    float4 x = *p;
+                    x.x += off.x; x.y += off.y; x.z += off.z; x.w += off.w;
+                    *p = x;
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---- A (strictly lower, row-scaled by beta) and P (lower incl.) on
+        //      MFMA, one 16x16 tile pair (I, J <= I) per wave, while the
+        //      remaining waves do the elementwise transposes:
+        //      (beta k e^Gam)^T, the K~^T staging and (beta v)^T ----
+        constexpr int NPAIR = NT * (NT + 1) / 2;
+        static_assert(NPAIR < kIWaves, "A/P tile pairs must leave waves for the elementwise work");
         floatx4 accA = zero4(), accP = zero4();
+        if (wid < NPAIR) {
+            int I = 0, rem = wid;
+            while (rem > I) { rem -= I + 1; ++I; }
+            const int J = rem;
+            const int row = kTile * I + l16;  // token t of the A fragment
+            const int col = kTile * J + l16;  // token s of the B fragment
+            const float *gref = sG + (I > 0 ? kTile * I - 1 : 0) * G_LD;  // r_I: row before tile I
+#pragma unroll 1
+            for (int kk = 0; kk < DK / M::K; ++kk) {
+                const int cb = kk * M::K + grp * M::KPL;
+                Frag fk, fq, fb;
+                if constexpr (M::KPL == 8) {
+                    float gr[8], gc8[8], rr[8];
+                    lds_read8(sG + row * G_LD + cb, gr);
+                    lds_read8(sG + col * G_LD + cb, gc8);
+                    if (I > 0) lds_read8(gref + cb, rr);
+                    else {
 #pragma unroll
-        for (int kk = 0; kk < DK / M::K; ++kk) {
-            Frag fk, fq, fb;
+                        for (int j = 0; j < 8; ++j) rr[j] = 0.f;
+                    }
+                    const Frag kr = M::load(sK + row * K_LD + cb);
+                    const Frag qr = M::load(sQ + row * K_LD + cb);
+                    const Frag kc = M::load(sK + col * K_LD + cb);
 #pragma unroll
-            for (int j = 0; j < M::KPL; ++j) {
-                const int c = kk * M::K + grp * M::KPL + j;
-                const float r = (I > 0) ? gref[c] : 0.f;
-                const float ea = exp_e(sG[row * G_LD + c] - r);  // <= 1
-                const float eb = exp_e(r - sG[col * G_LD + c]);  // <= e^80
-                M::set(fk, j, to_f32(sK[row * K_LD + c]) * ea);
-                M::set(fq, j, to_f32(sQ[row * K_LD + c]) * ea);
-                M::set(fb, j, to_f32(sK[col * K_LD + c]) * eb);
+                    for (int j = 0; j < 8; ++j) {
+                        const float ea = exp_e(gr[j] - rr[j]);   // <= 1
+                        const float eb = exp_e(rr[j] - gc8[j]);  // <= e^80
+                        M::set(fk, j, to_f32(kr[j]) * ea);
+                        M::set(fq, j, to_f32(qr[j]) * ea);
+                        M::set(fb, j, to_f32(kc[j]) * eb);
+                    }
+                } else {
+                    const float r = (I > 0) ? gref[cb] : 0.f;
+                    const float ea = exp_e(sG[row * G_LD + cb] - r);
+                    const float eb = exp_e(r - sG[col * G_LD + cb]);
+                    M::set(fk, 0, to_f32(sK[row * K_LD + cb]) * ea);
+                    M::set(fq, 0, to_f32(sQ[row * K_LD + cb]) * ea);
+                    M::set(fb, 0, to_f32(sK[col * K_LD + cb]) * eb);
+                }
+                accA = M::mma(fk, fb, accA);
+                accP = M::mma(fq, fb, accP);
             }
-            accA = M::mma(fk, fb, accA);
-            accP = M::mma(fq, fb, accP);
-        }
+        } else {
+            // a thread reads 8 channels of one token; consecutive lanes take
+            // consecutive tokens, so each transposed row write is contiguous
+            constexpr int NK8 = C * DK / 8, NV8 = C * DV / 8;
+            constexpr int ET = (kIWaves - NPAIR) * kWave;
+            for (int idx = tid - NPAIR * kWave; idx < NK8 + NV8; idx += ET) {
+                if (idx < NK8) {
+                    const int t = idx % C, c0 = 8 * (idx / C);
+                    float gt[8], gl[8];
+                    lds_read8(sG + t * G_LD + c0, gt);
+                    lds_read8(sG + (C - 1) * G_LD + c0, gl);
+                    const float bt = sB[t];
+                    Vec16<T> kx[8 / EV];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = kTile * I + 4 * grp + r;
-            sA[t * A_LD + col] = (col < t) ? sB[t] * accA[r] : 0.f;
-            sP[t * P_LD + col] = from_f32<T>((col <= t) ? accP[r] : 0.f);
+                    for (int w = 0; w < 8 / EV; ++w) kx[w].raw = *reinterpret_cast<const uint4 *>(sK + t * K_LD + c0 + w * EV);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float kv = kx[e / EV].get(e % EV);
+                        sKT[(c0 + e) * KT_LD + t] = from_f32<T>(bt * kv * exp_e(gt[e]));
+                        sKtT[(c0 + e) * KT_LD + t] = from_f32<T>(kv * exp_e(gl[e] - gt[e]));
+                    }
+                } else {
+                    const int e8 = idx - NK8;
+                    const int t = e8 % C, j0 = 8 * (e8 / C);
+                    const float bt = sB[t];
+                    Vec16<T> vx[8 / EV];
+#pragma unroll
+                    for (int w = 0; w < 8 / EV; ++w) vx[w].raw = *reinterpret_cast<const uint4 *>(sV + t * Ly::V_LD + j0 + w * EV);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sVT[(j0 + e) * KT_LD + t] = from_f32<T>(bt * vx[e / EV].get(e % EV));
+                }
+            }
+            if (tid - NPAIR * kWave < DK) {
+                const int c = tid - NPAIR * kWave;
+                a.D[slot * DK + c] = exp_e(sG[(C - 1) * G_LD + c]);
+            }
         }
-    }
-    for (int i = tid; i < C * C; i += kThreads) {  // tiles above the diagonal
-        const int t = i / C, s = i - t * C;
-        if ((s >> 4) > (t >> 4)) {
-            sA[t * A_LD + s] = 0.f;
-            sP[t * P_LD + s] = from_f32<T>(0.f);
+        __syncthreads();
+        {   // K~^T out, operand order: 4 consecutive tokens per store
+            T *KtT = static_cast<T *>(a.KtT) + slot * DK * kpad<T>(C);
+            constexpr int NV4 = DK * C / 4;
+            for (int idx = tid; idx < NV4; idx += kIThreads) {
+                const int c = idx / (C / 4), t0 = 4 * (idx % (C / 4));
+                const T *p = sKtT + c * KT_LD + t0;
+                store_frag4<T, C>(KtT, c, t0, to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3]));
+            }
         }
-    }
-    __syncthreads();
+        // q e^Gam in place (the output's state-free part subtracts P W from it)
+        for (int idx = tid; idx < C * DK / 4; idx += kIThreads) {
+            const int t = idx / (DK / 4), c0 = 4 * (idx % (DK / 4));
+            const float4 g4 = *reinterpret_cast<const float4 *>(sG + t * G_LD + c0);
+            T *p = sQ + t * K_LD + c0;
+            store4(p, to_f32(p[0]) * exp_e(g4.x), to_f32(p[1]) * exp_e(g4.y), to_f32(p[2]) * exp_e(g4.z),
+                   to_f32(p[3]) * exp_e(g4.w));
+        }
+        __syncthreads();  // the K~^T staging is copied out: its LDS becomes A and L
+        for (int i = tid; i < C * A_LD; i += kIThreads) sL[i] = 0.f;
+        for (int i = tid; i < C * C; i += kIThreads) {  // tiles above the diagonal
+            const int t = i / C, s = i - t * C;
+            if ((s >> 4) > (t >> 4)) {
+                sA[t * A_LD + s] = 0.f;
+                sP[t * P_LD + s] = from_f32<T>(0.f);
+            }
+        }
+        if (wid < NPAIR) {
+            int I = 0, rem = wid;
+            while (rem > I) { rem -= I + 1; ++I; }
+            const int J = rem;
+            const int col = kTile * J + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = kTile * I + 4 * grp + r;
+                sA[t * A_LD + col] = (col < t) ? sB[t] * accA[r] : 0.f;
+                sP[t * P_LD + col] = from_f32<T>((col <= t) ? accP[r] : 0.f);
+            }
+        }
+        __syncthreads();
 
-    // ---- phase 4: L = (I + A)^-1 by blocked forward substitution (fp32) ----
-    // 4a: the NT diagonal 16x16 blocks, one column per lane (wave 0)
-    if (wid == 0) {
-        const int b = lane >> 4, colx = lane & 15;
-        if (b < NT) {
-            const float *Ab = sA + (kTile * b) * A_LD + kTile * b;
-            float X[16];
+        // ---- L = (I + A)^-1 by blocked forward substitution (fp32) ----
+        // the NT diagonal 16x16 blocks, one column per lane (wave 0)
+        if (wid == 0) {
+            const int b = lane >> 4, colx = lane & 15;
+            if (b < NT) {
+                const float *Ab = sA + (kTile * b) * A_LD + kTile * b;
+                float X[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == colx) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) {
+                    float acc = (i == colx) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc -= Ab[i * A_LD + j] * X[j];
-                X[i] = acc;
+                    for (int j = 0; j < i; ++j) acc -= Ab[i * A_LD + j] * X[j];
+                    X[i] = acc;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sL[(kTile * b + i) * A_LD + kTile * b + colx] = X[i];
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sL[(kTile * b + i) * A_LD + kTile * b + colx] = X[i];
         }
-    }
-    __syncthreads();
-    // 4b: off-diagonal blocks by distance d from the diagonal:
-    //     L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ
-    for (int d = 1; d < NT; ++d) {
-        const int nitems = NT - d;
-        if (wid < nitems) {
-            const int I = d + wid, J = wid;
-            floatx4 acc = zero4();
-            for (int K = J; K < I; ++K) {
+        __syncthreads();
+        // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ
+        for (int d = 1; d < NT; ++d) {
+            const int nb = NT - d;
+            if (wid < nb) {
+                const int I = d + wid, J = wid;
+                floatx4 acc = zero4();
+                for (int K = J; K < I; ++K) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const float af = sA[(kTile * I + l16) * A_LD + kTile * K + 4 * kk + grp];
+                        const float bf = sL[(kTile * K + 4 * kk + grp) * A_LD + kTile * J + l16];
+                        acc = mma_f32(af, bf, acc);
+                    }
+                }
+                float *Y = sY + wid * 16 * Y_LD;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Y[(4 * grp + r) * Y_LD + l16] = acc[r];
+            }
+            __syncthreads();
+            if (wid < nb) {
+                const int I = d + wid, J = wid;
+                const float *Y = sY + wid * 16 * Y_LD;
+                floatx4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const float af = sA[(kTile * I + l16) * A_LD + kTile * K + 4 * kk + grp];
-                    const float bf = sL[(kTile * K + 4 * kk + grp) * A_LD + kTile * J + l16];
+                    const float af = sL[(kTile * I + l16) * A_LD + kTile * I + 4 * kk + grp];
+                    const float bf = Y[(4 * kk + grp) * Y_LD + l16];
                     acc = mma_f32(af, bf, acc);
                 }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -acc[r];
             }
-            float *Y = sY + wid * 16 * Y_LD;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Y[(4 * grp + r) * Y_LD + l16] = acc[r];
+            __syncthreads();
         }
-        __syncthreads();
-        if (wid < nitems) {
-            const int I = d + wid, J = wid;
-            const float *Y = sY + wid * 16 * Y_LD;
-            floatx4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const float af = sL[(kTile * I + l16) * A_LD + kTile * I + 4 * kk + grp];
-                const float bf = Y[(4 * kk + grp) * Y_LD + l16];
-                acc = mma_f32(af, bf, acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -acc[r];
-        }
-        __syncthreads();
-    }
 
-    // ---- phase 5: W = L (beta k e^Gam), Ut = L (beta v) ----
-    constexpr int NCK = DK / kTile, NCV = DV / kTile;
-    constexpr int NITEM = NT * (NCK + NCV);
-    constexpr int IPW = (NITEM + kWaves - 1) / kWaves;
-    constexpr int KSTEPS = (C + M::K - 1) / M::K;
-    floatx4 res[IPW];
-#pragma unroll
-    for (int it = 0; it < IPW; ++it) {
-        const int item = wid + kWaves * it;
-        res[it] = zero4();
-        if (item < NITEM) {
-            const int I = item % NT, n = item / NT;
-            const T *Bop = (n < NCK) ? sKT + (kTile * n) * KT_LD : sVT + (kTile * (n - NCK)) * KT_LD;
-            const int ks = min(KSTEPS, (kTile * (I + 1) + M::K - 1) / M::K);
-            floatx4 acc = zero4();
-            for (int kk = 0; kk < ks; ++kk) {
-                const int kb = kk * M::K + grp * M::KPL;
-                Frag af, bf;
-                if (kb < C) {
-                    af = M::load_f32(sL + (kTile * I + l16) * A_LD + kb);
-                    bf = M::load(Bop + l16 * KT_LD + kb);
-                } else {
-                    af = Frag{};
-                    bf = Frag{};
-                }
-                acc = M::mma(af, bf, acc);
-            }
-            res[it] = acc;
-        }
-    }
-    __syncthreads();  // every read of the beta k e^Gam / beta v operands is done
-    {
-        T *Wg = static_cast<T *>(a.W) + slot * C * DK;
-        T *Ug = static_cast<T *>(a.Ut) + slot * C * DV;
+        // ---- W = L (beta k e^Gam) as W^T = (beta k e^Gam)^T L^T, so that a
+        //      lane's output is four consecutive channels of one token;
+        //      Ut = L (beta v).  Items: W tiles (m over dk, token tile n),
+        //      then Ut tiles (token tile I, n over dv); with NT == 4, wave w
+        //      always has token tile w, so its L fragments repeat. ----
+        constexpr int NCK = DK / kTile, NCV = DV / kTile;
+        constexpr int NIW = NT * NCK, NITEM = NT * (NCK + NCV);
+        constexpr int IPW = (NITEM + kIWaves - 1) / kIWaves;
+        constexpr int KSTEPS = (C + M::K - 1) / M::K;
+        floatx4 res[IPW];
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            const int item = wid + kWaves * it;
-            if (item < NITEM) {
-                const int I = item % NT, n = item / NT;
-                const bool isW = n < NCK;
-                const int cc = kTile * (isW ? n : n - NCK) + l16;
-                const int t0 = kTile * I + 4 * grp;
-                const floatx4 acc = res[it];
-                store4((isW ? sKT : sVT) + cc * KT_LD + t0, acc[0], acc[1], acc[2], acc[3]);
-                T *dst = isW ? Wg : Ug;
-                const int ld = isW ? DK : DV;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[size_t(t0 + r) * ld + cc] = from_f32<T>(acc[r]);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 6: Q' = q e^Gam - P W and Oi = P Ut ----
-    {
-        T *Qg = static_cast<T *>(a.Qp) + slot * C * DK;
-        T *Og = static_cast<T *>(a.Oi) + slot * C * DV;
-#pragma unroll
-        for (int it = 0; it < IPW; ++it) {
-            const int item = wid + kWaves * it;
-            if (item < NITEM) {
-                const int I = item % NT, n = item / NT;
-                const bool isW = n < NCK;
-                const T *Bop = isW ? sKT + (kTile * n) * KT_LD : sVT + (kTile * (n - NCK)) * KT_LD;
-                const int ks = min(KSTEPS, (kTile * (I + 1) + M::K - 1) / M::K);
+            const int wi = wid + kIWaves * it;
+            res[it] = zero4();
+            if (wi < NITEM) {
+                const bool isW = wi < NIW;
+                const int e = isW ? wi : wi - NIW;
+                const int tt = e % NT, cc = e / NT;  // token tile, channel / value tile
+                const int ks = min(KSTEPS, (kTile * (tt + 1) + M::K - 1) / M::K);
                 floatx4 acc = zero4();
                 for (int kk = 0; kk < ks; ++kk) {
                     const int kb = kk * M::K + grp * M::KPL;
-                    Frag af, bf;
+                    Frag fa, fb;
                     if (kb < C) {
-                        af = M::load(sP + (kTile * I + l16) * P_LD + kb);
-                        bf = M::load(Bop + l16 * KT_LD + kb);
+                        const Frag fl = M::load_f32(sL + (kTile * tt + l16) * A_LD + kb);
+                        const Frag fo = M::load((isW ? sKT : sVT) + (kTile * cc + l16) * KT_LD + kb);
+                        fa = isW ? fo : fl;
+                        fb = isW ? fl : fo;
                     } else {
-                        af = Frag{};
-                        bf = Frag{};
+                        fa = Frag{};
+                        fb = Frag{};
                     }
-                    acc = M::mma(af, bf, acc);
+                    acc = M::mma(fa, fb, acc);
                 }
-                const int cc = kTile * (isW ? n : n - NCK) + l16;
-                const int t0 = kTile * I + 4 * grp;
-                if (isW) {
+                res[it] = acc;
+            }
+        }
+        __syncthreads();  // every read of the beta k e^Gam / beta v operands is done
+        {
+            T *Wg = static_cast<T *>(a.W) + slot * C * DK;
+            T *Ug = static_cast<T *>(a.Ut) + slot * C * DV;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = t0 + r;
-                        const float qgam = to_f32(sQ[t * K_LD + cc]) * exp_e(sG[t * G_LD + cc]);
-                        Qg[size_t(t) * DK + cc] = from_f32<T>(qgam - acc[r]);
+            for (int it = 0; it < IPW; ++it) {
+                const int wi = wid + kIWaves * it;
+                if (wi < NITEM) {
+                    const floatx4 acc = res[it];
+                    if (wi < NIW) {
+                        // lane holds W[t][c0..c0+3]: t = 16n + l16, c0 = 16m + 4grp
+                        const int n = wi % NT, m = wi / NT;
+                        const int t = kTile * n + l16, c0 = kTile * m + 4 * grp;
+                        store_frag4<T, DK>(Wg, t, c0, acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sKT[(c0 + r) * KT_LD + t] = from_f32<T>(acc[r]);  // W^T
+                    } else {
+                        // lane holds Ut[t0..t0+3][j]: t0 = 16I + 4grp, j = 16n + l16
+                        const int e = wi - NIW;
+                        const int I = e % NT, n = e / NT;
+                        store4(Ug + quad_off<DV>(I, n, lane), acc[0], acc[1], acc[2], acc[3]);
+                        store4(sVT + (kTile * n + l16) * KT_LD + kTile * I + 4 * grp, acc[0], acc[1], acc[2],
+                               acc[3]);  // Ut^T
                     }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) Og[size_t(t0 + r) * DV + cc] = from_f32<T>(acc[r]);
                 }
             }
         }
+        __syncthreads();
+
+        // ---- Q' = q e^Gam - P W (as (P W)^T = W^T P^T, four channels of one
+        //      token per lane) and Oi = P Ut ----
+        {
+            T *Qg = static_cast<T *>(a.Qp) + slot * C * DK;
+            T *Og = static_cast<T *>(a.Oi) + slot * C * DV;
+#pragma unroll
+            for (int it = 0; it < IPW; ++it) {
+                const int wi = wid + kIWaves * it;
+                if (wi < NITEM) {
+                    const bool isW = wi < NIW;
+                    const int e = isW ? wi : wi - NIW;
+                    const int tt = e % NT, cc = e / NT;
+                    const int ks = min(KSTEPS, (kTile * (tt + 1) + M::K - 1) / M::K);
+                    floatx4 acc = zero4();
+                    for (int kk = 0; kk < ks; ++kk) {
+                        const int kb = kk * M::K + grp * M::KPL;
+                        Frag fa, fb;
+                        if (kb < C) {
+                            const Frag fp = M::load(sP + (kTile * tt + l16) * P_LD + kb);
+                            const Frag fo = M::load((isW ? sKT : sVT) + (kTile * cc + l16) * KT_LD + kb);
+                            fa = isW ? fo : fp;
+                            fb = isW ? fp : fo;
+                        } else {
+                            fa = Frag{};
+                            fb = Frag{};
+                        }
+                        acc = M::mma(fa, fb, acc);
+                    }
+                    if (isW) {
+                        const int t = kTile * tt + l16, c0 = kTile * cc + 4 * grp;
+                        const T *qp = sQ + t * K_LD + c0;
+                        store_frag4<T, DK>(Qg, t, c0, to_f32(qp[0]) - acc[0], to_f32(qp[1]) - acc[1],
+                                           to_f32(qp[2]) - acc[2], to_f32(qp[3]) - acc[3]);
+                    } else {
+                        store4(Og + quad_off<DV>(tt, cc, lane), acc[0], acc[1], acc[2], acc[3]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // LDS is restaged for the next item
+        item = nxt;
+        (void)cur;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 2: state propagation over chunks, with the output fused in.
-// One workgroup per (sequence, head, block of BV value columns).
+// One workgroup per (sequence, head, block of BV value columns).  The chain
+// over chunks is serial, so every operand of chunk c + NS - 1 is requested
+// while chunk c computes (a ring of NS register stages): the per-chunk cost
+// is then the MFMA work and two LDS round trips, not the HBM latency.
 // ---------------------------------------------------------------------------
+template <class T> struct Quad;  // four consecutive values of T, as floats
+template <> struct Quad<bf16> {
+    bf16x4 v;
+    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const bf16x4 *>(p); }
+    __device__ __forceinline__ float operator[](int i) const { return static_cast<float>(v[i]); }
+};
+template <> struct Quad<float> {
+    floatx4 v;
+    __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const floatx4 *>(p); }
+    __device__ __forceinline__ float operator[](int i) const { return v[i]; }
+};
+
+template <class T, int DK, int DV, int C, int BV>
+struct InterCfg {
+    typedef typename Mma<T>::Frag Frag;
+    static constexpr int NT = C / kTile, NB = DV / BV, NCT = BV / kTile, NRT = DK / kTile;
+    static constexpr int KSD = DK / Mma<T>::K;                  // k-steps over dk
+    static constexpr int KSC = (C + Mma<T>::K - 1) / Mma<T>::K;  // k-steps over the chunk
+    static constexpr int NSI = NRT * NCT;                        // state tiles
+    static constexpr int SPW = (NSI + kWaves - 1) / kWaves;
+    static constexpr int NXI = NT * NCT;                         // output tiles
+    static constexpr int XPW = (NXI + kWaves - 1) / kWaves;
+    static constexpr int NS = BV >= 32 ? 2 : 3;                  // register stages
+};
+
+// Operands of one chunk, as held by one lane.
+template <class T, int DK, int DV, int C, int BV>
+struct InterStage {
+    using Cfg = InterCfg<T, DK, DV, C, BV>;
+    typename Cfg::Frag w[Cfg::KSD], q[Cfg::KSD];   // rows of W and Q' of this wave's row tile
+    typename Cfg::Frag kt[Cfg::SPW][Cfg::KSC];     // rows of (k e^{Gam_last-Gam})^T per state tile
+    floatx4 d[Cfg::SPW];                           // e^{Gam_last} per state-tile row
+    Quad<T> ut[Cfg::XPW], oi[Cfg::XPW];            // Ut, Oi at this lane's output positions
+};
+
+template <class T, int DK, int DV, int C, int BV>
+__device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, const PrefillArgs &a, int gc,
+                                           int h, int wid, int grp, int l16, int jb) {
+    using Cfg = InterCfg<T, DK, DV, C, BV>;
+    using M = Mma<T>;
+    const size_t slot = size_t(gc) * a.H + h;
+    const T *W = static_cast<const T *>(a.W) + slot * C * DK;
+    const T *Qp = static_cast<const T *>(a.Qp) + slot * C * DK;
+    const T *KtT = static_cast<const T *>(a.KtT) + slot * DK * kpad<T>(C);
+    const T *UtT = static_cast<const T *>(a.Ut) + slot * C * DV;  // quad order
+    const T *OiT = static_cast<const T *>(a.Oi) + slot * C * DV;  // quad order
+    const float *D = a.D + slot * DK;
+    const int I = wid % Cfg::NT;  // this wave's output row tile
+    const int lane = l16 + 16 * grp;
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSD; ++kk) {
+        const size_t off = size_t(I * Cfg::KSD + kk) * (16 * M::K) + lane * M::KPL;
+        st.w[kk] = M::load(W + off);
+        st.q[kk] = M::load(Qp + off);
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::SPW; ++i) {
+        const int item = wid + kWaves * i;
+        if (item < Cfg::NSI) {
+            const int m = item % Cfg::NRT;
+#pragma unroll
+            for (int kk = 0; kk < Cfg::KSC; ++kk) {
+                const int kb = kk * M::K + grp * M::KPL;
+                st.kt[i][kk] = (kb < C) ? M::load(KtT + size_t(m * Cfg::KSC + kk) * (16 * M::K) + lane * M::KPL)
+                                        : typename Cfg::Frag{};
+            }
+            st.d[i] = *reinterpret_cast<const floatx4 *>(D + kTile * m + 4 * grp);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::XPW; ++i) {
+        const int item = wid + kWaves * i;
+        if (item < Cfg::NXI) {
+            const int nn = item / Cfg::NT;
+            st.ut[i].load(UtT + quad_off<DV>(I, jb / kTile + nn, lane));
+            st.oi[i].load(OiT + quad_off<DV>(I, jb / kTile + nn, lane));
+        }
+    }
+}
+
+// One chunk of the chain for one workgroup: S (fp32, in registers) -> o rows
+// of this chunk and the next state.  ``len`` < C only on a sequence's last
+// chunk; rows past it are written to a dummy area instead of o (a select,
+// not a branch, so that no prefetched operand gets sunk into a branch).
+template <class T, int DK, int DV, int C, int BV>
+__device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &cur, floatx4 (&S)[InterCfg<T, DK, DV, C, BV>::SPW],
+                                            T *sST, T *sUT, T *og, T *dummy, int tok0, int len, int H, int h,
+                                            int wid, int grp, int l16, int jb) {
+    using M = Mma<T>;
+    using Cfg = InterCfg<T, DK, DV, C, BV>;
+    typedef typename M::Frag Frag;
+    constexpr int NT = Cfg::NT, NRT = Cfg::NRT, NSI = Cfg::NSI, SPW = Cfg::SPW, NXI = Cfg::NXI, XPW = Cfg::XPW;
+    constexpr int PT = 16 / sizeof(T);
+    constexpr int ST_LD = DK + PT, UT_LD = C + PT;
+    const int I = wid % NT;
+
+    // 1. S^T -> LDS in the operand dtype
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int item = wid + kWaves * i;
+        if (item < NSI) {
+            const int m = item % NRT, nn = item / NRT;
+            store4(sST + (kTile * nn + l16) * ST_LD + kTile * m + 4 * grp, S[i][0], S[i][1], S[i][2], S[i][3]);
+        }
+    }
+    __syncthreads();
+
+    // 2. X = W S and O = Q' S; U = Ut - X -> LDS; o = Oi + O
+#pragma unroll
+    for (int i = 0; i < XPW; ++i) {
+        const int item = wid + kWaves * i;
+        if (item < NXI) {
+            const int nn = item / NT;
+            floatx4 ax = zero4(), ao = zero4();
+#pragma unroll
+            for (int kk = 0; kk < Cfg::KSD; ++kk) {
+                const int kb = kk * M::K + grp * M::KPL;
+                const Frag sf = M::load(sST + (kTile * nn + l16) * ST_LD + kb);
+                ax = M::mma(cur.w[kk], sf, ax);
+                ao = M::mma(cur.q[kk], sf, ao);
+            }
+            const int j = jb + kTile * nn + l16;
+            const int t0 = kTile * I + 4 * grp;
+            store4(sUT + (kTile * nn + l16) * UT_LD + t0, cur.ut[i][0] - ax[0], cur.ut[i][1] - ax[1],
+                   cur.ut[i][2] - ax[2], cur.ut[i][3] - ax[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                T *dst = (t0 + r < len) ? og + (size_t(tok0 + t0 + r) * H + h) * DV + j : dummy;
+                *dst = from_f32<T>(cur.oi[i][r] + ao[r]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3. S = Diag(e^{Gam_last}) S + (k e^{Gam_last - Gam})^T U
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int item = wid + kWaves * i;
+        if (item < NSI) {
+            const int nn = item / NRT;
+            floatx4 acc = S[i] * cur.d[i];
+#pragma unroll
+            for (int kk = 0; kk < Cfg::KSC; ++kk) {
+                const int kb = kk * M::K + grp * M::KPL;
+                const Frag bf = (kb < C) ? M::load(sUT + (kTile * nn + l16) * UT_LD + kb) : Frag{};
+                acc = M::mma(cur.kt[i][kk], bf, acc);
+            }
+            S[i] = acc;
+        }
+    }
+}
+
 template <class T, int DK, int DV, int C, int BV>
 __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
-    using M = Mma<T>;
-    typedef typename M::Frag Frag;
-    constexpr int NT = C / kTile, NB = DV / BV, NCT = BV / kTile, NRT = DK / kTile;
+    using Cfg = InterCfg<T, DK, DV, C, BV>;
+    constexpr int NB = Cfg::NB, NRT = Cfg::NRT;
+    constexpr int NSI = Cfg::NSI, SPW = Cfg::SPW, NS = Cfg::NS;
     constexpr int PT = 16 / sizeof(T);
-    constexpr int ST_LD = DK + PT;  // S^T as operand  [BV][DK]
-    constexpr int UT_LD = C + PT;   // U^T as operand  [BV][C]
-    constexpr int KSC = (C + M::K - 1) / M::K;
-    __shared__ __align__(16) T sST[BV * ST_LD];
-    __shared__ __align__(16) T sUT[BV * UT_LD];
+    __shared__ __align__(16) T sST[BV * (DK + PT)];
+    __shared__ __align__(16) T sUT[BV * (C + PT)];
 
     const int H = a.H;
     const int nchains = a.N * H;
@@ -460,11 +823,7 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
         tok_end = clampi(a.cu[n + 1], tok_start, a.T);
     }
 
-    // state tiles (m, nn): rows 16m.., value columns jb + 16nn..; wave-owned
-    constexpr int NSI = NRT * NCT;
-    constexpr int SPW = (NSI + kWaves - 1) / kWaves;
-    constexpr int NXI = NT * NCT;
-    constexpr int XPW = (NXI + kWaves - 1) / kWaves;
+    // fp32 state tiles (m, nn): rows 16m.., value columns jb + 16nn..
     floatx4 S[SPW];
     const size_t sbase = size_t(chain) * DK * DV;
 #pragma unroll
@@ -478,85 +837,37 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
                 S[i][r] = a.h0[sbase + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16];
         }
     }
+    // the initial state must have arrived before the first prefetch is
+    // issued; otherwise every later wait on the loop header drains the ring
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) asm volatile("" : "+v"(S[i]));
 
     T *og = static_cast<T *>(a.o);
-    for (int gc = c_begin; gc < c_end; ++gc) {
-        const int tok0 = tok_start + (gc - c_begin) * C;
-        const int len = min(C, tok_end - tok0);
-        const size_t slot = size_t(gc) * H + h;
-        const T *W = static_cast<const T *>(a.W) + slot * C * DK;
-        const T *Qp = static_cast<const T *>(a.Qp) + slot * C * DK;
-        const T *KtT = static_cast<const T *>(a.KtT) + slot * DK * C;
-        const T *Ut = static_cast<const T *>(a.Ut) + slot * C * DV;
-        const T *Oi = static_cast<const T *>(a.Oi) + slot * C * DV;
-        const float *D = a.D + slot * DK;
-
-        // 1. S^T -> LDS in the operand dtype
+    T *dummy = static_cast<T *>(a.dummy) + tid;
+    InterStage<T, DK, DV, C, BV> st[NS];
+    if (c_begin < c_end) {
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int item = wid + kWaves * i;
-            if (item < NSI) {
-                const int m = item % NRT, nn = item / NRT;
-                store4(sST + (kTile * nn + l16) * ST_LD + kTile * m + 4 * grp, S[i][0], S[i][1], S[i][2], S[i][3]);
-            }
+        for (int s = 0; s < NS - 1; ++s) inter_load(st[s], a, min(c_begin + s, c_end - 1), h, wid, grp, l16, jb);
+    }
+    int gc = c_begin;
+    // full groups of NS chunks, branch-free: the chunk loaded NS-1 steps
+    // ahead is clamped to the last one (a harmless repeated load at the end)
+    for (; gc + NS <= c_end; gc += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            inter_load(st[(s + NS - 1) % NS], a, min(gc + s + NS - 1, c_end - 1), h, wid, grp, l16, jb);
+            const int tok0 = tok_start + (gc + s - c_begin) * C;
+            inter_chunk<T, DK, DV, C, BV>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
+                                          grp, l16, jb);
         }
-        __syncthreads();
-
-        // 2. X = W S and O = Q' S; U = Ut - X -> LDS; o = Oi + O
+    }
+    // the last (c_end - gc) < NS chunks are already in st[0], st[1], ...
 #pragma unroll
-        for (int i = 0; i < XPW; ++i) {
-            const int item = wid + kWaves * i;
-            if (item < NXI) {
-                const int I = item % NT, nn = item / NT;
-                floatx4 ax = zero4(), ao = zero4();
-#pragma unroll
-                for (int kk = 0; kk < DK / M::K; ++kk) {
-                    const int kb = kk * M::K + grp * M::KPL;
-                    const Frag wf = M::load(W + (kTile * I + l16) * DK + kb);
-                    const Frag qf = M::load(Qp + (kTile * I + l16) * DK + kb);
-                    const Frag sf = M::load(sST + (kTile * nn + l16) * ST_LD + kb);
-                    ax = M::mma(wf, sf, ax);
-                    ao = M::mma(qf, sf, ao);
-                }
-                const int j = jb + kTile * nn + l16;
-                const int t0 = kTile * I + 4 * grp;
-                float u[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) u[r] = to_f32(Ut[size_t(t0 + r) * DV + j]) - ax[r];
-                store4(sUT + (kTile * nn + l16) * UT_LD + t0, u[0], u[1], u[2], u[3]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (t0 + r < len)
-                        og[(size_t(tok0 + t0 + r) * H + h) * DV + j] =
-                            from_f32<T>(to_f32(Oi[size_t(t0 + r) * DV + j]) + ao[r]);
-            }
-        }
-        __syncthreads();
-
-        // 3. S = Diag(e^{Gam_last}) S + (k e^{Gam_last - Gam})^T U
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int item = wid + kWaves * i;
-            if (item < NSI) {
-                const int m = item % NRT, nn = item / NRT;
-                floatx4 acc = S[i];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] *= D[kTile * m + 4 * grp + r];
-#pragma unroll
-                for (int kk = 0; kk < KSC; ++kk) {
-                    const int kb = kk * M::K + grp * M::KPL;
-                    Frag af, bf;
-                    if (kb < C) {
-                        af = M::load(KtT + (kTile * m + l16) * C + kb);
-                        bf = M::load(sUT + (kTile * nn + l16) * UT_LD + kb);
-                    } else {
-                        af = Frag{};
-                        bf = Frag{};
-                    }
-                    acc = M::mma(af, bf, acc);
-                }
-                S[i] = acc;
-            }
+    for (int s = 0; s < NS - 1; ++s) {
+        if (gc + s < c_end) {
+            const int tok0 = tok_start + (gc + s - c_begin) * C;
+            inter_chunk<T, DK, DV, C, BV>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
+                                          grp, l16, jb);
         }
     }
 
@@ -589,9 +900,12 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         attr_set = true;
     }
     if (a.nc_max > 0) {
+        // persistent: one workgroup per compute unit (LDS allows one), each
+        // walking (chunk, head) items with its next item's inputs in flight
+        const int items = a.nc_max * a.H;
+        const int grid = items < a.num_cu ? items : a.num_cu;
         prof_begin(s);
-        hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV, C>), dim3(a.nc_max, a.H), dim3(kThreads),
-                           Ly::bytes, s, a);
+        hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV, C>), dim3(grid), dim3(kIThreads), Ly::bytes, s, a);
         prof_end(s, "kda_intra");
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

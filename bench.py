@@ -73,6 +73,54 @@ def load_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+PREFILL_WORKLOAD = "prefill B=1 H=32 T=8192 d=128 bf16 chunk=64"
+DECODE_WORKLOAD = "decode N=256 H=32 d=128 bf16"
+CALIB_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
+
+
+def ingest_pmc(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE; both with --calibration-copy) into profiles/traffic.json:
+    HBM bytes per launch of each KDA kernel, each counter scaled by what it
+    reads for the 1 GiB calibration copy."""
+    import csv
+    import statistics
+
+    def load(d, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = ("kda_intra" if "kda_intra_kernel" in name else "kda_inter" if "kda_inter_kernel" in name
+                       else "kda_decode" if "kda_decode_kernel" in name
+                       else "copy" if "copy" in name.lower() and float(r["Counter_Value"]) > 0 else None)
+                if key:
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    calib_kib = CALIB_BYTES / 1024
+    f_scale = calib_kib / max(fetch["copy"])   # the copy is the largest copy-named dispatch
+    w_scale = calib_kib / max(write["copy"])
+    out = {"calibration": {"copy_bytes": CALIB_BYTES, "fetch_size_kib": max(fetch["copy"]),
+                           "write_size_kib": max(write["copy"]), "fetch_scale": round(f_scale, 4),
+                           "write_scale": round(w_scale, 4)}}
+    for k, wl in (("kda_intra", PREFILL_WORKLOAD), ("kda_inter", PREFILL_WORKLOAD), ("kda_decode", DECODE_WORKLOAD)):
+        if k in fetch and k in write:
+            fk, wk = statistics.mean(fetch[k]), statistics.mean(write[k])
+            out[k] = {"workload": wl, "source_digest": source_digest(), "dispatches": len(fetch[k]),
+                      "fetch_size_kib": round(fk, 1), "write_size_kib": round(wk, 1),
+                      "read_bytes_per_launch": int(fk * 1024 * f_scale),
+                      "write_bytes_per_launch": int(wk * 1024 * w_scale),
+                      "hbm_bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,7 +128,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="finish with a 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs; no GPU needed")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -138,7 +193,7 @@ def main():
     dom = max(per_kernel_us, key=per_kernel_us.get)
     dom_us = per_kernel_us[dom]
     achieved = kernel_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
-    workload = "prefill B=1 H=32 T=8192 d=128 bf16 chunk=64"
+    workload = PREFILL_WORKLOAD
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(dom, workload),
@@ -195,7 +250,7 @@ def main():
               "ms_per_step": round(1e3 * t_pass / dspec.steps, 4),
               "roofline": {"kernel": "kda_decode", "bound": "hbm", "achieved": round(dec_gbs, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                           "traffic": load_traffic("kda_decode", "decode N=256 H=32 d=128 bf16"),
+                           "traffic": load_traffic("kda_decode", DECODE_WORKLOAD),
                            "avg_launch_us": round(dec_launch_us, 2),
                            "algorithmic_bytes_per_launch": dec_bytes}}
 
@@ -234,6 +289,14 @@ def main():
         t_dec_cpu = (time.perf_counter() - t0) / 4
         decode["cpu_baseline"] = {"value": round(1.0 / t_dec_cpu, 3), "unit": "steps/s", "cores": threads,
                                   "kind": "oracle", "sample": "first 4 of the 128 decode steps"}
+
+    if args.calibration_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),

@@ -115,94 +115,117 @@ __device__ __forceinline__ size_t quad_off(int tile_r, int tile_n, int lane) {
     return (size_t(tile_r) * (N / 16) + tile_n) * 256 + lane * 4;
 }
 
-constexpr int kIThreads = 1024;  // kernel 1
-constexpr int kIWaves = kIThreads / kWave;
-
 // ---------------------------------------------------------------------------
 // Kernel 1: intra-chunk work, persistent.  Its LDS footprint allows one
 // workgroup per compute unit, so the workgroup is 16 wavefronts (four per
-// SIMD) to overlap the latencies of its many short dependent steps.  Each workgroup walks (chunk, head)
-// items in chunk-major order; while it computes one item, the raw inputs of
-// its next item are already in flight into registers.  LDS row pitches are
-// chosen so that 16 lanes reading 16 bytes from 16 consecutive rows hit 64
-// distinct banks.
+// SIMD) to overlap the latencies of its dependent steps.  Each workgroup
+// walks (chunk, head) items in chunk-major order; the raw inputs of its next
+// item are loaded into registers while the current one computes, directly
+// in the layout their first consumer wants ("owner" layout):
+//   g, k, q: thread (channel group cg of 4, segment sg of 4 tokens)
+//   v:       thread (channel group jg of 8, segment sg of 4 tokens)
+// so the cumulative decay, every decay-factored operand, the transposes and
+// K~^T come out of registers in one pass, and raw inputs never touch LDS.
 // ---------------------------------------------------------------------------
+constexpr int kIThreads = 1024;
+constexpr int kIWaves = kIThreads / kWave;
+constexpr int kSR = 4;  // tokens per owner segment
+
 template <class T, int DK, int DV, int C>
 struct IntraLds {
     static constexpr int PT = 16 / sizeof(T);  // 16-byte row pad, in elements
-    static constexpr int G_LD = DK + 4;        // fp32 Gam        [C][DK]
-    static constexpr int K_LD = DK + PT;       // k, q (q e^Gam)  [C][DK]
-    static constexpr int KT_LD = C + PT;       // transposed ops  [DK|DV][C]
-    static constexpr int A_LD = C + 4;         // fp32 A, L       [C][C]
-    static constexpr int P_LD = C + PT;        // P               [C][C]
-    static constexpr int Y_LD = 20;            // fp32 16x16 scratch
-    static constexpr size_t oG = 0;
-    static constexpr size_t oK = oG + size_t(C) * G_LD * 4;
-    static constexpr size_t oQ = oK + size_t(C) * K_LD * sizeof(T);
-    static constexpr size_t oB = oQ + size_t(C) * K_LD * sizeof(T);
-    static constexpr size_t oKT = oB + size_t(C) * 4;
-    static constexpr size_t oVT = oKT + size_t(DK) * KT_LD * sizeof(T);
-    // one region holds, in turn: natural v and the K~^T staging, then A and L
-    static constexpr int V_LD = DV + PT;                               // natural v [C][DV]
-    static constexpr size_t oA = oVT + size_t(DV) * KT_LD * sizeof(T);
+    static constexpr int NT = C / kTile, NSEG = C / kSR, NOFF = NT * (NT - 1) / 2;
+    static constexpr int K_LD = DK + PT;        // K+, K-, Q+          [C][DK]
+    static constexpr int KT_LD = C + PT;        // transposed operands [DK|DV][C]
+    static constexpr int A_LD = C + 4;          // fp32 A, L           [C][C]
+    static constexpr int P_LD = C + PT;         // P                   [C][C]
+    static constexpr int Y_LD = 20;             // fp32 16x16 scratch
+    static constexpr size_t kKK = size_t(2) * C * K_LD * sizeof(T);  // K+ and K-
+    static constexpr size_t kAL = size_t(2) * C * A_LD * 4;          // A and L (reuse K+, K-)
+    static constexpr size_t oKp = 0;
+    static constexpr size_t oKm = oKp + size_t(C) * K_LD * sizeof(T);
+    static constexpr size_t oA = 0;
     static constexpr size_t oL = oA + size_t(C) * A_LD * 4;
-    static constexpr size_t oV = oA;
-    static constexpr size_t oKtT = oV + size_t(C) * V_LD * sizeof(T);
-    static constexpr size_t kAL = size_t(2) * C * A_LD * 4;
-    static constexpr size_t kVK = size_t(C) * V_LD * sizeof(T) + size_t(DK) * KT_LD * sizeof(T);
-    static constexpr size_t oP = oA + (kAL > kVK ? kAL : kVK);
+    static constexpr size_t oQp = (kKK > kAL ? kKK : kAL);
+    static constexpr size_t oKT = oQp + size_t(C) * K_LD * sizeof(T);
+    static constexpr size_t oVT = oKT + size_t(DK) * KT_LD * sizeof(T);
+    static constexpr size_t oP = oVT + size_t(DV) * KT_LD * sizeof(T);
     static constexpr size_t oY = oP + size_t(C) * P_LD * sizeof(T);
-    static constexpr size_t oT = oY + size_t(3) * 16 * Y_LD * 4;      // cumsum segment totals
-    static constexpr size_t bytes = oT + size_t(8) * (DK / 4) * 16;
+    static constexpr size_t oTot = oY + size_t(3) * 16 * Y_LD * 4;
+    static constexpr size_t oF = oTot + size_t(NSEG) * DK * 4;
+    static constexpr size_t oR = oF + size_t(NOFF > 0 ? NOFF : 1) * DK * 4;
+    static constexpr size_t oB = oR + size_t(NT) * DK * 4;
+    static constexpr size_t bytes = oB + size_t(C) * 4;
 };
 
-// Raw inputs of one (chunk, head) item as held by one thread.
+template <class T, int DK, int DV, int C>
+struct IntraRoles {
+    static constexpr int NSEG = C / kSR;
+    static constexpr int NG = (DK / 4) * NSEG;  // g/k/q owner threads
+    static constexpr int NV = (DV / 8) * NSEG;  // v owner threads
+    static_assert(NG + NV + DK / 4 <= kIThreads, "owner threads");
+    // raw registers: g (kSR x 16 B) + k, q (kSR rows x 4 values each) for
+    // role G; v (kSR rows x 8 values) for role V
+    static constexpr int GQ = kSR * 4 * 2 * int(sizeof(T)) / 16;  // uint4 for k and q
+    static constexpr int RAW_G = kSR + GQ;
+    static constexpr int RAW_V = kSR * 8 * int(sizeof(T)) / 16;
+    static constexpr int RAW = RAW_G > RAW_V ? RAW_G : RAW_V;
+};
+
 template <class T, int DK, int DV, int C>
 struct IntraIn {
-    static constexpr int EV = 16 / sizeof(T);
-    static constexpr int NKV = (C * DK / EV + kIThreads - 1) / kIThreads;  // k, q vectors per thread
-    static constexpr int NVV = (C * DV / EV + kIThreads - 1) / kIThreads;  // v vectors per thread
-    static constexpr int NGV = (C * DK / 4 + kIThreads - 1) / kIThreads;   // g float4 per thread
-    uint4 k[NKV], q[NKV], v[NVV];
-    float4 g[NGV];
-    float bv[NVV];  // beta of each v row
+    uint4 raw[IntraRoles<T, DK, DV, C>::RAW];
+    float b[kSR];
 };
+
+// four values of T from / to a uint4 register array at element offset e
+template <class T>
+__device__ __forceinline__ float raw_get(const uint4 *raw, int e) {
+    return to_f32(reinterpret_cast<const T *>(raw)[e]);
+}
 
 template <class T, int DK, int DV, int C>
 __device__ __forceinline__ void intra_fetch(IntraIn<T, DK, DV, C> &in, const PrefillArgs &a, const ChunkLoc &loc,
                                             int h, int tid) {
-    using In = IntraIn<T, DK, DV, C>;
-    constexpr int EV = In::EV, KV = DK / EV, VV = DV / EV, GV = DK / 4;
-    const T *kg = static_cast<const T *>(a.k);
-    const T *qg = static_cast<const T *>(a.q);
-    const T *vg = static_cast<const T *>(a.v);
+    using R = IntraRoles<T, DK, DV, C>;
     const int H = a.H;
+    if (tid < R::NG) {
+        const int cg = tid % (DK / 4), sg = tid / (DK / 4);
+        const T *kg = static_cast<const T *>(a.k);
+        const T *qg = static_cast<const T *>(a.q);
 #pragma unroll
-    for (int u = 0; u < In::NKV; ++u) {
-        const int idx = tid + kIThreads * u, t = idx / KV, cv = idx % KV;
-        in.k[u] = in.q[u] = make_uint4(0, 0, 0, 0);
-        if (idx < C * KV && t < loc.len) {
-            const size_t off = (size_t(loc.tok0 + t) * H + h) * DK + cv * EV;
-            in.k[u] = *reinterpret_cast<const uint4 *>(kg + off);
-            in.q[u] = *reinterpret_cast<const uint4 *>(qg + off);
+        for (int r = 0; r < kSR; ++r) {
+            const int t = kSR * sg + r;
+            const bool ok = t < loc.len;
+            const size_t row = size_t(loc.tok0 + t) * H + h;
+            in.raw[r] = ok ? *reinterpret_cast<const uint4 *>(a.g + row * DK + 4 * cg) : make_uint4(0, 0, 0, 0);
+            in.b[r] = ok ? a.beta[row] : 0.f;
+            if constexpr (sizeof(T) == 2) {  // k and q: 8 bytes each, packed into one uint4
+                uint2 kk = ok ? *reinterpret_cast<const uint2 *>(kg + row * DK + 4 * cg) : make_uint2(0, 0);
+                uint2 qq = ok ? *reinterpret_cast<const uint2 *>(qg + row * DK + 4 * cg) : make_uint2(0, 0);
+                in.raw[kSR + r] = make_uint4(kk.x, kk.y, qq.x, qq.y);
+            } else {
+                in.raw[kSR + r] = ok ? *reinterpret_cast<const uint4 *>(kg + row * DK + 4 * cg) : make_uint4(0, 0, 0, 0);
+                in.raw[2 * kSR + r] = ok ? *reinterpret_cast<const uint4 *>(qg + row * DK + 4 * cg) : make_uint4(0, 0, 0, 0);
+            }
         }
-    }
+    } else if (tid < R::NG + R::NV) {
+        const int u = tid - R::NG;
+        const int jg = u % (DV / 8), sg = u / (DV / 8);
+        const T *vg = static_cast<const T *>(a.v);
+        constexpr int VW = 8 * int(sizeof(T)) / 16;  // uint4 per 8 values
 #pragma unroll
-    for (int u = 0; u < In::NVV; ++u) {
-        const int idx = tid + kIThreads * u, t = idx / VV, cv = idx % VV;
-        in.v[u] = make_uint4(0, 0, 0, 0);
-        in.bv[u] = 0.f;
-        if (idx < C * VV && t < loc.len) {
-            in.v[u] = *reinterpret_cast<const uint4 *>(vg + (size_t(loc.tok0 + t) * H + h) * DV + cv * EV);
-            in.bv[u] = a.beta[size_t(loc.tok0 + t) * H + h];
+        for (int r = 0; r < kSR; ++r) {
+            const int t = kSR * sg + r;
+            const bool ok = t < loc.len;
+            const size_t row = size_t(loc.tok0 + t) * H + h;
+#pragma unroll
+            for (int w = 0; w < VW; ++w)
+                in.raw[r * VW + w] =
+                    ok ? *reinterpret_cast<const uint4 *>(vg + row * DV + 8 * jg + w * (16 / sizeof(T)))
+                       : make_uint4(0, 0, 0, 0);
+            in.b[r] = ok ? a.beta[row] : 0.f;
         }
-    }
-#pragma unroll
-    for (int u = 0; u < In::NGV; ++u) {
-        const int idx = tid + kIThreads * u, t = idx / GV, cv = idx % GV;
-        in.g[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (idx < C * GV && t < loc.len)
-            in.g[u] = *reinterpret_cast<const float4 *>(a.g + (size_t(loc.tok0 + t) * H + h) * DK + cv * 4);
     }
 }
 
@@ -220,31 +243,43 @@ __device__ __forceinline__ void lds_read8(const float *p, float (&x)[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// 8 consecutive values of T to LDS or global memory (16 bytes for bf16)
+__device__ __forceinline__ void store8(bf16 *p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(x[i]);
+    *reinterpret_cast<bf16x8 *>(p) = v;
+}
+__device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
+    store4(p, x[0], x[1], x[2], x[3]);
+    store4(p + 4, x[4], x[5], x[6], x[7]);
+}
+
 template <class T, int DK, int DV, int C>
 __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     using Ly = IntraLds<T, DK, DV, C>;
+    using R = IntraRoles<T, DK, DV, C>;
     using In = IntraIn<T, DK, DV, C>;
     using M = Mma<T>;
     typedef typename M::Frag Frag;
-    constexpr int NT = C / kTile;
-    constexpr int G_LD = Ly::G_LD, K_LD = Ly::K_LD, KT_LD = Ly::KT_LD;
+    constexpr int NT = C / kTile, NSEG = Ly::NSEG;
+    constexpr int K_LD = Ly::K_LD, KT_LD = Ly::KT_LD;
     constexpr int A_LD = Ly::A_LD, P_LD = Ly::P_LD, Y_LD = Ly::Y_LD;
-    constexpr int EV = In::EV, KV = DK / EV, VV = DV / EV, GV = DK / 4;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    float *sG = reinterpret_cast<float *>(smem + Ly::oG);
-    T *sK = reinterpret_cast<T *>(smem + Ly::oK);
-    T *sQ = reinterpret_cast<T *>(smem + Ly::oQ);   // q, later q e^Gam
-    float *sB = reinterpret_cast<float *>(smem + Ly::oB);
-    T *sKT = reinterpret_cast<T *>(smem + Ly::oKT);  // (beta k e^Gam)^T, later W^T
-    T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);  // (beta v)^T,       later Ut^T
-    T *sKtT = reinterpret_cast<T *>(smem + Ly::oKtT);  // (k e^{Gam_last-Gam})^T staging
-    T *sV = reinterpret_cast<T *>(smem + Ly::oV);      // natural v staging
+    T *sKp = reinterpret_cast<T *>(smem + Ly::oKp);    // k e^{Gam - r_I}   (<= 1)
+    T *sKm = reinterpret_cast<T *>(smem + Ly::oKm);    // k e^{r_I - Gam}   (<= e^80)
+    T *sQp = reinterpret_cast<T *>(smem + Ly::oQp);    // q e^{Gam - r_I}   (<= 1)
+    T *sKT = reinterpret_cast<T *>(smem + Ly::oKT);    // (beta k e^Gam)^T, later W^T
+    T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);    // (beta v)^T,       later Ut^T
     float *sA = reinterpret_cast<float *>(smem + Ly::oA);
     float *sL = reinterpret_cast<float *>(smem + Ly::oL);
     T *sP = reinterpret_cast<T *>(smem + Ly::oP);
     float *sY = reinterpret_cast<float *>(smem + Ly::oY);
-    float4 *sTot = reinterpret_cast<float4 *>(smem + Ly::oT);
+    float *sTot = reinterpret_cast<float *>(smem + Ly::oTot);  // per-segment decay totals [NSEG][DK]
+    float *sF = reinterpret_cast<float *>(smem + Ly::oF);      // e^{r_I - r_J}, J < I    [NOFF][DK]
+    float *sR = reinterpret_cast<float *>(smem + Ly::oR);      // e^{r_I}                 [NT][DK]
+    float *sB = reinterpret_cast<float *>(smem + Ly::oB);
 
     const int H = a.H;
     const int nitems = a.nc_max * H;
@@ -265,182 +300,164 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const int grp = lane >> 4, l16 = lane & 15;
         const int gc = item / H, h = item % H;
         const size_t slot = size_t(gc) * H + h;
-        const ChunkLoc cur = loc;
 
-        // ---- stage the raw inputs (tail rows are neutral zeros) ----
+        // ---- cumulative log-decay: per-thread partial sums over kSR tokens ----
+        float G[kSR][4];
+        if (tid < R::NG) {
+            const int cg = tid % (DK / 4), sg = tid / (DK / 4);
+            float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < In::NKV; ++u) {
-            const int idx = tid + kIThreads * u, t = idx / KV, cv = idx % KV;
-            if (idx < C * KV) {
-                *reinterpret_cast<uint4 *>(sK + t * K_LD + cv * EV) = in.k[u];
-                *reinterpret_cast<uint4 *>(sQ + t * K_LD + cv * EV) = in.q[u];
+            for (int r = 0; r < kSR; ++r) {
+                const float4 g4 = *reinterpret_cast<const float4 *>(&in.raw[r]);
+                run[0] += g4.x; run[1] += g4.y; run[2] += g4.z; run[3] += g4.w;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) G[r][c] = run[c];
+            }
+            *reinterpret_cast<float4 *>(sTot + sg * DK + 4 * cg) = make_float4(run[0], run[1], run[2], run[3]);
+        }
+        __syncthreads();
+
+        // ---- decay-factored operands, transposes and K~^T, from registers ----
+        if (tid < R::NG) {
+            const int cg = tid % (DK / 4), sg = tid / (DK / 4), c0 = 4 * cg;
+            const int I = sg / (kTile / kSR);  // 16-token tile of this segment
+            float off[4] = {0.f, 0.f, 0.f, 0.f}, rI[4] = {0.f, 0.f, 0.f, 0.f}, gl[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+            for (int s2 = 0; s2 < NSEG; ++s2) {
+                const float4 x = *reinterpret_cast<const float4 *>(sTot + s2 * DK + c0);
+                const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (s2 < sg) off[c] += xv[c];
+                    if (s2 < (kTile / kSR) * I) rI[c] += xv[c];
+                    gl[c] += xv[c];
+                }
+            }
+            // rows: K+, K-, Q+ (row-major, four channels per store)
+#pragma unroll
+            for (int r = 0; r < kSR; ++r) {
+                const int t = kSR * sg + r;
+                float kp[4], km[4], qp[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float gam = G[r][c] + off[c];
+                    const float kv = raw_get<T>(in.raw + kSR, (sizeof(T) == 2 ? 8 * r : 4 * r) + c);
+                    const float qv = sizeof(T) == 2 ? raw_get<T>(in.raw + kSR, 8 * r + 4 + c)
+                                                    : raw_get<T>(in.raw + 2 * kSR, 4 * r + c);
+                    const float e = exp_e(gam - rI[c]);   // <= 1
+                    const float ei = exp_e(rI[c] - gam);  // <= e^80 (the decay bound)
+                    kp[c] = kv * e;
+                    qp[c] = qv * e;
+                    km[c] = kv * ei;
+                }
+                store4(sKp + t * K_LD + c0, kp[0], kp[1], kp[2], kp[3]);
+                store4(sKm + t * K_LD + c0, km[0], km[1], km[2], km[3]);
+                store4(sQp + t * K_LD + c0, qp[0], qp[1], qp[2], qp[3]);
+                if (cg == 0) sB[t] = in.b[r];
+            }
+            // channels: (beta k e^Gam)^T to LDS and K~^T to HBM, 4 tokens per store
+            T *KtT = static_cast<T *>(a.KtT) + slot * DK * kpad<T>(C);
+            static_assert(kSR == 4, "column stores are four tokens wide");
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float bke[4], ktv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gam = G[r][c] + off[c];
+                    const float kv = raw_get<T>(in.raw + kSR, (sizeof(T) == 2 ? 8 * r : 4 * r) + c);
+                    bke[r] = in.b[r] * kv * exp_e(gam);
+                    ktv[r] = kv * exp_e(gl[c] - gam);
+                }
+                store4(sKT + (c0 + c) * KT_LD + kSR * sg, bke[0], bke[1], bke[2], bke[3]);
+                store_frag4<T, C>(KtT, c0 + c, kSR * sg, ktv[0], ktv[1], ktv[2], ktv[3]);
+            }
+        } else if (tid < R::NG + R::NV) {
+            const int u = tid - R::NG;
+            const int jg = u % (DV / 8), sg = u / (DV / 8);
+            constexpr int VW = 8 * int(sizeof(T)) / 16;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, in.b[0] * raw_get<T>(in.raw, j),
+                       in.b[1] * raw_get<T>(in.raw + VW, j), in.b[2] * raw_get<T>(in.raw + 2 * VW, j),
+                       in.b[3] * raw_get<T>(in.raw + 3 * VW, j));
+        } else if (tid < R::NG + R::NV + DK / 4) {
+            // e^{Gam_last}, e^{r_I} and the tile-pair factors e^{r_I - r_J}
+            const int c0 = 4 * (tid - R::NG - R::NV);
+            float rr[NT][4];  // r_I: decay accumulated before tile I
+            float gl[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int I2 = 0; I2 < NT; ++I2)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) rr[I2][c] = 0.f;
+#pragma unroll 1
+            for (int s2 = 0; s2 < NSEG; ++s2) {
+                const float4 x = *reinterpret_cast<const float4 *>(sTot + s2 * DK + c0);
+                const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int I2 = 1; I2 < NT; ++I2)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (s2 < (kTile / kSR) * I2) rr[I2][c] += xv[c];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) gl[c] += xv[c];
+            }
+            *reinterpret_cast<float4 *>(a.D + slot * DK + c0) =
+                make_float4(exp_e(gl[0]), exp_e(gl[1]), exp_e(gl[2]), exp_e(gl[3]));
+#pragma unroll
+            for (int I2 = 0; I2 < NT; ++I2) {
+                *reinterpret_cast<float4 *>(sR + I2 * DK + c0) =
+                    make_float4(exp_e(rr[I2][0]), exp_e(rr[I2][1]), exp_e(rr[I2][2]), exp_e(rr[I2][3]));
+#pragma unroll
+                for (int J2 = 0; J2 < I2; ++J2)
+                    *reinterpret_cast<float4 *>(sF + (I2 * (I2 - 1) / 2 + J2) * DK + c0) =
+                        make_float4(exp_e(rr[I2][0] - rr[J2][0]), exp_e(rr[I2][1] - rr[J2][1]),
+                                    exp_e(rr[I2][2] - rr[J2][2]), exp_e(rr[I2][3] - rr[J2][3]));
             }
         }
-#pragma unroll
-        for (int u = 0; u < In::NGV; ++u) {
-            const int idx = tid + kIThreads * u, t = idx / GV, cv = idx % GV;
-            if (idx < C * GV) *reinterpret_cast<float4 *>(sG + t * G_LD + cv * 4) = in.g[u];
-        }
-#pragma unroll
-        for (int u = 0; u < In::NVV; ++u) {
-            const int idx = tid + kIThreads * u, t = idx / VV, jv = idx % VV;
-            if (idx < C * VV) {
-                *reinterpret_cast<uint4 *>(sV + t * Ly::V_LD + jv * EV) = in.v[u];
-                if (jv == 0) sB[t] = in.bv[u];
-            }
-        }
-        // ---- prefetch the next item's inputs while this one computes ----
+        // ---- the next item's inputs go in flight now ----
         int nxt = item + gridDim.x;
         while (nxt < nitems && !locate_chunk(a, nxt / H, C, loc)) nxt += gridDim.x;
         if (nxt < nitems) intra_fetch(in, a, loc, nxt % H, tid);
         __syncthreads();
 
-        // ---- Gam = cumulative log-decay along the chunk, per channel ----
-        {
-            constexpr int NCG = DK / 4;                                   // float4 channel groups
-            constexpr int NSEG0 = (kIThreads / NCG) < 8 ? (kIThreads / NCG) : 8;  // segments per channel
-            constexpr int NSEG = NSEG0 < C ? NSEG0 : C;
-            constexpr int SL = C / NSEG;
-            const int cg = tid % NCG, seg = tid / NCG;
-            float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (seg < NSEG) {
-#pragma unroll
-                for (int r = 0; r < SL; ++r) {
-                    float4 *p = reinterpret_cast<float4 *>(sG + (seg * SL + r) * G_LD + cg * 4);
-                    const float4 x = *p;
-                    run.x += x.x; run.y += x.y; run.z += x.z; run.w += x.w;
-                    *p = run;
-                }
-                sTot[seg * NCG + cg] = run;
-            }
-            __syncthreads();
-            if (seg < NSEG && seg > 0) {
-                float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int s2 = 0; s2 < seg; ++s2) {
-                    const float4 x = sTot[s2 * NCG + cg];
-                    off.x += x.x; off.y += x.y; off.z += x.z; off.w += x.w;
-                }
-#pragma unroll
-                for (int r = 0; r < SL; ++r) {
-                    float4 *p = reinterpret_cast<float4 *>(sG + (seg * SL + r) * G_LD + cg * 4);
-                    float4 x = *p;
-                    x.x += off.x; x.y += off.y; x.z += off.z; x.w += off.w;
-                    *p = x;
-                }
-            }
-            __syncthreads();
-        }
-
         // ---- A (strictly lower, row-scaled by beta) and P (lower incl.) on
-        //      MFMA, one 16x16 tile pair (I, J <= I) per wave, while the
-        //      remaining waves do the elementwise transposes:
-        //      (beta k e^Gam)^T, the K~^T staging and (beta v)^T ----
+        //      MFMA, one 16x16 tile pair (I, J <= I) per wave.  Operands are
+        //      K+ and Q+ of tile I and K- of tile J, times e^{r_I - r_J} when
+        //      J < I; on the diagonal the column operand is <= e^80. ----
         constexpr int NPAIR = NT * (NT + 1) / 2;
-        static_assert(NPAIR < kIWaves, "A/P tile pairs must leave waves for the elementwise work");
+        static_assert(NPAIR <= kIWaves, "A/P tile pairs");
         floatx4 accA = zero4(), accP = zero4();
         if (wid < NPAIR) {
             int I = 0, rem = wid;
             while (rem > I) { rem -= I + 1; ++I; }
             const int J = rem;
-            const int row = kTile * I + l16;  // token t of the A fragment
-            const int col = kTile * J + l16;  // token s of the B fragment
-            const float *gref = sG + (I > 0 ? kTile * I - 1 : 0) * G_LD;  // r_I: row before tile I
-#pragma unroll 1
+            const int row = kTile * I + l16, col = kTile * J + l16;
+            const float *fIJ = sF + (I * (I - 1) / 2 + J) * DK;
+#pragma unroll 2
             for (int kk = 0; kk < DK / M::K; ++kk) {
                 const int cb = kk * M::K + grp * M::KPL;
-                Frag fk, fq, fb;
-                if constexpr (M::KPL == 8) {
-                    float gr[8], gc8[8], rr[8];
-                    lds_read8(sG + row * G_LD + cb, gr);
-                    lds_read8(sG + col * G_LD + cb, gc8);
-                    if (I > 0) lds_read8(gref + cb, rr);
-                    else {
+                const Frag fk = M::load(sKp + row * K_LD + cb);
+                const Frag fq = M::load(sQp + row * K_LD + cb);
+                Frag fb = M::load(sKm + col * K_LD + cb);
+                if (J < I) {
+                    if constexpr (M::KPL == 8) {
+                        float f8[8];
+                        lds_read8(fIJ + cb, f8);
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) rr[j] = 0.f;
+                        for (int j = 0; j < 8; ++j) M::set(fb, j, to_f32(fb[j]) * f8[j]);
+                    } else {
+                        M::set(fb, 0, fb * fIJ[cb]);
                     }
-                    const Frag kr = M::load(sK + row * K_LD + cb);
-                    const Frag qr = M::load(sQ + row * K_LD + cb);
-                    const Frag kc = M::load(sK + col * K_LD + cb);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float ea = exp_e(gr[j] - rr[j]);   // <= 1
-                        const float eb = exp_e(rr[j] - gc8[j]);  // <= e^80
-                        M::set(fk, j, to_f32(kr[j]) * ea);
-                        M::set(fq, j, to_f32(qr[j]) * ea);
-                        M::set(fb, j, to_f32(kc[j]) * eb);
-                    }
-                } else {
-                    const float r = (I > 0) ? gref[cb] : 0.f;
-                    const float ea = exp_e(sG[row * G_LD + cb] - r);
-                    const float eb = exp_e(r - sG[col * G_LD + cb]);
-                    M::set(fk, 0, to_f32(sK[row * K_LD + cb]) * ea);
-                    M::set(fq, 0, to_f32(sQ[row * K_LD + cb]) * ea);
-                    M::set(fb, 0, to_f32(sK[col * K_LD + cb]) * eb);
                 }
                 accA = M::mma(fk, fb, accA);
                 accP = M::mma(fq, fb, accP);
             }
-        } else {
-            // a thread reads 8 channels of one token; consecutive lanes take
-            // consecutive tokens, so each transposed row write is contiguous
-            constexpr int NK8 = C * DK / 8, NV8 = C * DV / 8;
-            constexpr int ET = (kIWaves - NPAIR) * kWave;
-            for (int idx = tid - NPAIR * kWave; idx < NK8 + NV8; idx += ET) {
-                if (idx < NK8) {
-                    const int t = idx % C, c0 = 8 * (idx / C);
-                    float gt[8], gl[8];
-                    lds_read8(sG + t * G_LD + c0, gt);
-                    lds_read8(sG + (C - 1) * G_LD + c0, gl);
-                    const float bt = sB[t];
-                    Vec16<T> kx[8 / EV];
-#pragma unroll
-                    for (int w = 0; w < 8 / EV; ++w) kx[w].raw = *reinterpret_cast<const uint4 *>(sK + t * K_LD + c0 + w * EV);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float kv = kx[e / EV].get(e % EV);
-                        sKT[(c0 + e) * KT_LD + t] = from_f32<T>(bt * kv * exp_e(gt[e]));
-                        sKtT[(c0 + e) * KT_LD + t] = from_f32<T>(kv * exp_e(gl[e] - gt[e]));
-                    }
-                } else {
-                    const int e8 = idx - NK8;
-                    const int t = e8 % C, j0 = 8 * (e8 / C);
-                    const float bt = sB[t];
-                    Vec16<T> vx[8 / EV];
-#pragma unroll
-                    for (int w = 0; w < 8 / EV; ++w) vx[w].raw = *reinterpret_cast<const uint4 *>(sV + t * Ly::V_LD + j0 + w * EV);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sVT[(j0 + e) * KT_LD + t] = from_f32<T>(bt * vx[e / EV].get(e % EV));
-                }
-            }
-            if (tid - NPAIR * kWave < DK) {
-                const int c = tid - NPAIR * kWave;
-                a.D[slot * DK + c] = exp_e(sG[(C - 1) * G_LD + c]);
-            }
         }
-        __syncthreads();
-        {   // K~^T out, operand order: 4 consecutive tokens per store
-            T *KtT = static_cast<T *>(a.KtT) + slot * DK * kpad<T>(C);
-            constexpr int NV4 = DK * C / 4;
-            for (int idx = tid; idx < NV4; idx += kIThreads) {
-                const int c = idx / (C / 4), t0 = 4 * (idx % (C / 4));
-                const T *p = sKtT + c * KT_LD + t0;
-                store_frag4<T, C>(KtT, c, t0, to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3]));
-            }
-        }
-        // q e^Gam in place (the output's state-free part subtracts P W from it)
-        for (int idx = tid; idx < C * DK / 4; idx += kIThreads) {
-            const int t = idx / (DK / 4), c0 = 4 * (idx % (DK / 4));
-            const float4 g4 = *reinterpret_cast<const float4 *>(sG + t * G_LD + c0);
-            T *p = sQ + t * K_LD + c0;
-            store4(p, to_f32(p[0]) * exp_e(g4.x), to_f32(p[1]) * exp_e(g4.y), to_f32(p[2]) * exp_e(g4.z),
-                   to_f32(p[3]) * exp_e(g4.w));
-        }
-        __syncthreads();  // the K~^T staging is copied out: its LDS becomes A and L
-        for (int i = tid; i < C * A_LD; i += kIThreads) sL[i] = 0.f;
+        __syncthreads();  // K+ and K- are dead: their LDS becomes A and L
         for (int i = tid; i < C * C; i += kIThreads) {  // tiles above the diagonal
             const int t = i / C, s = i - t * C;
             if ((s >> 4) > (t >> 4)) {
-                sA[t * A_LD + s] = 0.f;
+                sL[t * A_LD + s] = 0.f;
                 sP[t * P_LD + s] = from_f32<T>(0.f);
             }
         }
@@ -607,10 +624,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                         acc = M::mma(fa, fb, acc);
                     }
                     if (isW) {
+                        // q e^Gam = Q+ e^{r_I} (token tile tt)
                         const int t = kTile * tt + l16, c0 = kTile * cc + 4 * grp;
-                        const T *qp = sQ + t * K_LD + c0;
-                        store_frag4<T, DK>(Qg, t, c0, to_f32(qp[0]) - acc[0], to_f32(qp[1]) - acc[1],
-                                           to_f32(qp[2]) - acc[2], to_f32(qp[3]) - acc[3]);
+                        const T *qp = sQp + t * K_LD + c0;
+                        const float4 er = *reinterpret_cast<const float4 *>(sR + tt * DK + c0);
+                        store_frag4<T, DK>(Qg, t, c0, to_f32(qp[0]) * er.x - acc[0], to_f32(qp[1]) * er.y - acc[1],
+                                           to_f32(qp[2]) * er.z - acc[2], to_f32(qp[3]) * er.w - acc[3]);
                     } else {
                         store4(Og + quad_off<DV>(tt, cc, lane), acc[0], acc[1], acc[2], acc[3]);
                     }
@@ -619,7 +638,6 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         }
         __syncthreads();  // LDS is restaged for the next item
         item = nxt;
-        (void)cur;
     }
 }
 

@@ -23,6 +23,8 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kTile = 16;  // MFMA tile edge, and the 16-token decay tile
@@ -93,6 +95,27 @@ __device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
     *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
+
+// Four consecutive values of one column (four tokens of a channel), rounded
+// to T as they are produced, so that fewer registers hold them until the
+// column is stored at once.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <class T> struct Col4 {
+    float v[4];
+    __device__ __forceinline__ void set(int r, float x) { v[r] = x; }
+    __device__ __forceinline__ void store(T *p) const { store4(p, v[0], v[1], v[2], v[3]); }
+};
+template <> struct Col4<bf16> {
+    bf16x2 h[2];
+    float lo;
+    __device__ __forceinline__ void set(int r, float x) {
+        if (r & 1) h[r >> 1] = bf16x2{static_cast<bf16>(lo), static_cast<bf16>(x)};
+        else lo = x;
+    }
+    __device__ __forceinline__ void store(bf16 *p) const {
+        *reinterpret_cast<bf16x4 *>(p) = bf16x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+    }
+};
 
 // 16-byte vector of T (8 bf16 or 4 fp32) for coalesced global <-> LDS copies.
 template <class T> struct Vec16 {

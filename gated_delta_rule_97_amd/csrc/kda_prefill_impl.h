@@ -48,6 +48,13 @@ struct ChunkLoc {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// A read-only int of the chunk map or cu_seqlens, through the constant
+// address space: with a wave-uniform index it becomes a scalar load, which
+// does not wait behind the wave's outstanding vector stores.
+__device__ __forceinline__ int ld_const(const int32_t *p, int i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
+}
+
 __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C, ChunkLoc &out) {
     if (!a.cu) {
         const int n = gc / a.nc_seq, ci = gc - n * a.nc_seq;
@@ -57,16 +64,16 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C
         out.len = min(C, a.T - ci * C);
         return out.len > 0;
     }
-    if (gc >= a.coff[a.N]) return false;
+    if (gc >= ld_const(a.coff, a.N)) return false;
     int lo = 0, hi = a.N;  // coff[lo] <= gc < coff[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (a.coff[mid] <= gc) lo = mid; else hi = mid;
+        if (ld_const(a.coff, mid) <= gc) lo = mid; else hi = mid;
     }
-    const int s = clampi(a.cu[lo], 0, a.T);
-    const int e = clampi(a.cu[lo + 1], s, a.T);
+    const int s = clampi(ld_const(a.cu, lo), 0, a.T);
+    const int e = clampi(ld_const(a.cu, lo + 1), s, a.T);
     out.seq = lo;
-    out.tok0 = s + (gc - a.coff[lo]) * C;
+    out.tok0 = s + (gc - ld_const(a.coff, lo)) * C;
     out.len = min(C, e - out.tok0);
     return out.len > 0;
 }
@@ -152,7 +159,7 @@ struct IntraLds {
     static constexpr size_t oP = oVT + size_t(DV) * KT_LD * sizeof(T);
     static constexpr size_t oY = oP + size_t(C) * P_LD * sizeof(T);
     static constexpr size_t oTot = oY + size_t(3) * 16 * Y_LD * 4;
-    static constexpr size_t oF = oTot + size_t(NSEG) * DK * 4;
+    static constexpr size_t oF = oTot + size_t(NSEG + 1) * DK * 4;
     static constexpr size_t oR = oF + size_t(NOFF > 0 ? NOFF : 1) * DK * 4;
     static constexpr size_t oB = oR + size_t(NT) * DK * 4;
     static constexpr size_t bytes = oB + size_t(C) * 4;
@@ -163,69 +170,138 @@ struct IntraRoles {
     static constexpr int NSEG = C / kSR;
     static constexpr int NG = (DK / 4) * NSEG;  // g/k/q owner threads
     static constexpr int NV = (DV / 8) * NSEG;  // v owner threads
-    static_assert(NG + NV + DK / 4 <= kIThreads, "owner threads");
+    static_assert(NG + NV + DK <= kIThreads, "owner and scan threads");
     // raw registers: g (kSR x 16 B) + k, q (kSR rows x 4 values each) for
     // role G; v (kSR rows x 8 values) for role V
-    static constexpr int GQ = kSR * 4 * 2 * int(sizeof(T)) / 16;  // uint4 for k and q
+    static constexpr int GQ = kSR * 4 * 2 * int(sizeof(T)) / 16;  // 16-byte registers for k and q
     static constexpr int RAW_G = kSR + GQ;
     static constexpr int RAW_V = kSR * 8 * int(sizeof(T)) / 16;
     static constexpr int RAW = RAW_G > RAW_V ? RAW_G : RAW_V;
+    // whole wavefronts per role: role branches can then be uniform
+    static constexpr bool ALIGNED = NG % kWave == 0 && NV % kWave == 0;
 };
+
+// The thread index used for role tests.  When every role covers whole
+// wavefronts this is the wave's first lane, read into a scalar register, so
+// role branches are uniform jumps instead of lane masks: the compiler then
+// sees the roles as exclusive paths (otherwise it must assume a wave runs
+// one role's code after the other's, and it serialises their loads).
+template <class T, int DK, int DV, int C>
+__device__ __forceinline__ int role_tid(int tid) {
+    if constexpr (IntraRoles<T, DK, DV, C>::ALIGNED) return __builtin_amdgcn_readfirstlane(tid);
+    else return tid;
+}
 
 template <class T, int DK, int DV, int C>
 struct IntraIn {
-    uint4 raw[IntraRoles<T, DK, DV, C>::RAW];
+    u32x4 raw[IntraRoles<T, DK, DV, C>::RAW];  // 16 bytes each, as loaded
     float b[kSR];
+    int len;  // valid tokens of the chunk; rows at or past it are zeroed on use
 };
 
-// four values of T from / to a uint4 register array at element offset e
+// Element e of an array of 16-byte registers holding values of T, by bit
+// operations on its 32-bit words (e is a constant after unrolling).  Reading
+// through a T pointer instead would let the compiler split the words into
+// 16-bit pieces right where they are loaded.
+__device__ __forceinline__ unsigned raw_word(const u32x4 &x, int i) { return x[i]; }
 template <class T>
-__device__ __forceinline__ float raw_get(const uint4 *raw, int e) {
-    return to_f32(reinterpret_cast<const T *>(raw)[e]);
+__device__ __forceinline__ float raw_get(const u32x4 *raw, int e) {
+    if constexpr (sizeof(T) == 2) {
+        const unsigned w = raw_word(raw[e >> 3], (e >> 1) & 3);
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        return __uint_as_float(raw_word(raw[e >> 2], e & 3));
+    }
 }
 
+// Owner coordinates: role G threads own (channel group cg of 4, segment sg),
+// role V threads (channel group jg of 8, segment sg).
+template <class T, int DK, int DV, int C>
+__device__ __forceinline__ void owner_coords(int tid, bool &is_g, int &cgrp, int &sg) {
+    using R = IntraRoles<T, DK, DV, C>;
+    is_g = tid < R::NG;
+    const int u = is_g ? tid : tid - R::NG;
+    cgrp = is_g ? u % (DK / 4) : u % (DV / 8);
+    sg = is_g ? u / (DK / 4) : u / (DV / 8);
+}
+
+// Value j (0..7) of token r of a role V thread.  Registers: raw[r] holds
+// the first 16 bytes of its 8 values, raw[kSR + r] the next 16 (fp32 only).
+template <class T, int DK, int DV, int C>
+__device__ __forceinline__ float v_get(const IntraIn<T, DK, DV, C> &in, int r, int j) {
+    if constexpr (sizeof(T) == 2) return raw_get<T>(in.raw + r, j);
+    else return j < 4 ? raw_get<T>(in.raw + r, j) : raw_get<T>(in.raw + kSR + r, j - 4);
+}
+
+// The G and V roles issue the same load instructions with role-selected
+// addresses (a V thread's unused k/q slots re-read its own v row), and the
+// loads are unconditional: rows past the chunk end re-read its last row and
+// are zeroed when consumed, after intra_fence.  A per-role or per-row branch
+// around the loads would make the compiler merge their registers with other
+// paths and wait for the data right where it is requested.
 template <class T, int DK, int DV, int C>
 __device__ __forceinline__ void intra_fetch(IntraIn<T, DK, DV, C> &in, const PrefillArgs &a, const ChunkLoc &loc,
                                             int h, int tid) {
     using R = IntraRoles<T, DK, DV, C>;
     const int H = a.H;
-    if (tid < R::NG) {
-        const int cg = tid % (DK / 4), sg = tid / (DK / 4);
-        const T *kg = static_cast<const T *>(a.k);
-        const T *qg = static_cast<const T *>(a.q);
+    in.len = loc.len;
+    if (role_tid<T, DK, DV, C>(tid) < R::NG + R::NV) {
+        bool is_g;
+        int cgrp, sg;
+        owner_coords<T, DK, DV, C>(tid, is_g, cgrp, sg);
 #pragma unroll
         for (int r = 0; r < kSR; ++r) {
-            const int t = kSR * sg + r;
-            const bool ok = t < loc.len;
+            const int t = min(kSR * sg + r, loc.len - 1);
             const size_t row = size_t(loc.tok0 + t) * H + h;
-            in.raw[r] = ok ? *reinterpret_cast<const uint4 *>(a.g + row * DK + 4 * cg) : make_uint4(0, 0, 0, 0);
-            in.b[r] = ok ? a.beta[row] : 0.f;
-            if constexpr (sizeof(T) == 2) {  // k and q: 8 bytes each, packed into one uint4
-                uint2 kk = ok ? *reinterpret_cast<const uint2 *>(kg + row * DK + 4 * cg) : make_uint2(0, 0);
-                uint2 qq = ok ? *reinterpret_cast<const uint2 *>(qg + row * DK + 4 * cg) : make_uint2(0, 0);
-                in.raw[kSR + r] = make_uint4(kk.x, kk.y, qq.x, qq.y);
+            const char *pv = reinterpret_cast<const char *>(static_cast<const T *>(a.v) + row * DV + 8 * cgrp);
+            const char *p16 = is_g ? reinterpret_cast<const char *>(a.g + row * DK + 4 * cgrp) : pv;
+            const char *pk = is_g ? reinterpret_cast<const char *>(static_cast<const T *>(a.k) + row * DK + 4 * cgrp)
+                                  : pv + (sizeof(T) == 4 ? 16 : 0);
+            const char *pq = is_g ? reinterpret_cast<const char *>(static_cast<const T *>(a.q) + row * DK + 4 * cgrp)
+                                  : pv;
+            in.raw[r] = *reinterpret_cast<const u32x4 *>(p16);
+            in.b[r] = a.beta[row];
+            if constexpr (sizeof(T) == 2) {  // k and q: 8 bytes each, packed into one register
+                const u32x2 kk = *reinterpret_cast<const u32x2 *>(pk);
+                const u32x2 qq = *reinterpret_cast<const u32x2 *>(pq);
+                in.raw[kSR + r] = u32x4{kk[0], kk[1], qq[0], qq[1]};
             } else {
-                in.raw[kSR + r] = ok ? *reinterpret_cast<const uint4 *>(kg + row * DK + 4 * cg) : make_uint4(0, 0, 0, 0);
-                in.raw[2 * kSR + r] = ok ? *reinterpret_cast<const uint4 *>(qg + row * DK + 4 * cg) : make_uint4(0, 0, 0, 0);
+                in.raw[kSR + r] = *reinterpret_cast<const u32x4 *>(pk);
+                in.raw[2 * kSR + r] = *reinterpret_cast<const u32x4 *>(pq);
             }
         }
-    } else if (tid < R::NG + R::NV) {
-        const int u = tid - R::NG;
-        const int jg = u % (DV / 8), sg = u / (DV / 8);
-        const T *vg = static_cast<const T *>(a.v);
-        constexpr int VW = 8 * int(sizeof(T)) / 16;  // uint4 per 8 values
+    }
+}
+
+__device__ __forceinline__ void zero_unless(u32x4 &x, bool ok) {
+    const unsigned m = ok ? ~0u : 0u;
+    x &= m;
+}
+
+// Marks every prefetched input register as redefined at this point, then
+// zeroes the rows past the chunk end (g = 0 keeps the cumulative decay flat
+// there; k = q = v = beta = 0 removes them from every product).
+template <class T, int DK, int DV, int C>
+__device__ __forceinline__ void intra_fence(IntraIn<T, DK, DV, C> &in, int tid) {
+    using R = IntraRoles<T, DK, DV, C>;
 #pragma unroll
-        for (int r = 0; r < kSR; ++r) {
-            const int t = kSR * sg + r;
-            const bool ok = t < loc.len;
-            const size_t row = size_t(loc.tok0 + t) * H + h;
+    for (int i = 0; i < R::RAW; ++i) asm volatile("" : "+v"(in.raw[i]));
 #pragma unroll
-            for (int w = 0; w < VW; ++w)
-                in.raw[r * VW + w] =
-                    ok ? *reinterpret_cast<const uint4 *>(vg + row * DV + 8 * jg + w * (16 / sizeof(T)))
-                       : make_uint4(0, 0, 0, 0);
-            in.b[r] = ok ? a.beta[row] : 0.f;
-        }
+    for (int r = 0; r < kSR; ++r) {
+        float b = in.b[r];
+        asm volatile("" : "+v"(b));
+        in.b[r] = b;
+    }
+    bool is_g;
+    int cgrp, sg;
+    owner_coords<T, DK, DV, C>(tid, is_g, cgrp, sg);
+#pragma unroll
+    for (int r = 0; r < kSR; ++r) {
+        const bool ok = kSR * sg + r < in.len;
+        zero_unless(in.raw[r], ok);
+        zero_unless(in.raw[kSR + r], ok);
+        if constexpr (sizeof(T) == 4) zero_unless(in.raw[2 * kSR + r], ok);
+        in.b[r] = ok ? in.b[r] : 0.f;
     }
 }
 
@@ -276,7 +352,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     float *sL = reinterpret_cast<float *>(smem + Ly::oL);
     T *sP = reinterpret_cast<T *>(smem + Ly::oP);
     float *sY = reinterpret_cast<float *>(smem + Ly::oY);
-    float *sTot = reinterpret_cast<float *>(smem + Ly::oTot);  // per-segment decay totals [NSEG][DK]
+    float *sTot = reinterpret_cast<float *>(smem + Ly::oTot);  // segment decay totals, then their
+                                                               // exclusive prefix     [NSEG + 1][DK]
     float *sF = reinterpret_cast<float *>(smem + Ly::oF);      // e^{r_I - r_J}, J < I    [NOFF][DK]
     float *sR = reinterpret_cast<float *>(smem + Ly::oR);      // e^{r_I}                 [NT][DK]
     float *sB = reinterpret_cast<float *>(smem + Ly::oB);
@@ -296,59 +373,102 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         // thread coordinates pass through an opaque copy each iteration, so
         // that the many per-stage LDS addresses are recomputed here instead
         // of being hoisted out of the loop and held in registers throughout
-        const int tid = opaque(int(threadIdx.x)), lane = tid & 63, wid = tid >> 6;
+        const int tid = opaque(int(threadIdx.x)), lane = tid & 63;
+        const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile math stays scalar
         const int grp = lane >> 4, l16 = lane & 15;
         const int gc = item / H, h = item % H;
         const size_t slot = size_t(gc) * H + h;
+        // The prefetched registers are consumed from here on, and only from
+        // here: without this fence the compiler moves unpacking work up to
+        // the loads at the end of the previous item, which then must wait
+        // for them there and the prefetch hides no latency.
+        intra_fence(in, tid);
 
         // ---- cumulative log-decay: per-thread partial sums over kSR tokens ----
-        float G[kSR][4];
-        if (tid < R::NG) {
+        const int rt = role_tid<T, DK, DV, C>(tid);
+        if (rt < R::NG) {
             const int cg = tid % (DK / 4), sg = tid / (DK / 4);
             float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < kSR; ++r) {
-                const float4 g4 = *reinterpret_cast<const float4 *>(&in.raw[r]);
-                run[0] += g4.x; run[1] += g4.y; run[2] += g4.z; run[3] += g4.w;
+            for (int r = 0; r < kSR; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) G[r][c] = run[c];
-            }
+                for (int c = 0; c < 4; ++c) run[c] += __uint_as_float(in.raw[r][c]);
             *reinterpret_cast<float4 *>(sTot + sg * DK + 4 * cg) = make_float4(run[0], run[1], run[2], run[3]);
         }
         __syncthreads();
 
-        // ---- decay-factored operands, transposes and K~^T, from registers ----
-        if (tid < R::NG) {
-            const int cg = tid % (DK / 4), sg = tid / (DK / 4), c0 = 4 * cg;
-            const int I = sg / (kTile / kSR);  // 16-token tile of this segment
-            float off[4] = {0.f, 0.f, 0.f, 0.f}, rI[4] = {0.f, 0.f, 0.f, 0.f}, gl[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-            for (int s2 = 0; s2 < NSEG; ++s2) {
-                const float4 x = *reinterpret_cast<const float4 *>(sTot + s2 * DK + c0);
-                const float xv[4] = {x.x, x.y, x.z, x.w};
+        // ---- exclusive prefix of the segment totals (one thread per
+        //      channel), and the per-channel decay factors derived from it;
+        //      meanwhile role V stages (beta v)^T ----
+        if (rt >= R::NG + R::NV) {
+            const int c = tid - R::NG - R::NV;
+            if (c < DK) {
+                float x[NSEG];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (s2 < sg) off[c] += xv[c];
-                    if (s2 < (kTile / kSR) * I) rI[c] += xv[c];
-                    gl[c] += xv[c];
+                for (int s2 = 0; s2 < NSEG; ++s2) x[s2] = sTot[s2 * DK + c];
+                float run = 0.f, rr[NT];
+#pragma unroll
+                for (int s2 = 0; s2 < NSEG; ++s2) {
+                    if (s2 % (kTile / kSR) == 0) rr[s2 / (kTile / kSR)] = run;
+                    sTot[s2 * DK + c] = run;
+                    run += x[s2];
+                }
+                sTot[NSEG * DK + c] = run;
+                a.D[slot * DK + c] = exp_e(run);
+#pragma unroll
+                for (int I2 = 0; I2 < NT; ++I2) {
+                    sR[I2 * DK + c] = exp_e(rr[I2]);
+#pragma unroll
+                    for (int J2 = 0; J2 < I2; ++J2) sF[(I2 * (I2 - 1) / 2 + J2) * DK + c] = exp_e(rr[I2] - rr[J2]);
                 }
             }
-            // rows: K+, K-, Q+ (row-major, four channels per store)
+        } else if (rt >= R::NG) {
+            const int u = tid - R::NG;
+            const int jg = u % (DV / 8), sg = u / (DV / 8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, in.b[0] * v_get(in, 0, j), in.b[1] * v_get(in, 1, j),
+                       in.b[2] * v_get(in, 2, j), in.b[3] * v_get(in, 3, j));
+        }
+        __syncthreads();
+
+        // ---- decay-factored operands, transposes and K~^T, from registers:
+        //      with x = Gam - r_I (<= 0 within tile I),
+        //        K+ = k e^x, Q+ = q e^x, K- = k e^-x (<= e^80, the decay bound),
+        //        beta k e^Gam = beta K+ e^{r_I}   (when e^{r_I} underflows, so does e^Gam),
+        //        K~ = k e^{Gam_last - Gam}, its own exponential: e^-x e^{Gam_last - r_I}
+        //        would lose it when the second factor underflows and the first is large ----
+        if (rt < R::NG) {
+            const int cg = tid % (DK / 4), sg = tid / (DK / 4), c0 = 4 * cg;
+            const int I = sg / (kTile / kSR);  // 16-token tile of this segment
+            const float4 off4 = *reinterpret_cast<const float4 *>(sTot + sg * DK + c0);
+            const float4 rI4 = *reinterpret_cast<const float4 *>(sTot + (kTile / kSR) * I * DK + c0);
+            const float4 er4 = *reinterpret_cast<const float4 *>(sR + I * DK + c0);
+            const float4 gl4 = *reinterpret_cast<const float4 *>(sTot + NSEG * DK + c0);
+            const float base[4] = {off4.x - rI4.x, off4.y - rI4.y, off4.z - rI4.z, off4.w - rI4.w};
+            const float glr[4] = {gl4.x - rI4.x, gl4.y - rI4.y, gl4.z - rI4.z, gl4.w - rI4.w};
+            const float er[4] = {er4.x, er4.y, er4.z, er4.w};
+            // per channel: four tokens' beta k e^Gam and K~, for the column stores
+            Col4<T> bke[4], ktv[4];
+            float run[4] = {base[0], base[1], base[2], base[3]};  // Gam - r_I, token by token
 #pragma unroll
             for (int r = 0; r < kSR; ++r) {
                 const int t = kSR * sg + r;
                 float kp[4], km[4], qp[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const float gam = G[r][c] + off[c];
+                    run[c] += __uint_as_float(in.raw[r][c]);
+                    const float x = run[c];
                     const float kv = raw_get<T>(in.raw + kSR, (sizeof(T) == 2 ? 8 * r : 4 * r) + c);
                     const float qv = sizeof(T) == 2 ? raw_get<T>(in.raw + kSR, 8 * r + 4 + c)
                                                     : raw_get<T>(in.raw + 2 * kSR, 4 * r + c);
-                    const float e = exp_e(gam - rI[c]);   // <= 1
-                    const float ei = exp_e(rI[c] - gam);  // <= e^80 (the decay bound)
+                    const float e = exp_e(x);    // <= 1
+                    const float ei = exp_e(-x);  // <= e^80
                     kp[c] = kv * e;
                     qp[c] = qv * e;
                     km[c] = kv * ei;
+                    bke[c].set(r, in.b[r] * er[c] * kp[c]);
+                    ktv[c].set(r, kv * exp_e(glr[c] - x));  // <= 1
                 }
                 store4(sKp + t * K_LD + c0, kp[0], kp[1], kp[2], kp[3]);
                 store4(sKm + t * K_LD + c0, km[0], km[1], km[2], km[3]);
@@ -360,64 +480,22 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             static_assert(kSR == 4, "column stores are four tokens wide");
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                float bke[4], ktv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float gam = G[r][c] + off[c];
-                    const float kv = raw_get<T>(in.raw + kSR, (sizeof(T) == 2 ? 8 * r : 4 * r) + c);
-                    bke[r] = in.b[r] * kv * exp_e(gam);
-                    ktv[r] = kv * exp_e(gl[c] - gam);
+                bke[c].store(sKT + (c0 + c) * KT_LD + kSR * sg);
+                if constexpr (Mma<T>::KPL >= 4) {
+                    ktv[c].store(KtT + frag_off<T, C>(c0 + c, kSR * sg));
+                } else {
+                    store_frag4<T, C>(KtT, c0 + c, kSR * sg, ktv[c].v[0], ktv[c].v[1], ktv[c].v[2], ktv[c].v[3]);
                 }
-                store4(sKT + (c0 + c) * KT_LD + kSR * sg, bke[0], bke[1], bke[2], bke[3]);
-                store_frag4<T, C>(KtT, c0 + c, kSR * sg, ktv[0], ktv[1], ktv[2], ktv[3]);
-            }
-        } else if (tid < R::NG + R::NV) {
-            const int u = tid - R::NG;
-            const int jg = u % (DV / 8), sg = u / (DV / 8);
-            constexpr int VW = 8 * int(sizeof(T)) / 16;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, in.b[0] * raw_get<T>(in.raw, j),
-                       in.b[1] * raw_get<T>(in.raw + VW, j), in.b[2] * raw_get<T>(in.raw + 2 * VW, j),
-                       in.b[3] * raw_get<T>(in.raw + 3 * VW, j));
-        } else if (tid < R::NG + R::NV + DK / 4) {
-            // e^{Gam_last}, e^{r_I} and the tile-pair factors e^{r_I - r_J}
-            const int c0 = 4 * (tid - R::NG - R::NV);
-            float rr[NT][4];  // r_I: decay accumulated before tile I
-            float gl[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int I2 = 0; I2 < NT; ++I2)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) rr[I2][c] = 0.f;
-#pragma unroll 1
-            for (int s2 = 0; s2 < NSEG; ++s2) {
-                const float4 x = *reinterpret_cast<const float4 *>(sTot + s2 * DK + c0);
-                const float xv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-                for (int I2 = 1; I2 < NT; ++I2)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        if (s2 < (kTile / kSR) * I2) rr[I2][c] += xv[c];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) gl[c] += xv[c];
-            }
-            *reinterpret_cast<float4 *>(a.D + slot * DK + c0) =
-                make_float4(exp_e(gl[0]), exp_e(gl[1]), exp_e(gl[2]), exp_e(gl[3]));
-#pragma unroll
-            for (int I2 = 0; I2 < NT; ++I2) {
-                *reinterpret_cast<float4 *>(sR + I2 * DK + c0) =
-                    make_float4(exp_e(rr[I2][0]), exp_e(rr[I2][1]), exp_e(rr[I2][2]), exp_e(rr[I2][3]));
-#pragma unroll
-                for (int J2 = 0; J2 < I2; ++J2)
-                    *reinterpret_cast<float4 *>(sF + (I2 * (I2 - 1) / 2 + J2) * DK + c0) =
-                        make_float4(exp_e(rr[I2][0] - rr[J2][0]), exp_e(rr[I2][1] - rr[J2][1]),
-                                    exp_e(rr[I2][2] - rr[J2][2]), exp_e(rr[I2][3] - rr[J2][3]));
             }
         }
-        // ---- the next item's inputs go in flight now ----
+        // ---- the next item's inputs go in flight now.  After the last item
+        //      the loads repeat this item's (and go unused): an unconditional
+        //      load keeps the registers free of merges that would wait here ----
+        const ChunkLoc cur = loc;
         int nxt = item + gridDim.x;
         while (nxt < nitems && !locate_chunk(a, nxt / H, C, loc)) nxt += gridDim.x;
-        if (nxt < nitems) intra_fetch(in, a, loc, nxt % H, tid);
+        if (nxt >= nitems) loc = cur;
+        intra_fetch(in, a, loc, (nxt < nitems ? nxt : item) % H, tid);
         __syncthreads();
 
         // ---- A (strictly lower, row-scaled by beta) and P (lower incl.) on

@@ -98,10 +98,11 @@ template <class T> __host__ __device__ constexpr int kpad(int K) {
 template <class T, int K>
 __device__ __forceinline__ size_t frag_off(int r, int k) {
     using M = Mma<T>;
-    constexpr int KP = kpad<T>(K);
-    const int blk = (r >> 4) * (KP / M::K) + k / M::K;
-    const int ln = (r & 15) + 16 * ((k % M::K) / M::KPL);
-    return size_t(blk) * (16 * M::K) + ln * M::KPL + (k % M::KPL);
+    constexpr unsigned KP = kpad<T>(K);
+    const unsigned ur = unsigned(r), uk = unsigned(k);  // non-negative: unsigned keeps / and % cheap
+    const unsigned blk = (ur >> 4) * (KP / M::K) + uk / M::K;
+    const unsigned ln = (ur & 15u) + 16u * ((uk % M::K) / M::KPL);
+    return size_t(blk) * (16 * M::K) + ln * M::KPL + (uk % M::KPL);
 }
 
 // four consecutive k of row r (k0 % 4 == 0) into operand order
@@ -119,7 +120,7 @@ __device__ __forceinline__ void store_frag4(T *base, int r, int k0, float a, flo
 
 template <int N>
 __device__ __forceinline__ size_t quad_off(int tile_r, int tile_n, int lane) {
-    return (size_t(tile_r) * (N / 16) + tile_n) * 256 + lane * 4;
+    return size_t(unsigned(tile_r) * (N / 16) + unsigned(tile_n)) * 256 + unsigned(lane) * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -532,11 +533,17 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             }
         }
         __syncthreads();  // K+ and K- are dead: their LDS becomes A and L
-        for (int i = tid; i < C * C; i += kIThreads) {  // tiles above the diagonal
-            const int t = i / C, s = i - t * C;
-            if ((s >> 4) > (t >> 4)) {
-                sL[t * A_LD + s] = 0.f;
-                sP[t * P_LD + s] = from_f32<T>(0.f);
+        static_assert(NT * NT <= kIWaves, "one tile of A/P or of the zero upper part per wave");
+        if (wid >= NPAIR && wid < NT * NT) {
+            // tile (row J, column I), J < I, is zero in L and P
+            int I = 1, rem = wid - NPAIR;
+            while (rem >= I) { rem -= I; ++I; }
+            const int J = rem, col = kTile * I + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = kTile * J + 4 * grp + r;
+                sL[t * A_LD + col] = 0.f;
+                sP[t * P_LD + col] = from_f32<T>(0.f);
             }
         }
         if (wid < NPAIR) {
@@ -609,37 +616,45 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
 
         // ---- W = L (beta k e^Gam) as W^T = (beta k e^Gam)^T L^T, so that a
         //      lane's output is four consecutive channels of one token;
-        //      Ut = L (beta v).  Items: W tiles (m over dk, token tile n),
-        //      then Ut tiles (token tile I, n over dv); with NT == 4, wave w
-        //      always has token tile w, so its L fragments repeat. ----
+        //      Ut = L (beta v).  Items: W tiles (channel tile m, token tile n),
+        //      then Ut tiles (token tile I, value tile n); item wi of wave w
+        //      is w + kIWaves * it, so every item of a wave has the same token
+        //      tile and the L fragments are read once.  Wave-uniform branches
+        //      pick the W or Ut form. ----
         constexpr int NCK = DK / kTile, NCV = DV / kTile;
         constexpr int NIW = NT * NCK, NITEM = NT * (NCK + NCV);
         constexpr int IPW = (NITEM + kIWaves - 1) / kIWaves;
         constexpr int KSTEPS = (C + M::K - 1) / M::K;
+        static_assert(kIWaves % NT == 0, "a wave keeps one token tile");
+        const int tt = wid % NT;
+        const int ks = min(KSTEPS, (kTile * (tt + 1) + M::K - 1) / M::K);  // L and P are lower triangular
+        // k-fragment kk of a row starting at p; zero past the chunk (when C < K)
+        auto frag_at = [&](const T *p, int kk) -> Frag {
+            const int kb = kk * M::K + grp * M::KPL;
+            return (C % M::K == 0 || kb < C) ? M::load(p + kb) : Frag{};
+        };
         floatx4 res[IPW];
+        {
+            Frag lf[KSTEPS];
 #pragma unroll
-        for (int it = 0; it < IPW; ++it) {
-            const int wi = wid + kIWaves * it;
-            res[it] = zero4();
-            if (wi < NITEM) {
-                const bool isW = wi < NIW;
-                const int e = isW ? wi : wi - NIW;
-                const int tt = e % NT, cc = e / NT;  // token tile, channel / value tile
-                const int ks = min(KSTEPS, (kTile * (tt + 1) + M::K - 1) / M::K);
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const int kb = kk * M::K + grp * M::KPL;
+                lf[kk] = (C % M::K == 0 || kb < C) ? M::load_f32(sL + (kTile * tt + l16) * A_LD + kb) : Frag{};
+            }
+#pragma unroll
+            for (int it = 0; it < IPW; ++it) {
+                const int wi = wid + kIWaves * it;
                 floatx4 acc = zero4();
-                for (int kk = 0; kk < ks; ++kk) {
-                    const int kb = kk * M::K + grp * M::KPL;
-                    Frag fa, fb;
-                    if (kb < C) {
-                        const Frag fl = M::load_f32(sL + (kTile * tt + l16) * A_LD + kb);
-                        const Frag fo = M::load((isW ? sKT : sVT) + (kTile * cc + l16) * KT_LD + kb);
-                        fa = isW ? fo : fl;
-                        fb = isW ? fl : fo;
-                    } else {
-                        fa = Frag{};
-                        fb = Frag{};
-                    }
-                    acc = M::mma(fa, fb, acc);
+                if (wi < NIW) {
+                    const T *ob = sKT + (kTile * (wi / NT) + l16) * KT_LD;
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS; ++kk)
+                        if (kk < ks) acc = M::mma(frag_at(ob, kk), lf[kk], acc);
+                } else if (wi < NITEM) {
+                    const T *ob = sVT + (kTile * ((wi - NIW) / NT) + l16) * KT_LD;
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS; ++kk)
+                        if (kk < ks) acc = M::mma(lf[kk], frag_at(ob, kk), acc);
                 }
                 res[it] = acc;
             }
@@ -651,23 +666,19 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
 #pragma unroll
             for (int it = 0; it < IPW; ++it) {
                 const int wi = wid + kIWaves * it;
-                if (wi < NITEM) {
-                    const floatx4 acc = res[it];
-                    if (wi < NIW) {
-                        // lane holds W[t][c0..c0+3]: t = 16n + l16, c0 = 16m + 4grp
-                        const int n = wi % NT, m = wi / NT;
-                        const int t = kTile * n + l16, c0 = kTile * m + 4 * grp;
-                        store_frag4<T, DK>(Wg, t, c0, acc[0], acc[1], acc[2], acc[3]);
+                const floatx4 acc = res[it];
+                if (wi < NIW) {
+                    // lane holds W[t][c0..c0+3]: t = 16 tt + l16, c0 = 16 m + 4 grp
+                    const int t = kTile * tt + l16, c0 = kTile * (wi / NT) + 4 * grp;
+                    store_frag4<T, DK>(Wg, t, c0, acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) sKT[(c0 + r) * KT_LD + t] = from_f32<T>(acc[r]);  // W^T
-                    } else {
-                        // lane holds Ut[t0..t0+3][j]: t0 = 16I + 4grp, j = 16n + l16
-                        const int e = wi - NIW;
-                        const int I = e % NT, n = e / NT;
-                        store4(Ug + quad_off<DV>(I, n, lane), acc[0], acc[1], acc[2], acc[3]);
-                        store4(sVT + (kTile * n + l16) * KT_LD + kTile * I + 4 * grp, acc[0], acc[1], acc[2],
-                               acc[3]);  // Ut^T
-                    }
+                    for (int r = 0; r < 4; ++r) sKT[(c0 + r) * KT_LD + t] = from_f32<T>(acc[r]);  // W^T
+                } else if (wi < NITEM) {
+                    // lane holds Ut[t0..t0+3][j]: t0 = 16 tt + 4 grp, j = 16 n + l16
+                    const int n = (wi - NIW) / NT;
+                    store4(Ug + quad_off<DV>(tt, n, lane), acc[0], acc[1], acc[2], acc[3]);
+                    store4(sVT + (kTile * n + l16) * KT_LD + kTile * tt + 4 * grp, acc[0], acc[1], acc[2],
+                           acc[3]);  // Ut^T
                 }
             }
         }
@@ -678,39 +689,32 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         {
             T *Qg = static_cast<T *>(a.Qp) + slot * C * DK;
             T *Og = static_cast<T *>(a.Oi) + slot * C * DV;
+            Frag pf[KSTEPS];
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) pf[kk] = frag_at(sP + (kTile * tt + l16) * P_LD, kk);
 #pragma unroll
             for (int it = 0; it < IPW; ++it) {
                 const int wi = wid + kIWaves * it;
-                if (wi < NITEM) {
-                    const bool isW = wi < NIW;
-                    const int e = isW ? wi : wi - NIW;
-                    const int tt = e % NT, cc = e / NT;
-                    const int ks = min(KSTEPS, (kTile * (tt + 1) + M::K - 1) / M::K);
-                    floatx4 acc = zero4();
-                    for (int kk = 0; kk < ks; ++kk) {
-                        const int kb = kk * M::K + grp * M::KPL;
-                        Frag fa, fb;
-                        if (kb < C) {
-                            const Frag fp = M::load(sP + (kTile * tt + l16) * P_LD + kb);
-                            const Frag fo = M::load((isW ? sKT : sVT) + (kTile * cc + l16) * KT_LD + kb);
-                            fa = isW ? fo : fp;
-                            fb = isW ? fp : fo;
-                        } else {
-                            fa = Frag{};
-                            fb = Frag{};
-                        }
-                        acc = M::mma(fa, fb, acc);
-                    }
-                    if (isW) {
-                        // q e^Gam = Q+ e^{r_I} (token tile tt)
-                        const int t = kTile * tt + l16, c0 = kTile * cc + 4 * grp;
-                        const T *qp = sQp + t * K_LD + c0;
-                        const float4 er = *reinterpret_cast<const float4 *>(sR + tt * DK + c0);
-                        store_frag4<T, DK>(Qg, t, c0, to_f32(qp[0]) * er.x - acc[0], to_f32(qp[1]) * er.y - acc[1],
-                                           to_f32(qp[2]) * er.z - acc[2], to_f32(qp[3]) * er.w - acc[3]);
-                    } else {
-                        store4(Og + quad_off<DV>(tt, cc, lane), acc[0], acc[1], acc[2], acc[3]);
-                    }
+                floatx4 acc = zero4();
+                if (wi < NIW) {
+                    const int cc = wi / NT;
+                    const T *ob = sKT + (kTile * cc + l16) * KT_LD;
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS; ++kk)
+                        if (kk < ks) acc = M::mma(frag_at(ob, kk), pf[kk], acc);
+                    // q e^Gam = Q+ e^{r_I} (token tile tt)
+                    const int t = kTile * tt + l16, c0 = kTile * cc + 4 * grp;
+                    const T *qp = sQp + t * K_LD + c0;
+                    const float4 er = *reinterpret_cast<const float4 *>(sR + tt * DK + c0);
+                    store_frag4<T, DK>(Qg, t, c0, to_f32(qp[0]) * er.x - acc[0], to_f32(qp[1]) * er.y - acc[1],
+                                       to_f32(qp[2]) * er.z - acc[2], to_f32(qp[3]) * er.w - acc[3]);
+                } else if (wi < NITEM) {
+                    const int n = (wi - NIW) / NT;
+                    const T *ob = sVT + (kTile * n + l16) * KT_LD;
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS; ++kk)
+                        if (kk < ks) acc = M::mma(pf[kk], frag_at(ob, kk), acc);
+                    store4(Og + quad_off<DV>(tt, n, lane), acc[0], acc[1], acc[2], acc[3]);
                 }
             }
         }

@@ -61,6 +61,9 @@ _lib.kda_chunk_prefill_workspace_size.restype = _i
 _lib.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _u,
                                    _vp, _vp, _vp, _sz, _vp]
 _lib.kda_chunk_prefill.restype = _i
+_lib.kda_chunk_prefill_checkpointed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                                _i, _u, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
+_lib.kda_chunk_prefill_checkpointed.restype = _i
 _lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _u, _vp]
 _lib.kda_decode_step.restype = _i
 _lib.kda_status_string.argtypes = [_i]
@@ -97,6 +100,17 @@ def kda_chunk_prefill(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seq
     return _lib.kda_chunk_prefill(q or None, k or None, v or None, g or None, beta or None, h0 or None,
                                   cu_seqlens or None, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags,
                                   o or None, ht or None, workspace or None, workspace_bytes, stream or None)
+
+
+def kda_chunk_prefill_checkpointed(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size,
+                                   dtype, flags, o, ht, ckpt, ckpt_stride, num_ckpt, workspace, workspace_bytes,
+                                   stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_chunk_prefill_checkpointed(q or None, k or None, v or None, g or None, beta or None,
+                                               h0 or None, cu_seqlens or None, B, T, H, dk, dv, num_seqs,
+                                               chunk_size, dtype, flags, o or None, ht or None, ckpt or None,
+                                               ckpt_stride, num_ckpt, workspace or None, workspace_bytes,
+                                               stream or None)
 
 
 def kda_decode_step(q, k, v, g, beta, state, o, N, H, dk, dv, dtype, flags, stream) -> int:
@@ -159,13 +173,24 @@ def workspace_bytes(B, T, H, dk, dv, num_seqs, chunk_size, dtype) -> int:
     return kda_chunk_prefill_workspace_size(B, T, H, dk, dv, num_seqs, chunk_size, dtype)
 
 
+def checkpoint_count(T, ckpt_stride, B=1, seqlens=None) -> int:
+    """Checkpoint slots a checkpointed prefill writes: sum of len // stride
+    over the sequences (B of length T, or the given lengths)."""
+    if seqlens is not None:
+        return int(sum(int(n) // ckpt_stride for n in seqlens))
+    return int(B) * (int(T) // ckpt_stride)
+
+
 def chunk_prefill(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk_size=64, o=None, ht=None,
-                  output_final_state=True, workspace=None, flags=0, stream=None):
+                  output_final_state=True, workspace=None, flags=0, stream=None, ckpt_stride=None, ckpt=None):
     """Chunked KDA prefill on device tensors.
 
     q, k [B, T, H, dk]; v [B, T, H, dv] (bf16 or fp32, same dtype);
     g [B, T, H, dk] fp32; beta [B, T, H] fp32; h0 [N, H, dk, dv] fp32 or None;
-    cu_seqlens int32 [N+1] (packed, B = 1) or None.  Returns (o, ht)."""
+    cu_seqlens int32 [N+1] (packed, B = 1) or None.  Returns (o, ht).
+    With ckpt_stride (a multiple of chunk_size) the call also writes strided
+    state checkpoints and returns (o, ht, ckpt), ckpt [num_ckpt, H, dk, dv]
+    fp32 (allocated from the sequence lengths when not given)."""
     torch = _torch()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -178,6 +203,24 @@ def chunk_prefill(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk_size=64, 
     need = workspace_bytes(B, T, H, dk, dv, N, chunk_size, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if ckpt_stride is not None:
+        if ckpt is None:
+            lens = None
+            if cu_seqlens is not None:
+                cu = cu_seqlens.cpu().tolist()
+                lens = [cu[i + 1] - cu[i] for i in range(N)]
+            ckpt = torch.empty((checkpoint_count(T, ckpt_stride, B, lens), H, dk, dv), dtype=torch.float32,
+                               device=q.device)
+        st = kda_chunk_prefill_checkpointed(
+            _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"), _ptr(g, torch.float32, "g"),
+            _ptr(beta, torch.float32, "beta"), _ptr(h0, torch.float32, "h0"),
+            _ptr(cu_seqlens, torch.int32, "cu_seqlens"), B, T, H, dk, dv, N, chunk_size, dt, flags,
+            _ptr(o, q.dtype, "o"), _ptr(ht, torch.float32, "ht"), _ptr(ckpt, torch.float32, "ckpt"),
+            int(ckpt_stride), ckpt.shape[0], _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _stream(stream))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_prefill_checkpointed")
+        return o, ht, ckpt
     st = kda_chunk_prefill(_ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
                            _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
                            _ptr(h0, torch.float32, "h0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),

@@ -23,6 +23,8 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
     size_t off = 0;
     L.coff = off;
     off = align_up(off + sizeof(int32_t) * size_t(N + 1), 256);
+    L.ckoff = off;
+    off = align_up(off + sizeof(int32_t) * size_t(N + 1), 256);
     L.W = off;
     off = align_up(off + slots * C * dk * elem_bytes, 256);
     L.Qp = off;
@@ -163,10 +165,18 @@ int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int nu
     return KDA_OK;
 }
 
-int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                      const float *h0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
-                      int num_seqs, int chunk_size, kda_dtype dtype, unsigned flags, void *o, float *ht,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Optional strided checkpoints of a prefill call (ckpt null: none).
+struct CkptReq {
+    float *ckpt;
+    int stride, num_ckpt;
+};
+
+int prefill_impl(const void *q, const void *k, const void *v, const float *g, const float *beta, const float *h0,
+                 const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                 kda_dtype dtype, unsigned flags, void *o, float *ht, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream, const CkptReq &ck) {
     const bool packed = cu_seqlens != nullptr;
     int nc_max = 0, N = 0;
     int st = prefill_shape(B, T, H, dk, dv, num_seqs, chunk_size, dtype, packed, &nc_max, &N);
@@ -183,17 +193,19 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
     if (N > 0 && workspace_bytes < need) return KDA_ERR_WORKSPACE;
 
     for (const void *p : {q, k, v, (const void *)g, (const void *)beta, (const void *)h0, (const void *)o,
-                          (const void *)ht, (const void *)cu_seqlens})
+                          (const void *)ht, (const void *)cu_seqlens, (const void *)ck.ckpt})
         if (misaligned(p, 16)) return KDA_ERR_ALIGN;
     if (misaligned(workspace, 256)) return KDA_ERR_ALIGN;
 
     const size_t nq = rows * H * dk * eb, nv = rows * H * dv * eb, ng = rows * H * dk * 4, nb = rows * H * 4;
     const size_t ns = size_t(N) * H * dk * dv * 4;
     const size_t ncu = packed ? sizeof(int32_t) * size_t(N + 1) : 0;
+    const size_t nck = size_t(ck.num_ckpt) * H * dk * dv * 4;
     struct Buf { const void *p; size_t n; };
     const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {g, ng}, {beta, nb}, {h0, ns}, {cu_seqlens, ncu}};
-    const Buf outs[] = {{o, nv}, {ht, ns}, {workspace, need}};
-    for (int i = 0; i < 3; ++i) {
+    const Buf outs[] = {{o, nv}, {ht, ns}, {workspace, need}, {ck.ckpt, nck}};
+    constexpr int NOUT = 4;
+    for (int i = 0; i < NOUT; ++i) {
         for (const Buf &b : ins) {
             if (i == 1 && b.p == h0) {  // ht == h0 exactly is an in-place resume
                 if (ht && h0 && ht != h0 && overlap(ht, ns, h0, ns)) return KDA_ERR_ALIAS;
@@ -201,7 +213,7 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
             }
             if (overlap(outs[i].p, outs[i].n, b.p, b.n)) return KDA_ERR_ALIAS;
         }
-        for (int j = i + 1; j < 3; ++j)
+        for (int j = i + 1; j < NOUT; ++j)
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return KDA_ERR_ALIAS;
     }
 
@@ -228,10 +240,17 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
     a.W = ws + L.W; a.Qp = ws + L.Qp; a.KtT = ws + L.KtT; a.Ut = ws + L.Ut; a.Oi = ws + L.Oi;
     a.D = reinterpret_cast<float *>(ws + L.D);
     a.dummy = ws + L.dummy;
+    const bool want_ck = ck.ckpt && ck.num_ckpt > 0;
+    a.ckpt = want_ck ? ck.ckpt : nullptr;
+    a.ckoff = reinterpret_cast<int32_t *>(ws + L.ckoff);
+    a.ck_every = want_ck ? ck.stride / chunk_size : 1;
+    a.ck_per_seq = (want_ck && !packed) ? T / ck.stride : 0;
+    a.num_ckpt = want_ck ? ck.num_ckpt : 0;
 
     if (!any_tokens) a.nc_max = 0;  // only the state copy h0 -> ht remains
     if (packed && a.nc_max > 0) {
-        if (launch_chunk_offsets(cu_seqlens, N, T, chunk_size, nc_max, a.coff, stream) != hipSuccess)
+        if (launch_chunk_offsets(cu_seqlens, N, T, chunk_size, nc_max, a.coff, want_ck ? ck.stride : 0, a.ckoff,
+                                 stream) != hipSuccess)
             return KDA_ERR_LAUNCH;
     }
     if (packed && a.nc_max == 0) {
@@ -240,6 +259,8 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
         a.cu = nullptr;
         a.nc_seq = 0;
         a.T = 0;
+        a.ckpt = nullptr;
+        a.ck_per_seq = 0;
     }
     // value-column block: narrow blocks when few (sequence, head) chains
     // would leave compute units idle
@@ -247,6 +268,27 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *
     hipError_t e = (dtype == KDA_DTYPE_BF16) ? launch_prefill_bf16(a, dk, dv, chunk_size, bv, stream)
                                              : launch_prefill_f32(a, dk, dv, chunk_size, bv, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const float *h0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                      int num_seqs, int chunk_size, kda_dtype dtype, unsigned flags, void *o, float *ht,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return prefill_impl(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags, o,
+                        ht, workspace, workspace_bytes, stream, CkptReq{nullptr, 0, 0});
+}
+
+int kda_chunk_prefill_checkpointed(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *h0, const int32_t *cu_seqlens, int B, int T,
+                                   int H, int dk, int dv, int num_seqs, int chunk_size, kda_dtype dtype,
+                                   unsigned flags, void *o, float *ht, float *ckpt, int ckpt_stride,
+                                   int num_ckpt, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_ckpt < 0 || ckpt_stride <= 0 || chunk_size <= 0 || ckpt_stride % chunk_size != 0) return KDA_ERR_SHAPE;
+    if (num_ckpt > 0 && !ckpt) return KDA_ERR_NULL;
+    return prefill_impl(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags, o,
+                        ht, workspace, workspace_bytes, stream, CkptReq{ckpt, ckpt_stride, num_ckpt});
 }
 
 int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,

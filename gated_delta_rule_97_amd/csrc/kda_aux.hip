@@ -5,47 +5,63 @@
 namespace kda {
 
 // coff[n] = first chunk slot of sequence n = sum over m < n of
-// ceil(len_m / C), clamped to the workspace's nc_max slots.  Lengths come
-// from cu_seqlens clamped to [0, T], so malformed offsets can never produce
-// an out-of-range slot.  One workgroup; sequences in tiles of 1024.
+// ceil(len_m / C), clamped to the workspace's nc_max slots; with ck_tokens
+// > 0 also ckoff[n] = sum over m < n of floor(len_m / ck_tokens), the first
+// checkpoint of sequence n.  Lengths come from cu_seqlens clamped to
+// [0, T], so malformed offsets can never produce an out-of-range slot.  One
+// workgroup; sequences in tiles of 1024.
 __global__ __launch_bounds__(1024) void kda_chunk_offsets_kernel(const int32_t *__restrict__ cu, int N, int T,
-                                                                 int C, int nc_max, int32_t *__restrict__ coff) {
-    __shared__ int32_t scan[1024];
-    __shared__ int32_t carry;
+                                                                 int C, int nc_max, int32_t *__restrict__ coff,
+                                                                 int ck_tokens, int32_t *__restrict__ ckoff) {
+    __shared__ int32_t scan[2][1024];
+    __shared__ int32_t carry[2];
     const int tid = threadIdx.x;
+    const bool ck = ck_tokens > 0;
     if (tid == 0) {
-        carry = 0;
+        carry[0] = carry[1] = 0;
         coff[0] = 0;
+        if (ck) ckoff[0] = 0;
     }
     __syncthreads();
     for (int base = 0; base < N; base += 1024) {
         const int n = base + tid;
-        int cnt = 0;
+        int cnt = 0, nck = 0;
         if (n < N) {
             int s = cu[n], e = cu[n + 1];
             s = s < 0 ? 0 : (s > T ? T : s);
             e = e < s ? s : (e > T ? T : e);
             cnt = (e - s + C - 1) / C;
+            nck = ck ? (e - s) / ck_tokens : 0;
         }
-        scan[tid] = cnt;
+        scan[0][tid] = cnt;
+        scan[1][tid] = nck;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {
-            const int x = (tid >= off) ? scan[tid - off] : 0;
+            const int x0 = (tid >= off) ? scan[0][tid - off] : 0;
+            const int x1 = (tid >= off) ? scan[1][tid - off] : 0;
             __syncthreads();
-            scan[tid] += x;
+            scan[0][tid] += x0;
+            scan[1][tid] += x1;
             __syncthreads();
         }
-        if (n < N) coff[n + 1] = min(carry + scan[tid], nc_max);
+        if (n < N) {
+            coff[n + 1] = min(carry[0] + scan[0][tid], nc_max);
+            if (ck) ckoff[n + 1] = carry[1] + scan[1][tid];
+        }
         __syncthreads();
-        if (tid == 1023) carry = min(carry + scan[1023], nc_max);
+        if (tid == 1023) {
+            carry[0] = min(carry[0] + scan[0][1023], nc_max);
+            carry[1] = carry[1] + scan[1][1023];
+        }
         __syncthreads();
     }
 }
 
-hipError_t launch_chunk_offsets(const int32_t *cu, int N, int T, int C, int nc_max, int32_t *coff,
-                                hipStream_t s) {
+hipError_t launch_chunk_offsets(const int32_t *cu, int N, int T, int C, int nc_max, int32_t *coff, int ck_tokens,
+                                int32_t *ckoff, hipStream_t s) {
     prof_begin(s);
-    hipLaunchKernelGGL(kda_chunk_offsets_kernel, dim3(1), dim3(1024), 0, s, cu, N, T, C, nc_max, coff);
+    hipLaunchKernelGGL(kda_chunk_offsets_kernel, dim3(1), dim3(1024), 0, s, cu, N, T, C, nc_max, coff, ck_tokens,
+                       ckoff);
     prof_end(s, "kda_chunk_offsets");
     return hipGetLastError();
 }

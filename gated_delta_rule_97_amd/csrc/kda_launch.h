@@ -31,11 +31,18 @@ struct PrefillArgs {
     void *Oi;                  // [C][dv]  P (I+A)^-1 (beta v), quad order
     float *D;                  // [dk]     e^{Gam_last}
     void *dummy;               // 1 KiB sink for the o rows past a sequence's end
+    // strided state checkpoints (null ckpt: none): after every ck_every
+    // chunks of a sequence (a full chunk ending there), S goes to checkpoint
+    // ckoff[n] + j (packed) or n * ck_per_seq + j (fixed length) of
+    // ckpt [num_ckpt][H][dk][dv]; indices at or past num_ckpt are dropped
+    float *ckpt;
+    int32_t *ckoff;            // per-sequence first checkpoint [N+1] (packed only)
+    int ck_every, ck_per_seq, num_ckpt;
 };
 
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {
-    size_t coff, W, Qp, KtT, Ut, Oi, D, dummy, total;
+    size_t coff, ckoff, W, Qp, KtT, Ut, Oi, D, dummy, total;
 };
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
                              size_t elem_bytes);
@@ -51,8 +58,11 @@ void prof_end(hipStream_t s, const char *name);
 
 // Kernel launchers.  They return hipSuccess or the launch error.  Shapes have
 // been validated by the caller.
+// coff (chunk slots) and, when ck_tokens > 0, ckoff (checkpoints of
+// ck_tokens tokens each) per packed sequence
 hipError_t launch_chunk_offsets(const int32_t *cu, int N, int T, int C,
-                                int nc_max, int32_t *coff, hipStream_t s);
+                                int nc_max, int32_t *coff, int ck_tokens,
+                                int32_t *ckoff, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int dk, int dv, int C,
                                int bv, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int dk, int dv, int C,

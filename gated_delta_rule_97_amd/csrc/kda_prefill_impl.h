@@ -882,6 +882,29 @@ __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &
     }
 }
 
+// Strided checkpoint: after the lc-th chunk of sequence n (0-based), when
+// it is a full chunk and lc + 1 is a multiple of ck_every, the state goes to
+// the sequence's checkpoint (lc + 1) / ck_every - 1.  The tests are uniform
+// over the workgroup (scalar branches holding only stores).
+template <class T, int DK, int DV, int C, int BV>
+__device__ __forceinline__ void inter_ckpt(const PrefillArgs &a, const floatx4 (&S)[InterCfg<T, DK, DV, C, BV>::SPW],
+                                           int n, int h, int lc, bool full, int wid, int grp, int l16, int jb) {
+    using Cfg = InterCfg<T, DK, DV, C, BV>;
+    if (!a.ckpt || !full || (lc + 1) % a.ck_every != 0) return;
+    const int idx = (a.cu ? ld_const(a.ckoff, n) : n * a.ck_per_seq) + (lc + 1) / a.ck_every - 1;
+    if (idx >= a.num_ckpt) return;
+    float *dst = a.ckpt + (size_t(idx) * a.H + h) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < Cfg::SPW; ++i) {
+        const int item = wid + kWaves * i;
+        if (item < Cfg::NSI) {
+            const int m = item % Cfg::NRT, nn = item / Cfg::NRT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
+        }
+    }
+}
+
 template <class T, int DK, int DV, int C, int BV>
 __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     using Cfg = InterCfg<T, DK, DV, C, BV>;
@@ -959,6 +982,7 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
             const int tok0 = tok_start + (gc + s - c_begin) * C;
             inter_chunk<T, DK, DV, C, BV>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
                                           grp, l16, jb);
+            inter_ckpt<T, DK, DV, C, BV>(a, S, n, h, gc + s - c_begin, tok0 + C <= tok_end, wid, grp, l16, jb);
         }
     }
     // the last (c_end - gc) < NS chunks are already in st[0], st[1], ...
@@ -968,6 +992,7 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
             const int tok0 = tok_start + (gc + s - c_begin) * C;
             inter_chunk<T, DK, DV, C, BV>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
                                           grp, l16, jb);
+            inter_ckpt<T, DK, DV, C, BV>(a, S, n, h, gc + s - c_begin, tok0 + C <= tok_end, wid, grp, l16, jb);
         }
     }
 

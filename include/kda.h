@@ -110,6 +110,42 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_prefill that also writes strided state checkpoints, for a
+ * prefix cache that restores a sequence's recurrent state at a fixed token
+ * boundary (the serving-stack section of the blog post: cached states are
+ * kept at block boundaries, and resuming from one is kda_chunk_prefill with
+ * h0 = that checkpoint).
+ *
+ *   ckpt        [num_ckpt, H, dk, dv] float32, written: checkpoint j of a
+ *               sequence is its state after its first (j + 1) * ckpt_stride
+ *               tokens, for j = 0 .. len / ckpt_stride - 1 (integer
+ *               division; a length that is an exact multiple gives a last
+ *               checkpoint equal to ht).  Sequences are laid out one after
+ *               another: fixed-length batches (cu_seqlens NULL) give
+ *               sequence n slots n * (T / ckpt_stride) ..; packed batches
+ *               give sequence n the slots after those of sequences 0..n-1.
+ *               Checkpoints past num_ckpt are not written (size ckpt from
+ *               the lengths: sum over sequences of len / ckpt_stride).
+ *   ckpt_stride tokens between checkpoints, a positive multiple of
+ *               chunk_size (else KDA_ERR_SHAPE).
+ *   num_ckpt    slots in ckpt (>= 0); ckpt may be NULL only when it is 0.
+ * ckpt must be 16-byte aligned and must not overlap any other argument
+ * (KDA_ERR_ALIGN, KDA_ERR_ALIAS).  Every other argument, error and the
+ * results o and ht are exactly those of kda_chunk_prefill; the workspace
+ * size is the same.
+ */
+int kda_chunk_prefill_checkpointed(const void *q, const void *k,
+                                   const void *v, const float *g,
+                                   const float *beta, const float *h0,
+                                   const int32_t *cu_seqlens, int B, int T,
+                                   int H, int dk, int dv, int num_seqs,
+                                   int chunk_size, kda_dtype dtype,
+                                   unsigned flags, void *o, float *ht,
+                                   float *ckpt, int ckpt_stride, int num_ckpt,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
  * One decode step for N independent sequences, one token each, updating the
  * state in place (the serving-stack section: the recurrent state is updated
  * in place).  Per (n, h): S' = Diag(exp(g)) S; u = beta (v - S'^T k);

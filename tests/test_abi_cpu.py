@@ -125,3 +125,37 @@ def test_decode_validation(kw, status):
 
 def test_decode_empty_batch():
     assert _decode(N=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
+
+
+def _prefill_ck(**kw):
+    args = dict(q=A, k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24), h0=0,
+                cu_seqlens=0, B=1, T=64, H=2, dk=32, dv=32, num_seqs=1, chunk_size=16, dtype=F32,
+                flags=0, o=A + (5 << 24), ht=A + (6 << 24), ckpt=A + (10 << 24), ckpt_stride=32, num_ckpt=2,
+                workspace=A + (7 << 24), workspace_bytes=1 << 20, stream=0)
+    args.update(kw)
+    return kda.kda_chunk_prefill_checkpointed(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ckpt_stride=0), kda.KDA_ERR_SHAPE),
+    (dict(ckpt_stride=24), kda.KDA_ERR_SHAPE),                        # not a multiple of the chunk
+    (dict(num_ckpt=-1), kda.KDA_ERR_SHAPE),
+    (dict(ckpt=0), kda.KDA_ERR_NULL),
+    (dict(ckpt=A + (10 << 24) + 4), kda.KDA_ERR_ALIGN),
+    (dict(ckpt=A + (6 << 24) + 1024), kda.KDA_ERR_ALIAS),             # inside ht
+    (dict(ckpt=A + 128), kda.KDA_ERR_ALIAS),                          # overlaps q
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),                           # the prefill's own checks still apply
+    (dict(q=0), kda.KDA_ERR_NULL),
+])
+def test_prefill_checkpointed_validation(kw, status):
+    assert _prefill_ck(**kw) == status
+
+
+def test_prefill_checkpointed_no_slots_and_nothing_to_do():
+    assert _prefill_ck(B=0, num_seqs=0, T=0, q=0, k=0, v=0, g=0, beta=0, o=0, ht=0, workspace=0, ckpt=0,
+                       num_ckpt=0) == kda.KDA_OK
+
+
+def test_checkpoint_count():
+    assert kda.checkpoint_count(700, 128, B=2) == 10
+    assert kda.checkpoint_count(0, 128, seqlens=[37, 0, 512, 129, 300]) == 0 + 0 + 4 + 1 + 2

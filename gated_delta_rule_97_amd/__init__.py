@@ -66,6 +66,10 @@ _lib.kda_chunk_prefill_checkpointed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _v
 _lib.kda_chunk_prefill_checkpointed.restype = _i
 _lib.kda_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _u, _vp]
 _lib.kda_decode_step.restype = _i
+_lib.kda_decode_verify.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _u, _vp]
+_lib.kda_decode_verify.restype = _i
+_lib.kda_decode_commit.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _u, _vp]
+_lib.kda_decode_commit.restype = _i
 _lib.kda_status_string.argtypes = [_i]
 _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_profile_start.argtypes = [_i]
@@ -117,6 +121,18 @@ def kda_decode_step(q, k, v, g, beta, state, o, N, H, dk, dv, dtype, flags, stre
     """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
     return _lib.kda_decode_step(q or None, k or None, v or None, g or None, beta or None, state or None,
                                 o or None, N, H, dk, dv, dtype, flags, stream or None)
+
+
+def kda_decode_verify(q, k, v, g, beta, state, o, N, K, H, dk, dv, dtype, flags, stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_decode_verify(q or None, k or None, v or None, g or None, beta or None, state or None,
+                                  o or None, N, K, H, dk, dv, dtype, flags, stream or None)
+
+
+def kda_decode_commit(k, v, g, beta, n_accept, state, N, K, H, dk, dv, dtype, flags, stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_decode_commit(k or None, v or None, g or None, beta or None, n_accept or None,
+                                  state or None, N, K, H, dk, dv, dtype, flags, stream or None)
 
 
 def kda_profile_start(max_launches: int) -> None:
@@ -248,3 +264,37 @@ def decode_step(q, k, v, g, beta, state, o=None, *, flags=0, stream=None):
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")
     return o
+
+
+def decode_verify(q, k, v, g, beta, state, o=None, *, flags=0, stream=None):
+    """K draft tokens per sequence from the committed state (left unchanged):
+    q, k [N, K, H, dk]; v [N, K, H, dv]; g [N, K, H, dk] fp32; beta [N, K, H]
+    fp32; state [N, H, dk, dv] fp32.  Returns o [N, K, H, dv]."""
+    torch = _torch()
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
+    st = kda_decode_verify(_ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
+                           _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+                           _ptr(state, torch.float32, "state"), _ptr(o, q.dtype, "o"),
+                           N, K, H, dk, dv, dt, flags, _stream(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_verify")
+    return o
+
+
+def decode_commit(k, v, g, beta, n_accept, state, *, flags=0, stream=None):
+    """Folds the first n_accept[n] (int32 [N] on the device) of the K draft
+    tokens into each sequence's state, in place.  Returns state."""
+    torch = _torch()
+    N, K, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(k)
+    st = kda_decode_commit(_ptr(k, k.dtype, "k"), _ptr(v, k.dtype, "v"), _ptr(g, torch.float32, "g"),
+                           _ptr(beta, torch.float32, "beta"), _ptr(n_accept, torch.int32, "n_accept"),
+                           _ptr(state, torch.float32, "state"), N, K, H, dk, dv, dt, flags, _stream(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_commit")
+    return state

@@ -320,6 +320,73 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *g,
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+namespace {
+
+// Shared checks of the multi-token decode calls.
+int decode_multi_shape(int N, int K, int H, int dk, int dv, kda_dtype dtype) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || K < 0 || H <= 0) return KDA_ERR_SHAPE;
+    auto okd = [](int d) { return d == 32 || d == 64 || d == 128; };
+    if (!okd(dk) || !okd(dv)) return KDA_ERR_UNSUPPORTED;
+    if (int64_t(N) * H > INT32_MAX || int64_t(N) * K * H > INT32_MAX) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+}  // namespace
+
+int kda_decode_verify(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const float *state, void *o, int N, int K, int H, int dk, int dv, kda_dtype dtype,
+                      unsigned flags, hipStream_t stream) {
+    int st = decode_multi_shape(N, K, H, dk, dv, dtype);
+    if (st != KDA_OK) return st;
+    if (N == 0 || K == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    for (const void *p : {q, k, v, (const void *)g, (const void *)beta, (const void *)state, (const void *)o})
+        if (misaligned(p, 16)) return KDA_ERR_ALIGN;
+    const size_t rows = size_t(N) * K * H, eb = dtype_bytes(dtype);
+    const size_t nstate = size_t(N) * H * dk * dv * 4, no = rows * dv * eb;
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{q, rows * dk * eb}, {k, rows * dk * eb}, {v, rows * dv * eb}, {g, rows * dk * 4},
+                       {beta, rows * 4}, {state, nstate}};
+    for (const Buf &b : ins)
+        if (overlap(o, no, b.p, b.n)) return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        unsigned flag = 0;
+        if (run_checks(g, rows * dk, nullptr, 0, 0, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    hipError_t e = launch_decode_verify(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, N, K, H, dk,
+                                        dv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_decode_commit(const void *k, const void *v, const float *g, const float *beta, const int32_t *n_accept,
+                      float *state, int N, int K, int H, int dk, int dv, kda_dtype dtype, unsigned flags,
+                      hipStream_t stream) {
+    int st = decode_multi_shape(N, K, H, dk, dv, dtype);
+    if (st != KDA_OK) return st;
+    if (N == 0 || K == 0) return KDA_OK;
+    if (!k || !v || !g || !beta || !n_accept || !state) return KDA_ERR_NULL;
+    for (const void *p : {k, v, (const void *)g, (const void *)beta, (const void *)state})
+        if (misaligned(p, 16)) return KDA_ERR_ALIGN;
+    if (misaligned(n_accept, 4)) return KDA_ERR_ALIGN;
+    const size_t rows = size_t(N) * K * H, eb = dtype_bytes(dtype);
+    const size_t nstate = size_t(N) * H * dk * dv * 4;
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{k, rows * dk * eb}, {v, rows * dv * eb}, {g, rows * dk * 4}, {beta, rows * 4},
+                       {n_accept, size_t(N) * 4}};
+    for (const Buf &b : ins)
+        if (overlap(state, nstate, b.p, b.n)) return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        unsigned flag = 0;
+        if (run_checks(g, rows * dk, nullptr, 0, 0, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    hipError_t e = launch_decode_commit(dtype == KDA_DTYPE_BF16 ? 1 : 0, k, v, g, beta, n_accept, state, N, K, H,
+                                        dk, dv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 int kda_profile_start(int max_launches) {
     if (max_launches <= 0) return KDA_ERR_SHAPE;
     if (g_prof.active) return KDA_ERR_SHAPE;

@@ -88,6 +88,155 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const T *__restrict__ q
     }
 }
 
+// ---------------------------------------------------------------------------
+// Several decode tokens per sequence with the state held in registers
+// (speculative decoding, serving-stack section of the blog post: drafted
+// tokens are checked against the committed state, then the accepted ones
+// are committed).  Inputs are [N][K][H][d] (token t of sequence n at row
+// n * K + t).  VERIFY: all K tokens, o written per token, the state only
+// read.  COMMIT: the first n_accept[n] (clamped to [0, K]) tokens of
+// sequence n, no o, the state written back once (not at all when zero
+// tokens are accepted).  Same per-token arithmetic as kda_decode_kernel.
+// ---------------------------------------------------------------------------
+template <class T, int DK, int DV, bool VERIFY>
+__global__ __launch_bounds__(256) void kda_decode_multi_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                              const T *__restrict__ v, const float *__restrict__ g,
+                                                              const float *__restrict__ beta,
+                                                              const int32_t *__restrict__ n_accept,
+                                                              float *__restrict__ state, T *__restrict__ o, int K,
+                                                              int H) {
+    constexpr int CG = DV / 4;
+    constexpr int RG = 256 / CG;
+    constexpr int RPT = DK / RG;
+    static_assert(RG * CG == 256 && RPT * RG == DK, "decode thread split");
+    __shared__ float sk[DK], sq[DK], sd[DK];
+    __shared__ float4 sw[RG][CG], sy[RG][CG];
+    __shared__ float skq;
+
+    const int ch = blockIdx.x;  // sequence * H + head
+    const int n = ch / H, h = ch - n * H;
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    int ntok = K;
+    if (!VERIFY) {
+        const int na = n_accept[n];
+        ntok = na < 0 ? 0 : (na > K ? K : na);
+        if (ntok == 0) return;  // nothing accepted: the state stays as it is
+    }
+    float *S = state + size_t(ch) * DK * DV;
+
+    floatx4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
+
+    for (int t = 0; t < ntok; ++t) {
+        const size_t row = (size_t(n) * K + t) * H + h;  // token row of [N][K][H]
+        __syncthreads();  // the previous token's reads of sk/sq/sd/sw/sy are done
+        for (int c = tid; c < DK; c += 256) {
+            sk[c] = to_f32(k[row * DK + c]);
+            if (VERIFY) sq[c] = to_f32(q[row * DK + c]);
+            sd[c] = exp_e(g[row * DK + c]);
+        }
+        __syncthreads();
+        if (VERIFY && tid < 64) {
+            float p = 0.f;
+            for (int c = tid; c < DK; c += 64) p += sk[c] * sq[c];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+            if (tid == 0) skq = p;
+        }
+        float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int c = i * RG + rg;
+            const float f = sd[c], kc = sk[c];
+            s[i] *= f;
+            w.x += kc * s[i][0]; w.y += kc * s[i][1]; w.z += kc * s[i][2]; w.w += kc * s[i][3];
+            if (VERIFY) {
+                const float qc = sq[c];
+                y.x += qc * s[i][0]; y.y += qc * s[i][1]; y.z += qc * s[i][2]; y.w += qc * s[i][3];
+            }
+        }
+        sw[rg][cg] = w;
+        if (VERIFY) sy[rg][cg] = y;
+        __syncthreads();
+        float4 W = make_float4(0.f, 0.f, 0.f, 0.f), Y = W;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const float4 a = sw[r][cg];
+            W.x += a.x; W.y += a.y; W.z += a.z; W.w += a.w;
+            if (VERIFY) {
+                const float4 b = sy[r][cg];
+                Y.x += b.x; Y.y += b.y; Y.z += b.z; Y.w += b.w;
+            }
+        }
+        const float bt = beta[row];
+        const T *vp = v + row * DV + 4 * cg;
+        float4 u;
+        u.x = bt * (to_f32(vp[0]) - W.x);
+        u.y = bt * (to_f32(vp[1]) - W.y);
+        u.z = bt * (to_f32(vp[2]) - W.z);
+        u.w = bt * (to_f32(vp[3]) - W.w);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float kc = sk[i * RG + rg];
+            s[i][0] += kc * u.x; s[i][1] += kc * u.y; s[i][2] += kc * u.z; s[i][3] += kc * u.w;
+        }
+        if (VERIFY && rg == 0) {
+            const float kq = skq;
+            store4(o + row * DV + 4 * cg, Y.x + kq * u.x, Y.y + kq * u.y, Y.z + kq * u.z, Y.w + kq * u.w);
+        }
+    }
+    if (!VERIFY) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
+    }
+}
+
+template <class T, int DK, int DV, bool VERIFY>
+static hipError_t launch_multi_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                 const int32_t *n_accept, float *state, void *o, int N, int K, int H,
+                                 hipStream_t s) {
+    if (N == 0 || K == 0) return hipSuccess;
+    prof_begin(s);
+    hipLaunchKernelGGL((kda_decode_multi_kernel<T, DK, DV, VERIFY>), dim3(N * H), dim3(256), 0, s,
+                       static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
+                       n_accept, state, static_cast<T *>(o), K, H);
+    prof_end(s, VERIFY ? "kda_decode_verify" : "kda_decode_commit");
+    return hipGetLastError();
+}
+
+template <class T, bool VERIFY>
+static hipError_t multi_dispatch(int dk, int dv, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const int32_t *n_accept, float *state, void *o, int N, int K,
+                                 int H, hipStream_t s) {
+#define KDA_MUL(DK_, DV_) \
+    if (dk == DK_ && dv == DV_) \
+        return launch_multi_t<T, DK_, DV_, VERIFY>(q, k, v, g, beta, n_accept, state, o, N, K, H, s);
+    KDA_MUL(32, 32) KDA_MUL(32, 64) KDA_MUL(32, 128)
+    KDA_MUL(64, 32) KDA_MUL(64, 64) KDA_MUL(64, 128)
+    KDA_MUL(128, 32) KDA_MUL(128, 64) KDA_MUL(128, 128)
+#undef KDA_MUL
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_verify(int dtype, const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *state, void *o, int N, int K, int H, int dk,
+                                int dv, hipStream_t s) {
+    float *st = const_cast<float *>(state);  // read only in this mode
+    if (dtype == 1) return multi_dispatch<bf16, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, N, K, H, s);
+    return multi_dispatch<float, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, N, K, H, s);
+}
+
+hipError_t launch_decode_commit(int dtype, const void *k, const void *v, const float *g, const float *beta,
+                                const int32_t *n_accept, float *state, int N, int K, int H, int dk, int dv,
+                                hipStream_t s) {
+    if (dtype == 1) return multi_dispatch<bf16, false>(dk, dv, nullptr, k, v, g, beta, n_accept, state, nullptr, N,
+                                                       K, H, s);
+    return multi_dispatch<float, false>(dk, dv, nullptr, k, v, g, beta, n_accept, state, nullptr, N, K, H, s);
+}
+
 template <class T, int DK, int DV>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, float *state, void *o, int NH, hipStream_t s) {

@@ -71,6 +71,17 @@ hipError_t launch_decode(int dtype, const void *q, const void *k,
                          const void *v, const float *g, const float *beta,
                          float *state, void *o, int N, int H, int dk, int dv,
                          hipStream_t s);
+// K decode tokens per sequence from one state read: outputs only (verify),
+// or the first n_accept[n] tokens folded into the state (commit).
+hipError_t launch_decode_verify(int dtype, const void *q, const void *k,
+                                const void *v, const float *g,
+                                const float *beta, const float *state,
+                                void *o, int N, int K, int H, int dk, int dv,
+                                hipStream_t s);
+hipError_t launch_decode_commit(int dtype, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                const int32_t *n_accept, float *state, int N,
+                                int K, int H, int dk, int dv, hipStream_t s);
 // Debug checks: set a device flag when g leaves [-5, 0] (bit 0) or when
 // cu_seqlens is malformed (bit 1), then read it back synchronously.
 hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N,

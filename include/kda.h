@@ -161,6 +161,40 @@ int kda_decode_step(const void *q, const void *k, const void *v,
                     int N, int H, int dk, int dv, kda_dtype dtype,
                     unsigned flags, hipStream_t stream);
 
+/*
+ * Speculative decoding (the serving-stack section of the blog post: K
+ * drafted tokens are checked in one pass from the committed recurrent
+ * state, rebuilt on chip from the cached per-token inputs, then the
+ * accepted prefix is committed).  Both calls read each (sequence, head)
+ * state from HBM once and apply the decode step's arithmetic token by token
+ * with the state held on chip.  Token t of sequence n is row n * K + t of
+ * the [N, K, H, d] inputs.
+ *
+ * kda_decode_verify: outputs of all K tokens; the state is only read.
+ *   q, k  [N, K, H, dk] dtype   v [N, K, H, dv] dtype
+ *   g     [N, K, H, dk] float32 beta [N, K, H] float32
+ *   state [N, H, dk, dv] float32, read only (the committed state)
+ *   o     [N, K, H, dv] dtype, written; must not overlap any input
+ *         o[n, t] equals what t + 1 consecutive kda_decode_step calls on a
+ *         copy of the state would give for token t.
+ */
+int kda_decode_verify(const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, const float *state,
+                      void *o, int N, int K, int H, int dk, int dv,
+                      kda_dtype dtype, unsigned flags, hipStream_t stream);
+
+/*
+ * kda_decode_commit: folds the first n_accept[n] draft tokens of each
+ * sequence into its state, in place (values are clamped to [0, K]; 0
+ * leaves the state untouched).  k, v, g, beta as in kda_decode_verify (q is
+ * not needed); n_accept device int32 [N]; state [N, H, dk, dv] float32, read
+ * and written; it must not overlap any input.
+ */
+int kda_decode_commit(const void *k, const void *v, const float *g,
+                      const float *beta, const int32_t *n_accept,
+                      float *state, int N, int K, int H, int dk, int dv,
+                      kda_dtype dtype, unsigned flags, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(int status);
 

@@ -159,3 +159,51 @@ def test_prefill_checkpointed_no_slots_and_nothing_to_do():
 def test_checkpoint_count():
     assert kda.checkpoint_count(700, 128, B=2) == 10
     assert kda.checkpoint_count(0, 128, seqlens=[37, 0, 512, 129, 300]) == 0 + 0 + 4 + 1 + 2
+
+
+def _verify(**kw):
+    args = dict(q=A, k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24),
+                state=A + (5 << 24), o=A + (6 << 24), N=4, K=3, H=2, dk=128, dv=128, dtype=BF16, flags=0,
+                stream=0)
+    args.update(kw)
+    return kda.kda_decode_verify(**args)
+
+
+def _commit(**kw):
+    args = dict(k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24), n_accept=A + (7 << 24),
+                state=A + (5 << 24), N=4, K=3, H=2, dk=128, dv=128, dtype=BF16, flags=0, stream=0)
+    args.update(kw)
+    return kda.kda_decode_commit(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dtype=3), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=-1), kda.KDA_ERR_SHAPE),
+    (dict(H=0), kda.KDA_ERR_SHAPE),
+    (dict(o=0), kda.KDA_ERR_NULL),
+    (dict(state=0), kda.KDA_ERR_NULL),
+    (dict(o=A + (6 << 24) + 2), kda.KDA_ERR_ALIGN),
+    (dict(o=A + (5 << 24) + 4096), kda.KDA_ERR_ALIAS),                # o inside the state
+    (dict(o=A + 256), kda.KDA_ERR_ALIAS),                             # o overlaps q
+])
+def test_verify_validation(kw, status):
+    assert _verify(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dv=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(N=-1), kda.KDA_ERR_SHAPE),
+    (dict(n_accept=0), kda.KDA_ERR_NULL),
+    (dict(state=A + (5 << 24) + 8), kda.KDA_ERR_ALIGN),
+    (dict(n_accept=A + (7 << 24) + 2), kda.KDA_ERR_ALIGN),
+    (dict(state=A + (1 << 24) + 1024), kda.KDA_ERR_ALIAS),            # state overlaps k
+])
+def test_commit_validation(kw, status):
+    assert _commit(**kw) == status
+
+
+def test_verify_commit_empty():
+    assert _verify(N=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
+    assert _verify(K=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
+    assert _commit(N=0, k=0, v=0, g=0, beta=0, n_accept=0, state=0) == kda.KDA_OK

@@ -1,0 +1,137 @@
+"""Speculative-decode verify and commit (needs a GPU), against the fp64
+oracle's token loop: verify's output for draft token t equals t + 1
+consecutive decode steps from the committed state, which verify leaves
+untouched; commit of n accepted tokens leaves the state the oracle reaches
+after n steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import TOL_BF16, TOL_FP32, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return workloads.to_numpy_f32(t)
+
+
+def oracle_drafts(x, state0, n_steps=None):
+    """fp64 oracle over the K draft tokens: outputs [N, K, H, dv] and the
+    state after n_steps[n] tokens of each sequence (all K when None)."""
+    N, K = x["q"].shape[:2]
+    S = state0.numpy().astype(np.float64)
+    outs = []
+    states = np.empty_like(S)
+    for t in range(K):
+        if n_steps is not None:
+            for n in range(N):
+                if n_steps[n] == t:
+                    states[n] = S[n]
+        outs.append(oracle.decode_step(*(_np(x[key][:, t]) for key in ("q", "k", "v", "g", "beta")), S))
+    if n_steps is None:
+        states = S
+    else:
+        for n in range(N):
+            if n_steps[n] >= K:
+                states[n] = S[n]
+    return np.stack(outs, axis=1), states
+
+
+@pytest.mark.parametrize("dk,dv,dtype,K", [(128, 128, "bf16", 4), (64, 32, "bf16", 7), (32, 128, "fp32", 3),
+                                          (128, 64, "fp32", 1)])
+def test_verify_matches_oracle_and_keeps_state(dk, dv, dtype, K):
+    import gated_delta_rule_97_amd as kda
+    spec = workloads.DecodeSpec(N=6, H=3, dk=dk, dv=dv, steps=K, dtype=dtype, state_std=1.0, g_mode="slow",
+                                seed=61)
+    state0 = workloads.make_decode_state(spec)
+    x = workloads.make_decode_drafts(spec, K)
+    d = {key: val.cuda() for key, val in x.items()}
+    state = state0.cuda()
+    o = kda.decode_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    torch.cuda.synchronize()
+    assert torch.equal(state.cpu(), state0), "verify must not write the state"
+    o_ref, _ = oracle_drafts(x, state0)
+    tol = TOL_FP32 if dtype == "fp32" else TOL_BF16
+    e = rel_l2(o.double().cpu().numpy(), o_ref)
+    print(f"[verify] dk={dk} dv={dv} {dtype} K={K}: o {e:.2e}", flush=True)
+    assert e <= tol
+    for t in range(K):  # every draft position, not only the norm over all
+        assert rel_l2(o[:, t].double().cpu().numpy(), o_ref[:, t]) <= tol
+
+
+def test_verify_one_token_is_a_decode_step():
+    import gated_delta_rule_97_amd as kda
+    spec = workloads.DecodeSpec(N=4, H=2, dk=128, dv=128, steps=1, dtype="bf16", state_std=1.0, seed=62)
+    state0 = workloads.make_decode_state(spec).cuda()
+    x = {key: val.cuda() for key, val in workloads.make_decode_drafts(spec, 1).items()}
+    o1 = kda.decode_verify(x["q"], x["k"], x["v"], x["g"], x["beta"], state0)
+    st = state0.clone()
+    o2 = kda.decode_step(*(x[key][:, 0].contiguous() for key in ("q", "k", "v", "g", "beta")), st)
+    torch.cuda.synchronize()
+    assert rel_l2(o1[:, 0].double().cpu().numpy(), o2.double().cpu().numpy()) <= 1e-6
+
+
+def test_commit_accepted_prefixes():
+    """Per-sequence accepted counts, including 0, K and out-of-range values
+    (clamped); sequences with nothing accepted keep their exact state."""
+    import gated_delta_rule_97_amd as kda
+    K = 5
+    spec = workloads.DecodeSpec(N=8, H=4, dk=128, dv=64, steps=K, dtype="bf16", state_std=1.0, g_mode="slow",
+                                seed=63)
+    state0 = workloads.make_decode_state(spec)
+    x = workloads.make_decode_drafts(spec, K)
+    n_acc = [0, 1, 2, 5, 3, -2, 9, 4]
+    clamped = [min(max(a, 0), K) for a in n_acc]
+    d = {key: val.cuda() for key, val in x.items()}
+    state = state0.cuda()
+    kda.decode_commit(d["k"], d["v"], d["g"], d["beta"], torch.tensor(n_acc, dtype=torch.int32).cuda(), state)
+    torch.cuda.synchronize()
+    _, s_ref = oracle_drafts(x, state0, clamped)
+    got = state.double().cpu().numpy()
+    for n, a in enumerate(clamped):
+        if a == 0:
+            assert torch.equal(state[n].cpu(), state0[n]), f"sequence {n} accepted nothing"
+        else:
+            e = rel_l2(got[n], s_ref[n])
+            assert e <= TOL_BF16, f"sequence {n} ({a} accepted): {e:.2e}"
+
+
+def test_verify_then_commit_all_equals_decode_steps():
+    import gated_delta_rule_97_amd as kda
+    K = 4
+    spec = workloads.DecodeSpec(N=3, H=2, dk=64, dv=64, steps=K, dtype="fp32", state_std=1.0, g_mode="slow",
+                                seed=64)
+    state0 = workloads.make_decode_state(spec).cuda()
+    x = {key: val.cuda() for key, val in workloads.make_decode_drafts(spec, K).items()}
+    o = kda.decode_verify(x["q"], x["k"], x["v"], x["g"], x["beta"], state0)
+    committed = state0.clone()
+    kda.decode_commit(x["k"], x["v"], x["g"], x["beta"], torch.full((3,), K, dtype=torch.int32).cuda(), committed)
+    stepped = state0.clone()
+    outs = [kda.decode_step(*(x[key][:, t].contiguous() for key in ("q", "k", "v", "g", "beta")), stepped)
+            for t in range(K)]
+    torch.cuda.synchronize()
+    assert rel_l2(committed.double().cpu().numpy(), stepped.double().cpu().numpy()) <= 1e-6
+    assert rel_l2(o.double().cpu().numpy(), torch.stack(outs, 1).double().cpu().numpy()) <= 1e-6
+
+
+def test_verify_headline_batch_sampled():
+    """The 256-sequence x 32-head decode batch with 4 draft tokens; the
+    oracle checks 16 sequences (all heads, all drafts)."""
+    import gated_delta_rule_97_amd as kda
+    K = 4
+    spec = workloads.DECODE
+    state0 = workloads.make_decode_state(spec)
+    x = workloads.make_decode_drafts(spec, K)
+    d = {key: val.cuda() for key, val in x.items()}
+    state = state0.cuda()
+    o = kda.decode_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    torch.cuda.synchronize()
+    seqs = list(range(0, 256, 16))
+    xs = {key: val[seqs] for key, val in x.items()}
+    o_ref, _ = oracle_drafts(xs, state0[seqs])
+    e = rel_l2(o[seqs].double().cpu().numpy(), o_ref)
+    print(f"[verify] headline batch K={K}: o {e:.2e}", flush=True)
+    assert e <= TOL_BF16

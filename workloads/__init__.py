@@ -176,6 +176,14 @@ def make_decode_state(spec: DecodeSpec, device="cpu") -> torch.Tensor:
                                         dtype=torch.float32)
 
 
+def make_decode_drafts(spec: DecodeSpec, K: int, first_step: int = 0, device="cpu") -> dict:
+    """K consecutive decode steps stacked as draft tokens: q, k [N, K, H, dk];
+    v [N, K, H, dv]; g [N, K, H, dk]; beta [N, K, H] (token t is step
+    first_step + t of ``make_decode_step``)."""
+    steps = [make_decode_step(spec, first_step + t, device) for t in range(K)]
+    return {key: torch.stack([st[key] for st in steps], dim=1).contiguous() for key in steps[0]}
+
+
 def make_decode_step(spec: DecodeSpec, step: int, device="cpu") -> dict:
     """Inputs of decode step ``step``: q, k [N, H, dk]; v [N, H, dv] (compute
     dtype); g [N, H, dk], beta [N, H] (float32)."""

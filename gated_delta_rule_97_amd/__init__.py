@@ -46,6 +46,7 @@ KDA_ERR_ALIAS = -6
 KDA_ERR_LAUNCH = -7
 KDA_ERR_DECAY_BOUND = -8
 KDA_FLAG_CHECK_DECAY = 1
+KDA_FLAG_NO_SEGMENTS = 2
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 

@@ -17,7 +17,20 @@ namespace kda {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, size_t elem_bytes) {
+SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq) {
+    // worth it when the chains (32-column blocks) number under half a device
+    // of compute units and the sequences are long; each segment keeps at
+    // least 8 chunks, and the segments aim at ~1024 chains in all
+    const int64_t chains = int64_t(N) * H * (dv >= 32 ? dv / 32 : 1);
+    if (packed || chains <= 0 || chains >= 128 || nc_seq < 64) return SegPlan{1, 0};
+    int64_t nseg = (1024 + chains - 1) / chains;
+    if (nseg > nc_seq / 8) nseg = nc_seq / 8;
+    if (nseg < 2) return SegPlan{1, 0};
+    const int seg_len = int((nc_seq + nseg - 1) / nseg);
+    return SegPlan{(nc_seq + seg_len - 1) / seg_len, seg_len};
+}
+
+PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, size_t elem_bytes, int nseg) {
     PrefillLayout L;
     const size_t slots = size_t(nc_max) * size_t(H);
     size_t off = 0;
@@ -37,6 +50,13 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
     off = align_up(off + slots * C * dv * elem_bytes, 256);
     L.D = off;
     off = align_up(off + slots * dk * sizeof(float), 256);
+    const size_t sch = nseg > 1 ? size_t(N) * nseg * H : 0;  // segment chains
+    L.Mseg = off;
+    off = align_up(off + sch * dk * dk * sizeof(float), 256);
+    L.Bseg = off;
+    off = align_up(off + sch * dk * dv * sizeof(float), 256);
+    L.Sin = off;
+    off = align_up(off + sch * dk * dv * sizeof(float), 256);
     L.dummy = off;
     off += 1024;
     L.total = off;
@@ -161,7 +181,9 @@ int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int nu
         return KDA_ERR_SHAPE;
     }
     const int nc = std::max(nc_a, nc_b);
-    *bytes = prefill_layout(nc, H, num_seqs, dk, dv, chunk_size, dtype_bytes(dtype)).total;
+    // segment buffers when the fixed-length reading of these sizes segments
+    const int nseg = (num_seqs == B) ? seg_plan(false, B, H, dv, (T + chunk_size - 1) / chunk_size).nseg : 1;
+    *bytes = prefill_layout(nc, H, num_seqs, dk, dv, chunk_size, dtype_bytes(dtype), nseg).total;
     return KDA_OK;
 }
 
@@ -225,7 +247,12 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     }
     if (N == 0) return KDA_OK;
 
-    const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb);
+    const SegPlan sp = (flags & KDA_FLAG_NO_SEGMENTS) ? SegPlan{1, 0}
+                                                     : seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
+    // the layout is the one the size query computed (segment buffers present
+    // whenever the sizes call for them, also when a flag turns them off)
+    const SegPlan sp_ws = seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
+    const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb, sp_ws.nseg);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0;
@@ -246,6 +273,11 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     a.ck_every = want_ck ? ck.stride / chunk_size : 1;
     a.ck_per_seq = (want_ck && !packed) ? T / ck.stride : 0;
     a.num_ckpt = want_ck ? ck.num_ckpt : 0;
+    a.seg_len = sp.seg_len;
+    a.nseg = sp.nseg;
+    a.Mseg = reinterpret_cast<float *>(ws + L.Mseg);
+    a.Bseg = reinterpret_cast<float *>(ws + L.Bseg);
+    a.Sin = reinterpret_cast<float *>(ws + L.Sin);
 
     if (!any_tokens) a.nc_max = 0;  // only the state copy h0 -> ht remains
     if (packed && a.nc_max > 0) {
@@ -261,6 +293,12 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
         a.T = 0;
         a.ckpt = nullptr;
         a.ck_per_seq = 0;
+        a.seg_len = 0;
+        a.nseg = 1;
+    }
+    if (!any_tokens) {
+        a.seg_len = 0;
+        a.nseg = 1;
     }
     // value-column block: narrow blocks when few (sequence, head) chains
     // would leave compute units idle

@@ -38,14 +38,29 @@ struct PrefillArgs {
     float *ckpt;
     int32_t *ckoff;            // per-sequence first checkpoint [N+1] (packed only)
     int ck_every, ck_per_seq, num_ckpt;
+    // segment-parallel state chain (fixed-length batches only; seg_len 0:
+    // off).  Sequence n's chunks split into nseg segments of seg_len chunks;
+    // segment chain (n * nseg + j) * H + h.  Mseg [chains][dk][dk] and Bseg
+    // [chains][dk][dv]: the segment's transition and zero-start end state;
+    // Sin [chains][dk][dv]: the true state entering each segment.
+    int seg_len, nseg;
+    float *Mseg, *Bseg, *Sin;
 };
+
+// Segment plan of a prefill: segments when long fixed-length sequences have
+// too few (sequence, head) chains to occupy the device.  A pure function of
+// the sizes, so the workspace size query and the call agree.
+struct SegPlan {
+    int nseg, seg_len;  // nseg 1, seg_len 0: no segmentation
+};
+SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq);
 
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {
-    size_t coff, ckoff, W, Qp, KtT, Ut, Oi, D, dummy, total;
+    size_t coff, ckoff, W, Qp, KtT, Ut, Oi, D, Mseg, Bseg, Sin, dummy, total;
 };
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
-                             size_t elem_bytes);
+                             size_t elem_bytes, int nseg);
 // chunk length rounded up to the MFMA contraction of the dtype (K~^T pad)
 inline int chunk_pad(int C, size_t elem_bytes) {
     const int k = elem_bytes == 2 ? 32 : 4;

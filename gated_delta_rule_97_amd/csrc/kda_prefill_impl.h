@@ -742,6 +742,12 @@ template <> struct Quad<float> {
     __device__ __forceinline__ float operator[](int i) const { return v[i]; }
 };
 
+// What one state-chain launch computes.  FULL: outputs o and the state
+// (ht or a checkpoint).  SUM_B: a segment's end state from a zero start, no
+// outputs.  SUM_M: a segment's transition, the chain applied to an identity
+// block with no value input (U = -W S), no outputs; instanced with DV = DK.
+enum InterMode { kFull = 0, kSumB = 1, kSumM = 2 };
+
 template <class T, int DK, int DV, int C, int BV>
 struct InterCfg {
     typedef typename Mma<T>::Frag Frag;
@@ -765,7 +771,7 @@ struct InterStage {
     Quad<T> ut[Cfg::XPW], oi[Cfg::XPW];            // Ut, Oi at this lane's output positions
 };
 
-template <class T, int DK, int DV, int C, int BV>
+template <class T, int DK, int DV, int C, int BV, int MODE>
 __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, const PrefillArgs &a, int gc,
                                            int h, int wid, int grp, int l16, int jb) {
     using Cfg = InterCfg<T, DK, DV, C, BV>;
@@ -783,7 +789,7 @@ __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, con
     for (int kk = 0; kk < Cfg::KSD; ++kk) {
         const size_t off = size_t(I * Cfg::KSD + kk) * (16 * M::K) + lane * M::KPL;
         st.w[kk] = M::load(W + off);
-        st.q[kk] = M::load(Qp + off);
+        if (MODE == kFull) st.q[kk] = M::load(Qp + off);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::SPW; ++i) {
@@ -804,8 +810,8 @@ __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, con
         const int item = wid + kWaves * i;
         if (item < Cfg::NXI) {
             const int nn = item / Cfg::NT;
-            st.ut[i].load(UtT + quad_off<DV>(I, jb / kTile + nn, lane));
-            st.oi[i].load(OiT + quad_off<DV>(I, jb / kTile + nn, lane));
+            if (MODE != kSumM) st.ut[i].load(UtT + quad_off<DV>(I, jb / kTile + nn, lane));
+            if (MODE == kFull) st.oi[i].load(OiT + quad_off<DV>(I, jb / kTile + nn, lane));
         }
     }
 }
@@ -814,7 +820,7 @@ __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, con
 // of this chunk and the next state.  ``len`` < C only on a sequence's last
 // chunk; rows past it are written to a dummy area instead of o (a select,
 // not a branch, so that no prefetched operand gets sunk into a branch).
-template <class T, int DK, int DV, int C, int BV>
+template <class T, int DK, int DV, int C, int BV, int MODE>
 __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &cur, floatx4 (&S)[InterCfg<T, DK, DV, C, BV>::SPW],
                                             T *sST, T *sUT, T *og, T *dummy, int tok0, int len, int H, int h,
                                             int wid, int grp, int l16, int jb) {
@@ -849,16 +855,22 @@ __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &
                 const int kb = kk * M::K + grp * M::KPL;
                 const Frag sf = M::load(sST + (kTile * nn + l16) * ST_LD + kb);
                 ax = M::mma(cur.w[kk], sf, ax);
-                ao = M::mma(cur.q[kk], sf, ao);
+                if (MODE == kFull) ao = M::mma(cur.q[kk], sf, ao);
             }
             const int j = jb + kTile * nn + l16;
             const int t0 = kTile * I + 4 * grp;
-            store4(sUT + (kTile * nn + l16) * UT_LD + t0, cur.ut[i][0] - ax[0], cur.ut[i][1] - ax[1],
-                   cur.ut[i][2] - ax[2], cur.ut[i][3] - ax[3]);
+            if (MODE == kSumM) {
+                store4(sUT + (kTile * nn + l16) * UT_LD + t0, -ax[0], -ax[1], -ax[2], -ax[3]);
+            } else {
+                store4(sUT + (kTile * nn + l16) * UT_LD + t0, cur.ut[i][0] - ax[0], cur.ut[i][1] - ax[1],
+                       cur.ut[i][2] - ax[2], cur.ut[i][3] - ax[3]);
+            }
+            if (MODE == kFull) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                T *dst = (t0 + r < len) ? og + (size_t(tok0 + t0 + r) * H + h) * DV + j : dummy;
-                *dst = from_f32<T>(cur.oi[i][r] + ao[r]);
+                for (int r = 0; r < 4; ++r) {
+                    T *dst = (t0 + r < len) ? og + (size_t(tok0 + t0 + r) * H + h) * DV + j : dummy;
+                    *dst = from_f32<T>(cur.oi[i][r] + ao[r]);
+                }
             }
         }
     }
@@ -905,22 +917,25 @@ __device__ __forceinline__ void inter_ckpt(const PrefillArgs &a, const floatx4 (
     }
 }
 
-template <class T, int DK, int DV, int C, int BV>
+template <class T, int DK, int DV, int C, int BV, int MODE>
 __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     using Cfg = InterCfg<T, DK, DV, C, BV>;
     constexpr int NB = Cfg::NB, NRT = Cfg::NRT;
     constexpr int NSI = Cfg::NSI, SPW = Cfg::SPW, NS = Cfg::NS;
     constexpr int PT = 16 / sizeof(T);
+    static_assert(MODE != kSumM || DV == DK, "a transition is dk x dk");
     __shared__ __align__(16) T sST[BV * (DK + PT)];
     __shared__ __align__(16) T sUT[BV * (C + PT)];
 
     const int H = a.H;
-    const int nchains = a.N * H;
+    const bool segmented = a.seg_len > 0;
+    const int nseg = segmented ? a.nseg : 1;
+    const int nchains = a.N * nseg * H;
     const int wg = blockIdx.x;
     int chain, blk;
     if ((nchains & 7) == 0) {
-        // the NB blocks of one (sequence, head) share an XCD (and its L2):
-        // workgroups are dealt round-robin to the 8 XCDs by linear id
+        // the NB blocks of one chain share an XCD (and its L2): workgroups
+        // are dealt round-robin to the 8 XCDs by linear id
         const int xcd = wg & 7, slot = wg >> 3;
         blk = slot % NB;
         chain = xcd + 8 * (slot / NB);
@@ -928,17 +943,26 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
         chain = wg / NB;
         blk = wg - chain * NB;
     }
-    const int n = chain / H, h = chain - n * H;
+    // chain = (n * nseg + segment) * H + h
+    const int h = chain % H, ns_idx = chain / H;
+    const int n = ns_idx / nseg, sgi = ns_idx - n * nseg;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int grp = lane >> 4, l16 = lane & 15;
     const int jb = blk * BV;
 
-    int c_begin, c_end, tok_start, tok_end;
+    int c_begin, c_end, tok_start, tok_end, lc0 = 0;
     if (!a.cu) {
         c_begin = n * a.nc_seq;
         c_end = c_begin + a.nc_seq;
         tok_start = n * a.T;
         tok_end = tok_start + a.T;
+        if (segmented) {
+            lc0 = sgi * a.seg_len;  // chunks of the sequence before this segment
+            c_begin += lc0;
+            c_end = min(c_end, c_begin + a.seg_len);
+            tok_start += lc0 * C;
+            tok_end = min(tok_end, tok_start + a.seg_len * C);
+        }
     } else {
         c_begin = min(a.coff[n], a.nc_max);
         c_end = min(max(a.coff[n + 1], c_begin), a.nc_max);
@@ -953,11 +977,16 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     for (int i = 0; i < SPW; ++i) {
         const int item = wid + kWaves * i;
         S[i] = zero4();
-        if (item < NSI && a.h0) {
+        if (item < NSI) {
             const int m = item % NRT, nn = item / NRT;
+            if (MODE == kSumM) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[i][r] = a.h0[sbase + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16];
+                for (int r = 0; r < 4; ++r) S[i][r] = (kTile * m + 4 * grp + r == jb + kTile * nn + l16) ? 1.f : 0.f;
+            } else if (MODE == kFull && a.h0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[i][r] = a.h0[sbase + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16];
+            }
         }
     }
     // the initial state must have arrived before the first prefetch is
@@ -970,7 +999,8 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     InterStage<T, DK, DV, C, BV> st[NS];
     if (c_begin < c_end) {
 #pragma unroll
-        for (int s = 0; s < NS - 1; ++s) inter_load(st[s], a, min(c_begin + s, c_end - 1), h, wid, grp, l16, jb);
+        for (int s = 0; s < NS - 1; ++s)
+            inter_load<T, DK, DV, C, BV, MODE>(st[s], a, min(c_begin + s, c_end - 1), h, wid, grp, l16, jb);
     }
     int gc = c_begin;
     // full groups of NS chunks, branch-free: the chunk loaded NS-1 steps
@@ -978,11 +1008,14 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     for (; gc + NS <= c_end; gc += NS) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            inter_load(st[(s + NS - 1) % NS], a, min(gc + s + NS - 1, c_end - 1), h, wid, grp, l16, jb);
+            inter_load<T, DK, DV, C, BV, MODE>(st[(s + NS - 1) % NS], a, min(gc + s + NS - 1, c_end - 1), h, wid,
+                                               grp, l16, jb);
             const int tok0 = tok_start + (gc + s - c_begin) * C;
-            inter_chunk<T, DK, DV, C, BV>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
-                                          grp, l16, jb);
-            inter_ckpt<T, DK, DV, C, BV>(a, S, n, h, gc + s - c_begin, tok0 + C <= tok_end, wid, grp, l16, jb);
+            inter_chunk<T, DK, DV, C, BV, MODE>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h,
+                                                wid, grp, l16, jb);
+            if (MODE == kFull)
+                inter_ckpt<T, DK, DV, C, BV>(a, S, n, h, lc0 + gc + s - c_begin, tok0 + C <= tok_end, wid, grp, l16,
+                                             jb);
         }
     }
     // the last (c_end - gc) < NS chunks are already in st[0], st[1], ...
@@ -990,23 +1023,101 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     for (int s = 0; s < NS - 1; ++s) {
         if (gc + s < c_end) {
             const int tok0 = tok_start + (gc + s - c_begin) * C;
-            inter_chunk<T, DK, DV, C, BV>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
-                                          grp, l16, jb);
-            inter_ckpt<T, DK, DV, C, BV>(a, S, n, h, gc + s - c_begin, tok0 + C <= tok_end, wid, grp, l16, jb);
+            inter_chunk<T, DK, DV, C, BV, MODE>(st[s], S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h,
+                                                wid, grp, l16, jb);
+            if (MODE == kFull)
+                inter_ckpt<T, DK, DV, C, BV>(a, S, n, h, lc0 + gc + s - c_begin, tok0 + C <= tok_end, wid, grp, l16,
+                                             jb);
         }
     }
 
-    if (a.ht) {
+    // the end state: a segment summary (its own slot), or ht from the last
+    // segment of the sequence (slot n * H + h)
+    float *dst = nullptr;
+    if (MODE != kFull) dst = a.ht + sbase;
+    else if (a.ht && sgi == nseg - 1) dst = a.ht + size_t(n * H + h) * DK * DV;
+    if (dst) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int item = wid + kWaves * i;
             if (item < NSI) {
                 const int m = item % NRT, nn = item / NRT;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    a.ht[sbase + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
+                for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
             }
         }
+    }
+}
+
+// Segment scan: the state entering segment j + 1 of (sequence n, head h) is
+// Sin_{j+1} = M_j Sin_j + B_j, Sin_0 = h0 (or zero), in fp32, serially over
+// the segments.  One workgroup per (n, h, 32 value columns); 256 threads,
+// each owning a 4 x 4 block of the 128 x 32 tile, Sin_j staged in LDS.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void kda_seg_scan_kernel(PrefillArgs a) {
+    constexpr int CB = DV < 32 ? DV : 32;       // columns per workgroup
+    constexpr int NCB = DV / CB;
+    constexpr int CQ = CB / 4;                  // 4-column groups
+    constexpr int RQ = DK / 4;                  // 4-row groups
+    static_assert(RQ * CQ <= 256, "scan tile");
+    __shared__ __align__(16) float sS[DK][CB];
+    const int H = a.H, nseg = a.nseg;
+    const int wg = blockIdx.x, cb = wg % NCB, nh = wg / NCB;
+    const int n = nh / H, h = nh - n * H;
+    const int tid = threadIdx.x, cq = tid % CQ, rq = tid / CQ;
+    const bool active = rq < RQ;
+    const int c0 = cb * CB + 4 * cq;
+    auto slot = [&](int j) { return size_t((n * nseg + j) * H + h); };
+    // Sin_0
+    for (int i = tid; i < DK * CB; i += 256) {
+        const int r = i / CB, c = i - r * CB;
+        const float x = a.h0 ? a.h0[size_t(n * H + h) * DK * DV + size_t(r) * DV + cb * CB + c] : 0.f;
+        sS[r][c] = x;
+        a.Sin[slot(0) * DK * DV + size_t(r) * DV + cb * CB + c] = x;
+    }
+    __syncthreads();
+    for (int j = 0; j + 1 < nseg; ++j) {
+        float acc[4][4];
+        if (active) {
+            const float *Mj = a.Mseg + slot(j) * DK * DK + size_t(4 * rq) * DK;
+            const float *Bj = a.Bseg + slot(j) * DK * DV + size_t(4 * rq) * DV + c0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4 b = *reinterpret_cast<const float4 *>(Bj + size_t(r) * DV);
+                acc[r][0] = b.x; acc[r][1] = b.y; acc[r][2] = b.z; acc[r][3] = b.w;
+            }
+            for (int kk = 0; kk < DK; kk += 4) {
+                float mv[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float4 m4 = *reinterpret_cast<const float4 *>(Mj + size_t(r) * DK + kk);
+                    mv[r][0] = m4.x; mv[r][1] = m4.y; mv[r][2] = m4.z; mv[r][3] = m4.w;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 s4 = *reinterpret_cast<const float4 *>(&sS[kk + q][4 * cq]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[r][0] += mv[r][q] * s4.x;
+                        acc[r][1] += mv[r][q] * s4.y;
+                        acc[r][2] += mv[r][q] * s4.z;
+                        acc[r][3] += mv[r][q] * s4.w;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every read of Sin_j is done
+        if (active) {
+            float *dst = a.Sin + slot(j + 1) * DK * DV + size_t(4 * rq) * DV + c0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                *reinterpret_cast<float4 *>(&sS[4 * rq + r][4 * cq]) =
+                    make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+                *reinterpret_cast<float4 *>(dst + size_t(r) * DV) =
+                    make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -1035,10 +1146,40 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (a.seg_len > 0) {
+        // segment-parallel chain: summaries, scan, then the output chains
+        constexpr int SB = 32;  // value-column block of the segmented chains
+        static_assert(DV % SB == 0 && DK % SB == 0, "segment blocks");
+        const int nsc = a.N * a.nseg * a.H;
+        PrefillArgs b = a;
+        b.h0 = nullptr;
+        b.ht = a.Bseg;
+        b.ckpt = nullptr;
+        prof_begin(s);
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, DV, C, SB, kSumB>), dim3(nsc * (DV / SB)), dim3(kThreads), 0, s,
+                           b);
+        prof_end(s, "kda_seg_sum_b");
+        PrefillArgs m = b;
+        m.ht = a.Mseg;
+        prof_begin(s);
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, DK, C, SB, kSumM>), dim3(nsc * (DK / SB)), dim3(kThreads), 0, s,
+                           m);
+        prof_end(s, "kda_seg_sum_m");
+        prof_begin(s);
+        hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 32)), dim3(256), 0, s, a);
+        prof_end(s, "kda_seg_scan");
+        PrefillArgs f = a;
+        f.h0 = a.Sin;
+        prof_begin(s);
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, DV, C, SB, kFull>), dim3(nsc * (DV / SB)), dim3(kThreads), 0, s,
+                           f);
+        prof_end(s, "kda_inter");
+        return hipGetLastError();
+    }
     const int nwg = a.N * a.H * (DV / BV);
     if (nwg > 0) {
         prof_begin(s);
-        hipLaunchKernelGGL((kda_inter_kernel<T, DK, DV, C, BV>), dim3(nwg), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((kda_inter_kernel<T, DK, DV, C, BV, kFull>), dim3(nwg), dim3(kThreads), 0, s, a);
         prof_end(s, "kda_inter");
     }
     return hipGetLastError();

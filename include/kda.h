@@ -63,6 +63,12 @@ enum {
  * starts at 0, never decreases and ends at T (KDA_ERR_SHAPE otherwise).
  * This breaks the no-host-sync rule on purpose. */
 #define KDA_FLAG_CHECK_DECAY 1u
+/* Prefill: keep one state chain per (sequence, head) even when the sizes
+ * would split long sequences into segments computed in parallel (the
+ * blog post's serving-stack section: a sequence split across devices, each
+ * part summarised by its state transition; here across compute units).
+ * Results agree up to rounding either way; for comparisons and timing. */
+#define KDA_FLAG_NO_SEGMENTS 2u
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes
  * (written to *bytes).  Same arguments as kda_chunk_prefill.  The figure

@@ -1,0 +1,99 @@
+"""Segment-parallel prefill (needs a GPU).  Long fixed-length sequences with
+few (sequence, head) chains are split into segments: each segment's
+zero-start end state B and transition M are computed in parallel, a scan
+gives every segment its true incoming state, and the output chains then run
+in parallel.  Checked against the fp64 oracle on whole outputs, including a
+state-isolation case (v = 0: everything comes from h0 carried through every
+segment's transition), against the unsegmented path, and with checkpoints."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from helpers import TOL_BF16, TOL_FP32, rel_l2
+from kda_cases import oracle_prefill, to_np64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+Spec = workloads.PrefillSpec
+
+
+def run(x, chunk, flags=0, **kw):
+    import gated_delta_rule_97_amd as kda
+    d = {key: (val.cuda() if val is not None else None) for key, val in x.items()}
+    kda.kda_profile_start(64)
+    res = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=chunk, flags=flags,
+                            **kw)
+    kt = kda.kda_profile_stop()
+    torch.cuda.synchronize()
+    return res, kt
+
+
+CASES = [
+    ("bf16 d128 ragged", Spec(H=2, dk=128, dv=128, T=8192 + 37, B=1, dtype="bf16", chunk=64, h0_std=1.0,
+                              g_mode="slow", seed=71), 64),
+    ("bf16 two seqs d64/32", Spec(H=1, dk=64, dv=32, T=4096, B=2, dtype="bf16", chunk=64, h0_std=1.0,
+                                  g_mode="slow", seed=72), 64),
+    ("fp32 chunk16", Spec(H=2, dk=32, dv=32, T=2048, B=1, dtype="fp32", chunk=16, h0_std=1.0, g_mode="slow",
+                          seed=73), 16),
+    ("bf16 no decay", Spec(H=1, dk=128, dv=64, T=4096, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="zero",
+                           seed=74), 64),
+    ("bf16 decay floor", Spec(H=1, dk=128, dv=128, T=4096, B=1, dtype="bf16", chunk=64, h0_std=1.0,
+                              g_mode="floor", seed=75), 64),
+    # v = 0: o and ht come only from h0 through every segment's transition;
+    # 1024 tokens (8 segments of 128 at chunk 16) keep that state well above
+    # underflow (over 8192 tokens it decays to ~1e-30)
+    ("bf16 state isolation", Spec(H=2, dk=128, dv=128, T=1024, B=1, dtype="bf16", chunk=16, h0_std=1.0,
+                                  g_mode="slow", v_zero=True, seed=76), 16),
+]
+
+
+@pytest.mark.parametrize("label,spec,chunk", CASES, ids=[c[0] for c in CASES])
+def test_segmented_matches_oracle(label, spec, chunk):
+    x = workloads.make_prefill(spec)
+    print(f"[parity] segmented {label}", flush=True)
+    (o, ht), kt = run(x, chunk)
+    assert "kda_seg_scan" in kt, "the sizes should select the segmented chain"
+    o_ref, ht_ref = oracle_prefill(x)
+    eo = rel_l2(to_np64(o).reshape(o_ref.shape), o_ref)
+    eh = rel_l2(to_np64(ht), ht_ref)
+    print(f"[parity]   rel-L2 o={eo:.3e} ht={eh:.3e}", flush=True)
+    tol = tol_for(spec.dtype)
+    assert eo <= tol and eh <= tol
+
+
+def test_segmented_equals_single_chain():
+    import gated_delta_rule_97_amd as kda
+    spec = Spec(H=2, dk=128, dv=128, T=8192, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow", seed=77)
+    x = workloads.make_prefill(spec)
+    (o1, h1), kt1 = run(x, 64)
+    (o2, h2), kt2 = run(x, 64, flags=kda.KDA_FLAG_NO_SEGMENTS)
+    assert "kda_seg_scan" in kt1 and "kda_seg_scan" not in kt2
+    assert rel_l2(to_np64(o1), to_np64(o2)) <= TOL_BF16
+    assert rel_l2(to_np64(h1), to_np64(h2)) <= TOL_BF16
+
+
+def test_segmented_with_checkpoints():
+    from test_gpu_checkpoints import ref_checkpoints
+    spec = Spec(H=2, dk=128, dv=64, T=8192, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow", seed=78)
+    x = workloads.make_prefill(spec)
+    (o, ht, ck), kt = run(x, 64, ckpt_stride=1024)
+    assert "kda_seg_scan" in kt
+    ref = ref_checkpoints(x, 1024)
+    assert ck.shape[0] == 8
+    for i in range(8):
+        assert rel_l2(to_np64(ck[i]), ref[i]) <= TOL_BF16, f"checkpoint {i}"
+    assert torch.equal(ck[7], ht[0])
+
+
+def test_segmented_in_place_resume():
+    """ht may be h0 itself with the segmented chain too."""
+    import gated_delta_rule_97_amd as kda
+    spec = Spec(H=1, dk=128, dv=128, T=4096, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow", seed=79)
+    x = workloads.make_prefill(spec)
+    d = {key: (val.cuda() if val is not None else None) for key, val in x.items()}
+    h = d["h0"].clone()
+    kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], h, ht=h)
+    torch.cuda.synchronize()
+    _, ht_ref = oracle_prefill(x)
+    assert rel_l2(to_np64(h), ht_ref) <= TOL_BF16

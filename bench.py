@@ -8,7 +8,10 @@ call over the whole batch (all of its kernels), inputs resident in HBM.
 value = tokens/s = B*T / (time per call).
 
 Also measured and reported in the same JSON line: decode (256 sequences x 32
-heads, d = 128, 128 consecutive in-place steps), per-kernel durations from
+heads, d = 128, 128 consecutive in-place steps); under "next": speculative
+verify/commit of 4 draft tokens on that batch, the headline prefill with a
+state checkpoint every 512 tokens, and the 1M-token x 8-head prefill
+(segment-parallel chain, and the single chain for comparison); per-kernel durations from
 HIP events recorded around every launch on the launch stream, roofline
 fractions against MI355X peaks (HBM 8 TB/s; bf16 MFMA 2.5 PFLOP/s), and the
 fp64 oracle timed on the host cores on the same inputs (a reported baseline,
@@ -254,6 +257,92 @@ def main():
                            "avg_launch_us": round(dec_launch_us, 2),
                            "algorithmic_bytes_per_launch": dec_bytes}}
 
+    # ------------------------------------- next rows: verify, checkpoints,
+    # long context (each with its own algorithmic bytes and roofline)
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+    K = 4
+    drafts = workloads.make_decode_drafts(dspec, K, device=dev)
+    ov = torch.empty((dspec.N, K, dspec.H, dspec.dv), dtype=torch.bfloat16, device=dev)
+    nacc = torch.full((dspec.N,), K, dtype=torch.int32, device=dev)
+    st_v = state0.clone()
+    t_verify = timed(lambda: kda.decode_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"], drafts["beta"],
+                                               st_v, o=ov), 20)
+    st_c = state0.clone()
+    t_commit = timed(lambda: kda.decode_commit(drafts["k"], drafts["v"], drafts["g"], drafts["beta"], nacc, st_c),
+                     20)
+    nh = dspec.N * dspec.H
+    vbytes = nh * (dspec.dk * dspec.dv * 4 + K * 1540)            # state read once + K tokens' vectors
+    cbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * 1284)        # state read + written, no q or o
+    vgbs = vbytes / (t_verify * 1e-3) / 1e9
+    cgbs = cbytes / (t_commit * 1e-3) / 1e9
+    log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s)")
+    verify = {"workload": f"decode batch N={dspec.N} H={dspec.H} d=128 bf16, {K} draft tokens",
+              "verify_us": round(t_verify * 1e3, 2), "commit_us": round(t_commit * 1e3, 2),
+              "draft_tokens_per_s": round(dspec.N * K / (t_verify * 1e-3), 1),
+              "vs_k_decode_steps": round(K * dec_launch_us / (t_verify * 1e3 + t_commit * 1e3), 3),
+              "roofline": {"kernel": "kda_decode_verify", "bound": "hbm", "achieved": round(vgbs, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(vgbs / HBM_PEAK_GBS, 4),
+                           "traffic": None, "avg_launch_us": round(t_verify * 1e3, 2),
+                           "algorithmic_bytes_per_launch": vbytes},
+              "commit_roofline": {"kernel": "kda_decode_commit", "bound": "hbm", "achieved": round(cgbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cgbs / HBM_PEAK_GBS, 4),
+                                  "avg_launch_us": round(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes}}
+    del drafts, ov, st_v, st_c
+
+    stride = 512
+    nck = kda.checkpoint_count(T, stride, B)
+    ck = torch.empty((nck, H, dk, dv), dtype=torch.float32, device=dev)
+    t_plain = timed(step, 10)
+    t_ck = timed(lambda: kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=C, o=o,
+                                           ht=ht, workspace=ws, ckpt_stride=stride, ckpt=ck), 10)
+    ckpt = {"workload": f"{workload}, a state checkpoint every {stride} tokens ({nck} per head)",
+            "ms_per_call": round(t_ck, 4), "plain_ms_per_call": round(t_plain, 4),
+            "overhead_frac": round(t_ck / t_plain - 1.0, 4), "checkpoint_bytes": nck * H * dk * dv * 4}
+    log(f"checkpoints: {t_ck * 1e3:.1f} us/call vs {t_plain * 1e3:.1f} plain")
+    del ck
+
+    lspec = workloads.CONFIGS[3]
+    log(f"long context: {lspec.name}")
+    xl = workloads.make_prefill(lspec, device=dev)
+    wl = torch.empty(kda.workspace_bytes(lspec.B, lspec.T, lspec.H, lspec.dk, lspec.dv, lspec.B, lspec.chunk,
+                                         kda.KDA_DTYPE_BF16), dtype=torch.uint8, device=dev)
+    ol = torch.empty((lspec.B, lspec.T, lspec.H, lspec.dv), dtype=torch.bfloat16, device=dev)
+    hl = torch.empty((lspec.B, lspec.H, lspec.dk, lspec.dv), dtype=torch.float32, device=dev)
+
+    def long_step(flags=0):
+        kda.chunk_prefill(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"], None, chunk_size=lspec.chunk, o=ol, ht=hl,
+                          workspace=wl, flags=flags)
+
+    t_single = timed(lambda: long_step(kda.KDA_FLAG_NO_SEGMENTS), 2)
+    long_step()
+    torch.cuda.synchronize()
+    kda.kda_profile_start(64)
+    t_long = timed(long_step, 3)
+    lkt = kda.kda_profile_stop()
+    lth = lspec.B * lspec.T * lspec.H
+    lbytes = BYTES_PER_TOKEN_HEAD * lth + lspec.B * lspec.H * lspec.dk * lspec.dv * 4
+    lgbs = lbytes / (t_long * 1e-3) / 1e9
+    log(f"long context: {t_long:.2f} ms/call segmented, {t_single:.2f} ms single chain")
+    long_ctx = {"workload": lspec.name.replace("long-context prefill ", "prefill ") + " chunk=64",
+                "ms_per_call": round(t_long, 3), "tokens_per_s": round(lspec.B * lspec.T / (t_long * 1e-3), 1),
+                "single_chain_ms_per_call": round(t_single, 3),
+                "kernels_us": {k: round(1e3 * v[1] / v[0], 1) for k, v in lkt.items()},
+                "path_roofline": {"bound": "hbm", "algorithmic_bytes": lbytes, "achieved_GBps": round(lgbs, 1),
+                                  "hbm_frac": round(lgbs / HBM_PEAK_GBS, 4),
+                                  "hbm_floor_ms": round(lbytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}}
+    del xl, wl, ol, hl
+    torch.cuda.empty_cache()
+
     # -------------------------------------------- oracle on the host cores
     cpu = None
     parity = None
@@ -307,6 +396,7 @@ def main():
            "roofline": roofline, "path_roofline": path_roofline,
            "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
            "cpu_baseline": cpu, "parity": parity, "decode": decode,
+           "next": {"speculative_verify": verify, "checkpoints": ckpt, "long_context": long_ctx},
            "source_digest": source_digest()}
     print(json.dumps(out), flush=True)
 

@@ -1121,6 +1121,294 @@ __global__ __launch_bounds__(256) void kda_seg_scan_kernel(PrefillArgs a) {
     }
 }
 
+// Strided checkpoint from the accumulator-resident state (see inter_ckpt).
+template <int DK, int DV>
+__device__ __forceinline__ void chain_ckpt(const PrefillArgs &a, const floatx4 (&S)[DK / kTile], int n, int h, int lc,
+                                           bool full, int grp, int l16, int nb) {
+    if (!full || (lc + 1) % a.ck_every != 0) return;
+    const int idx = (a.cu ? ld_const(a.ckoff, n) : n * a.ck_per_seq) + (lc + 1) / a.ck_every - 1;
+    if (idx >= a.num_ckpt) return;
+    float *dst = a.ckpt + (size_t(idx) * a.H + h) * DK * DV;
+#pragma unroll
+    for (int m = 0; m < DK / kTile; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + nb + l16] = S[m][r];
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2b (bf16): the state chain with the state held in MFMA accumulators.
+// One workgroup per (chain, block of 16 * NWV value columns); wave w owns the
+// 16 columns jb + 16 w of S, all dk rows, as 16x16 accumulator tiles (a lane
+// holds rows 4 grp .. 4 grp + 3 of column l16 of each tile).  Products use
+// the 16x16x32 bf16 MFMA with a permuted contraction order: slot j < 4 of a
+// lane's 8 operand values is row 4 grp + j of tile 2p, slot j >= 4 row
+// 4 grp + j - 4 of tile 2p + 1.  With that order the B operand of X = W S and
+// O = Q' S is just the lane's own accumulators of tiles 2p, 2p + 1, and
+// U = Ut - X (token tiles 2q, 2q + 1) is the B operand of S += K~^T U: the
+// state and U never leave the wave.  The A operands every wave needs — W,
+// Q', K~^T — are staged per chunk in LDS in the same permuted order (one
+// 16-byte read per operand), with e^{Gam_last}, double-buffered, from a
+// ring of NS register stages loaded NS - 1 chunks ahead; one barrier per
+// chunk.  The loop runs whole NS-chunk groups; chunks past the chain's end
+// are inactive (state kept, nothing stored): branch-free, static ring indices.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int C, int NWV, int MODE>
+struct ChainCfg {
+    static constexpr int NTHR = kWave * NWV;
+    static constexpr int BW = kTile * NWV;                  // value columns per workgroup
+    static constexpr int NT = C / kTile, MT = DK / kTile;
+    static constexpr int NQ = (NT + 1) / 2, MP = MT / 2;    // 32-wide token / dk slices
+    static constexpr int CP = kpad<bf16>(C);                // K~^T row length (operand order)
+    static constexpr bool HAS_Q = MODE == kFull;
+    static constexpr int W_EL = C * DK, K_EL = DK * CP;     // bf16 elements per chunk
+    static constexpr int PW = W_EL * 2 / 16, PK = K_EL * 2 / 16, PD = DK * 4 / 16;  // 16-byte pieces
+    static constexpr int KB = PW * (HAS_Q ? 2 : 1);        // first K~^T piece
+    static constexpr int P = KB + PK + PD;
+    static constexpr int PPT = (P + NTHR - 1) / NTHR;       // pieces per thread
+    static constexpr int BUF = PPT * NTHR * 16;             // bytes per LDS buffer (padded)
+    static constexpr int NS = PPT > 16 ? 2 : 4;             // register stages (fewer when each holds more)
+    static_assert(NS % 2 == 0, "the LDS buffer of a chunk is its index mod 2");
+    static_assert(DK % 32 == 0 && NTHR % kWave == 0, "chain shapes");
+};
+
+template <int DK, int DV, int C, int NWV, int MODE>
+struct ChainStage {
+    using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
+    u32x4 stg[Cfg::PPT];                  // this thread's pieces of the staged operands
+    bf16x4 ut[Cfg::NT], oi[Cfg::NT];      // Ut, Oi at this lane's positions of its column block
+};
+
+// Loads one chunk's stage: 16-byte pieces p = tid + NTHR i of the operand-
+// order W, Q', K~^T and of e^{Gam_last}, laid end to end; Ut and Oi (quad
+// order) at this lane's positions.  Bases are uniform (scalar registers).
+template <int DK, int DV, int C, int NWV, int MODE>
+__device__ __forceinline__ void chain_load(ChainStage<DK, DV, C, NWV, MODE> &st, const PrefillArgs &a, int gc, int h,
+                                           int tid, int loff, int nblk) {
+    using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
+    const size_t slot = size_t(gc) * a.H + h;
+    const char *W = static_cast<const char *>(a.W) + slot * Cfg::W_EL * 2;
+    const char *Q = static_cast<const char *>(a.Qp) + slot * Cfg::W_EL * 2;
+    const char *K = static_cast<const char *>(a.KtT) + slot * Cfg::K_EL * 2;
+    const char *D = reinterpret_cast<const char *>(a.D + slot * DK);
+#pragma unroll
+    for (int i = 0; i < Cfg::PPT; ++i) {
+        const int p = min(tid + Cfg::NTHR * i, Cfg::P - 1);  // the padding re-reads the last piece
+        const char *src;
+        if (p < Cfg::PW) src = W + p * 16;
+        else if (Cfg::HAS_Q && p < Cfg::KB) src = Q + (p - Cfg::PW) * 16;
+        else if (p < Cfg::KB + Cfg::PK) src = K + (p - Cfg::KB) * 16;
+        else src = D + (p - Cfg::KB - Cfg::PK) * 16;
+        st.stg[i] = *reinterpret_cast<const u32x4 *>(src);
+    }
+    if (MODE != kSumM) {
+        // quad order: tile (I, nblk) is 256 values, lane l holds 4 of them
+        const char *U = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.Ut) + slot * C * DV + nblk * 256);
+        const char *O = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.Oi) + slot * C * DV + nblk * 256);
+#pragma unroll
+        for (int I = 0; I < Cfg::NT; ++I) {
+            st.ut[I] = *reinterpret_cast<const bf16x4 *>(U + I * (DV / kTile) * 512 + loff);
+            if (MODE == kFull) st.oi[I] = *reinterpret_cast<const bf16x4 *>(O + I * (DV / kTile) * 512 + loff);
+        }
+    }
+}
+
+// Writes the stage into one LDS buffer.  A 16-byte operand-order piece (lane
+// ln = l16 + 16 q of its block: 8 consecutive k from 8 q) goes, as two
+// 8-byte halves, to the permuted order: the half with k offset c = 8 q + 4 h
+// lands in lane l16 + 16 g of the same block, slot c / 16, with g = (c % 16)
+// / 4.  K~^T columns past the chunk (the pad of a 16-token chunk) become 0.
+template <int DK, int DV, int C, int NWV, int MODE>
+__device__ __forceinline__ void chain_stage_write(unsigned char *buf, const ChainStage<DK, DV, C, NWV, MODE> &st,
+                                                  int tid) {
+    using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
+#pragma unroll
+    for (int i = 0; i < Cfg::PPT; ++i) {
+        const int p = tid + Cfg::NTHR * i;
+        const u32x4 v = st.stg[i];
+        if (p >= Cfg::KB + Cfg::PK) {  // e^{Gam_last} and the padding: as is
+            *reinterpret_cast<u32x4 *>(buf + p * 16) = v;
+            continue;
+        }
+        const int blk = p >> 6, ln = p & 63, l16 = ln & 15, q = ln >> 4;
+        const int s0 = q >> 1;                                      // slot of both halves
+        const int g0 = 2 * (q & 1);                                 // lane group of half 0; half 1: g0 + 1
+        u32x2 lo{v[0], v[1]}, hi{v[2], v[3]};
+        if (C < 32 && p >= Cfg::KB && s0 == 1) lo = hi = u32x2{0u, 0u};  // K~^T pad columns
+        unsigned char *base = buf + blk * 1024 + l16 * 16 + 8 * s0;
+        *reinterpret_cast<u32x2 *>(base + (16 * g0) * 16) = lo;
+        *reinterpret_cast<u32x2 *>(base + (16 * (g0 + 1)) * 16) = hi;
+    }
+}
+
+template <int DK, int DV, int C, int NWV, int MODE>
+__global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
+    using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
+    using Stage = ChainStage<DK, DV, C, NWV, MODE>;
+    using M = Mma<bf16>;
+    constexpr int NT = Cfg::NT, MT = Cfg::MT, NQ = Cfg::NQ, MP = Cfg::MP, NS = Cfg::NS, NB = DV / Cfg::BW;
+    static_assert(MODE != kSumM || DV == DK, "a transition is dk x dk");
+    static_assert(DV % Cfg::BW == 0, "chain blocks");
+    __shared__ __align__(16) unsigned char sbuf[2][Cfg::BUF];
+
+    const int H = a.H;
+    const bool segmented = a.seg_len > 0;
+    const int nseg = segmented ? a.nseg : 1;
+    const int nchains = a.N * nseg * H;
+    const int wg = blockIdx.x;
+    int chain, blk;
+    if ((nchains & 7) == 0) {  // the NB blocks of a chain share an XCD (and its L2)
+        const int xcd = wg & 7, sl = wg >> 3;
+        blk = sl % NB;
+        chain = xcd + 8 * (sl / NB);
+    } else {
+        chain = wg / NB;
+        blk = wg - chain * NB;
+    }
+    const int h = chain % H, ns_idx = chain / H;
+    const int n = ns_idx / nseg, sgi = ns_idx - n * nseg;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: column bases stay scalar
+    const int grp = lane >> 4, l16 = lane & 15;
+    const int nb = blk * Cfg::BW + kTile * wid;  // this wave's first value column
+    const int nblk = nb / kTile;
+
+    int c_begin, c_end, tok_start, tok_end, lc0 = 0;
+    if (!a.cu) {
+        c_begin = n * a.nc_seq;
+        c_end = c_begin + a.nc_seq;
+        tok_start = n * a.T;
+        tok_end = tok_start + a.T;
+        if (segmented) {
+            lc0 = sgi * a.seg_len;
+            c_begin += lc0;
+            c_end = min(c_end, c_begin + a.seg_len);
+            tok_start += lc0 * C;
+            tok_end = min(tok_end, tok_start + a.seg_len * C);
+        }
+    } else {
+        c_begin = min(ld_const(a.coff, n), a.nc_max);
+        c_end = min(max(ld_const(a.coff, n + 1), c_begin), a.nc_max);
+        tok_start = clampi(ld_const(a.cu, n), 0, a.T);
+        tok_end = clampi(ld_const(a.cu, n + 1), tok_start, a.T);
+    }
+
+    // S tile m: rows 16 m + 4 grp + r, column nb + l16
+    floatx4 S[MT];
+    const size_t sbase = size_t(chain) * DK * DV;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = kTile * m + 4 * grp + r, col = nb + l16;
+            float x = 0.f;
+            if (MODE == kSumM) x = (row == col) ? 1.f : 0.f;
+            else if (MODE == kFull && a.h0) x = a.h0[sbase + size_t(row) * DV + col];
+            S[m][r] = x;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(S[m]));
+
+    static_assert(Cfg::BUF <= 65536 - 64 * MT, "staged offsets fit the LDS immediate field");
+    const int nchunks = c_end - c_begin;
+    const int last = c_end - 1;
+    const int loff = 8 * lane;
+    Stage st[NS];
+    if (nchunks > 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c_begin + s, last), h, tid, loff, nblk);
+        chain_stage_write<DK, DV, C, NWV, MODE>(sbuf[0] + opaque(0), st[0], tid);
+    }
+    __syncthreads();
+
+    const int groups = (nchunks + NS - 1) / NS;
+    for (int gi = 0; gi < groups; ++gi) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int k = gi * NS + s;           // chunk index within the chain
+            const int c = c_begin + k;
+            const bool active = k < nchunks;
+            // stage chunk c + 1 into the other buffer (opaque per-chunk bases
+            // keep the compiler from holding every LDS address in a register)
+            chain_stage_write<DK, DV, C, NWV, MODE>(sbuf[0] + opaque(((s + 1) & 1) * Cfg::BUF), st[(s + 1) % NS], tid);
+            const unsigned char *ra = sbuf[0] + opaque((s & 1) * Cfg::BUF + 16 * lane);
+            const unsigned char *rd = sbuf[0] + opaque((s & 1) * Cfg::BUF + (Cfg::KB + Cfg::PK) * 16 + 16 * grp);
+            const Stage &cur = st[s];
+
+            // B operands from the state: tiles 2p, 2p + 1
+            M::Frag sb[MP];
+#pragma unroll
+            for (int pp = 0; pp < MP; ++pp)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sb[pp][j] = static_cast<bf16>(S[2 * pp][j]);
+                    sb[pp][4 + j] = static_cast<bf16>(S[2 * pp + 1][j]);
+                }
+            const int tok0 = tok_start + k * C;
+            const int len = active ? min(C, tok_end - tok0) : 0;
+            // o rows of this chunk through a buffer resource whose range ends
+            // at row len: stores of rows past the sequence's end are dropped
+            __amdgpu_buffer_rsrc_t orsrc;
+            if (MODE == kFull)
+                orsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<bf16 *>(a.o) + (size_t(tok0) * H + h) * DV + nb,
+                                                          (short)0, len * H * DV * 2, 0x00020000);
+            M::Frag ub[NQ];
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq) ub[qq] = M::Frag{};
+#pragma unroll
+            for (int I = 0; I < NT; ++I) {
+                floatx4 xa = zero4(), oa = zero4();
+#pragma unroll
+                for (int pp = 0; pp < MP; ++pp) {
+                    const int blkoff = (I * MP + pp) * 1024;
+                    xa = M::mma(*reinterpret_cast<const M::Frag *>(ra + blkoff), sb[pp], xa);
+                    if (Cfg::HAS_Q) oa = M::mma(*reinterpret_cast<const M::Frag *>(ra + Cfg::PW * 16 + blkoff), sb[pp], oa);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ub[I >> 1][4 * (I & 1) + r] =
+                        static_cast<bf16>((MODE == kSumM ? 0.f : static_cast<float>(cur.ut[I][r])) - xa[r]);
+                if (MODE == kFull) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bf16 v = static_cast<bf16>(static_cast<float>(cur.oi[I][r]) + oa[r]);
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), orsrc,
+                                                              (4 * grp * H * DV + l16) * 2,
+                                                              (kTile * I + r) * H * DV * 2, 0);
+                    }
+                }
+            }
+            // S = Diag(e^{Gam_last}) S + (k e^{Gam_last - Gam})^T U  (kept as is past the end)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float4 d = *reinterpret_cast<const float4 *>(rd + 64 * m);
+                floatx4 acc = S[m] * floatx4{d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int qq = 0; qq < NQ; ++qq)
+                    acc = M::mma(*reinterpret_cast<const M::Frag *>(ra + Cfg::KB * 16 + (m * (Cfg::CP / 32) + qq) * 1024),
+                                 ub[qq], acc);
+                S[m] = active ? acc : S[m];
+            }
+            if (MODE == kFull && active && a.ckpt)
+                chain_ckpt<DK, DV>(a, S, n, h, lc0 + k, tok0 + C <= tok_end, grp, l16, nb);
+            // this stage's registers now take chunk c + NS
+            chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c + NS, last), h, tid, loff, nblk);
+            __syncthreads();
+        }
+    }
+
+    float *dst = nullptr;
+    if (MODE != kFull) dst = a.ht + sbase;
+    else if (a.ht && sgi == nseg - 1) dst = a.ht + size_t(n * H + h) * DK * DV;
+    if (dst) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + nb + l16] = S[m][r];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch of one (dtype, dk, dv, chunk, bv) instance.
 // ---------------------------------------------------------------------------
@@ -1145,6 +1433,42 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         prof_end(s, "kda_intra");
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if constexpr (sizeof(T) == 2) {
+        if (a.seg_len > 0) {
+            // bf16 segments: the accumulator-resident chain, 16 * NWV columns
+            // per workgroup (fewer copies of the shared operands, which is
+            // what bounds the many-chain segment passes).  One chain per
+            // (sequence, head) keeps the register-operand kernel below, whose
+            // shorter per-chunk latency wins when there are few chains.
+            constexpr int NWV = DV / kTile < 4 ? DV / kTile : 4, NWK = DK / kTile < 4 ? DK / kTile : 4;
+            constexpr int BWV = kTile * NWV, BWK = kTile * NWK;
+            const int nsc = a.N * a.nseg * a.H;
+            PrefillArgs b = a;
+            b.h0 = nullptr;
+            b.ht = a.Bseg;
+            b.ckpt = nullptr;
+            prof_begin(s);
+            hipLaunchKernelGGL((kda_chain_kernel<DK, DV, C, NWV, kSumB>), dim3(nsc * (DV / BWV)), dim3(kWave * NWV), 0,
+                               s, b);
+            prof_end(s, "kda_seg_sum_b");
+            PrefillArgs m = b;
+            m.ht = a.Mseg;
+            prof_begin(s);
+            hipLaunchKernelGGL((kda_chain_kernel<DK, DK, C, NWK, kSumM>), dim3(nsc * (DK / BWK)), dim3(kWave * NWK), 0,
+                               s, m);
+            prof_end(s, "kda_seg_sum_m");
+            prof_begin(s);
+            hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 32)), dim3(256), 0, s, a);
+            prof_end(s, "kda_seg_scan");
+            PrefillArgs f = a;
+            f.h0 = a.Sin;
+            prof_begin(s);
+            hipLaunchKernelGGL((kda_chain_kernel<DK, DV, C, NWV, kFull>), dim3(nsc * (DV / BWV)), dim3(kWave * NWV), 0,
+                               s, f);
+            prof_end(s, "kda_inter");
+            return hipGetLastError();
+        }
     }
     if (a.seg_len > 0) {
         // segment-parallel chain: summaries, scan, then the output chains

@@ -216,14 +216,17 @@ __device__ __forceinline__ float raw_get(const u32x4 *raw, int e) {
 }
 
 // Owner coordinates: role G threads own (channel group cg of 4, segment sg),
-// role V threads (channel group jg of 8, segment sg).
+// channel groups fastest (their row stores of K+, K-, Q+ are then contiguous
+// across lanes); role V threads own (channel group jg of 8, segment sg),
+// segments fastest (their only stores, the columns of (beta v)^T, are then
+// contiguous across lanes).
 template <class T, int DK, int DV, int C>
 __device__ __forceinline__ void owner_coords(int tid, bool &is_g, int &cgrp, int &sg) {
     using R = IntraRoles<T, DK, DV, C>;
     is_g = tid < R::NG;
     const int u = is_g ? tid : tid - R::NG;
-    cgrp = is_g ? u % (DK / 4) : u % (DV / 8);
-    sg = is_g ? u / (DK / 4) : u / (DV / 8);
+    cgrp = is_g ? u % (DK / 4) : u / R::NSEG;
+    sg = is_g ? u / (DK / 4) : u % R::NSEG;
 }
 
 // Value j (0..7) of token r of a role V thread.  Registers: raw[r] holds
@@ -424,8 +427,9 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 }
             }
         } else if (rt >= R::NG) {
-            const int u = tid - R::NG;
-            const int jg = u % (DV / 8), sg = u / (DV / 8);
+            bool is_g;
+            int jg, sg;
+            owner_coords<T, DK, DV, C>(tid, is_g, jg, sg);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, in.b[0] * v_get(in, 0, j), in.b[1] * v_get(in, 1, j),
@@ -489,14 +493,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 }
             }
         }
-        // ---- the next item's inputs go in flight now.  After the last item
-        //      the loads repeat this item's (and go unused): an unconditional
-        //      load keeps the registers free of merges that would wait here ----
+        // the next item (its inputs are requested during the inversion below)
         const ChunkLoc cur = loc;
         int nxt = item + gridDim.x;
         while (nxt < nitems && !locate_chunk(a, nxt / H, C, loc)) nxt += gridDim.x;
         if (nxt >= nitems) loc = cur;
-        intra_fetch(in, a, loc, (nxt < nitems ? nxt : item) % H, tid);
+        const int nxt_h = (nxt < nitems ? nxt : item) % H;
         __syncthreads();
 
         // ---- A (strictly lower, row-scaled by beta) and P (lower incl.) on
@@ -578,6 +580,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 for (int i = 0; i < 16; ++i) sL[(kTile * b + i) * A_LD + kTile * b + colx] = X[i];
             }
         }
+        // ---- the next item's inputs go in flight now: the waves the diagonal
+        //      solve leaves idle get here at once, wave 0 after it.  After the
+        //      last item the loads repeat this item's (and go unused): an
+        //      unconditional load keeps the registers free of merges that
+        //      would wait here ----
+        intra_fetch(in, a, loc, nxt_h, tid);
         __syncthreads();
         // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ
         for (int d = 1; d < NT; ++d) {

@@ -1059,24 +1059,24 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
 
 // Segment scan: the state entering segment j + 1 of (sequence n, head h) is
 // Sin_{j+1} = M_j Sin_j + B_j, Sin_0 = h0 (or zero), in fp32, serially over
-// the segments.  One workgroup per (n, h, 32 value columns); 256 threads,
-// each owning a 4 x 4 block of the 128 x 32 tile, Sin_j staged in LDS.
+// the segments.  The serial steps are short when each thread owns little:
+// one workgroup per (n, h, 8 value columns), each thread a 2 x 2 block of
+// the dk x 8 tile, Sin_j staged in LDS.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void kda_seg_scan_kernel(PrefillArgs a) {
-    constexpr int CB = DV < 32 ? DV : 32;       // columns per workgroup
+    constexpr int CB = 8;                       // columns per workgroup
     constexpr int NCB = DV / CB;
-    constexpr int CQ = CB / 4;                  // 4-column groups
-    constexpr int RQ = DK / 4;                  // 4-row groups
-    static_assert(RQ * CQ <= 256, "scan tile");
+    constexpr int CQ = CB / 2;                  // 2-column groups
+    constexpr int RQ = DK / 2;                  // 2-row groups
+    static_assert(RQ * CQ <= 256 && DV % CB == 0, "scan tile");
     __shared__ __align__(16) float sS[DK][CB];
     const int H = a.H, nseg = a.nseg;
     const int wg = blockIdx.x, cb = wg % NCB, nh = wg / NCB;
     const int n = nh / H, h = nh - n * H;
     const int tid = threadIdx.x, cq = tid % CQ, rq = tid / CQ;
     const bool active = rq < RQ;
-    const int c0 = cb * CB + 4 * cq;
+    const int c0 = cb * CB + 2 * cq;
     auto slot = [&](int j) { return size_t((n * nseg + j) * H + h); };
-    // Sin_0
     for (int i = tid; i < DK * CB; i += 256) {
         const int r = i / CB, c = i - r * CB;
         const float x = a.h0 ? a.h0[size_t(n * H + h) * DK * DV + size_t(r) * DV + cb * CB + c] : 0.f;
@@ -1085,44 +1085,38 @@ __global__ __launch_bounds__(256) void kda_seg_scan_kernel(PrefillArgs a) {
     }
     __syncthreads();
     for (int j = 0; j + 1 < nseg; ++j) {
-        float acc[4][4];
+        float acc[2][2];
         if (active) {
-            const float *Mj = a.Mseg + slot(j) * DK * DK + size_t(4 * rq) * DK;
-            const float *Bj = a.Bseg + slot(j) * DK * DV + size_t(4 * rq) * DV + c0;
+            const float *Mj = a.Mseg + slot(j) * DK * DK + size_t(2 * rq) * DK;
+            const float *Bj = a.Bseg + slot(j) * DK * DV + size_t(2 * rq) * DV + c0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float4 b = *reinterpret_cast<const float4 *>(Bj + size_t(r) * DV);
-                acc[r][0] = b.x; acc[r][1] = b.y; acc[r][2] = b.z; acc[r][3] = b.w;
+            for (int r = 0; r < 2; ++r) {
+                const float2 b = *reinterpret_cast<const float2 *>(Bj + size_t(r) * DV);
+                acc[r][0] = b.x;
+                acc[r][1] = b.y;
             }
             for (int kk = 0; kk < DK; kk += 4) {
-                float mv[4][4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float4 m4 = *reinterpret_cast<const float4 *>(Mj + size_t(r) * DK + kk);
-                    mv[r][0] = m4.x; mv[r][1] = m4.y; mv[r][2] = m4.z; mv[r][3] = m4.w;
-                }
+                const float4 m0 = *reinterpret_cast<const float4 *>(Mj + kk);
+                const float4 m1 = *reinterpret_cast<const float4 *>(Mj + DK + kk);
+                const float mv[2][4] = {{m0.x, m0.y, m0.z, m0.w}, {m1.x, m1.y, m1.z, m1.w}};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 s4 = *reinterpret_cast<const float4 *>(&sS[kk + q][4 * cq]);
+                    const float2 s2 = *reinterpret_cast<const float2 *>(&sS[kk + q][2 * cq]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        acc[r][0] += mv[r][q] * s4.x;
-                        acc[r][1] += mv[r][q] * s4.y;
-                        acc[r][2] += mv[r][q] * s4.z;
-                        acc[r][3] += mv[r][q] * s4.w;
+                    for (int r = 0; r < 2; ++r) {
+                        acc[r][0] += mv[r][q] * s2.x;
+                        acc[r][1] += mv[r][q] * s2.y;
                     }
                 }
             }
         }
         __syncthreads();  // every read of Sin_j is done
         if (active) {
-            float *dst = a.Sin + slot(j + 1) * DK * DV + size_t(4 * rq) * DV + c0;
+            float *dst = a.Sin + slot(j + 1) * DK * DV + size_t(2 * rq) * DV + c0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                *reinterpret_cast<float4 *>(&sS[4 * rq + r][4 * cq]) =
-                    make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-                *reinterpret_cast<float4 *>(dst + size_t(r) * DV) =
-                    make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+            for (int r = 0; r < 2; ++r) {
+                *reinterpret_cast<float2 *>(&sS[2 * rq + r][2 * cq]) = make_float2(acc[r][0], acc[r][1]);
+                *reinterpret_cast<float2 *>(dst + size_t(r) * DV) = make_float2(acc[r][0], acc[r][1]);
             }
         }
         __syncthreads();
@@ -1274,6 +1268,7 @@ __global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
     }
     const int h = chain % H, ns_idx = chain / H;
     const int n = ns_idx / nseg, sgi = ns_idx - n * nseg;
+    if (MODE != kFull && sgi == nseg - 1) return;  // the scan never reads the last segment's summary
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: column bases stay scalar
     const int grp = lane >> 4, l16 = lane & 15;
@@ -1467,7 +1462,7 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
                                s, m);
             prof_end(s, "kda_seg_sum_m");
             prof_begin(s);
-            hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 32)), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 8)), dim3(256), 0, s, a);
             prof_end(s, "kda_seg_scan");
             PrefillArgs f = a;
             f.h0 = a.Sin;
@@ -1498,7 +1493,7 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
                            m);
         prof_end(s, "kda_seg_sum_m");
         prof_begin(s);
-        hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 32)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 8)), dim3(256), 0, s, a);
         prof_end(s, "kda_seg_scan");
         PrefillArgs f = a;
         f.h0 = a.Sin;

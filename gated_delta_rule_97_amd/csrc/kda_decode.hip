@@ -98,93 +98,108 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const T *__restrict__ q
 // sequence n, no o, the state written back once (not at all when zero
 // tokens are accepted).  Same per-token arithmetic as kda_decode_kernel.
 // ---------------------------------------------------------------------------
-template <class T, int DK, int DV, bool VERIFY>
+template <class T, int DK, int DV, int CPB, bool VERIFY>
 __global__ __launch_bounds__(256) void kda_decode_multi_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                              const T *__restrict__ v, const float *__restrict__ g,
-                                                              const float *__restrict__ beta,
-                                                              const int32_t *__restrict__ n_accept,
-                                                              float *__restrict__ state, T *__restrict__ o, int K,
-                                                              int H) {
-    constexpr int CG = DV / 4;
+                                                                 const T *__restrict__ v, const float *__restrict__ g,
+                                                                 const float *__restrict__ beta,
+                                                                 const int32_t *__restrict__ n_accept,
+                                                                 float *__restrict__ state, T *__restrict__ o, int K,
+                                                                 int H) {
+    constexpr int CG = CPB / 4;   // float4 column groups of this workgroup's CPB value columns
     constexpr int RG = 256 / CG;
     constexpr int RPT = DK / RG;
+    constexpr int KG = 8;  // draft tokens staged in LDS at once
+    static_assert(DV % CPB == 0, "column blocks");
     static_assert(RG * CG == 256 && RPT * RG == DK, "decode thread split");
-    __shared__ float sk[DK], sq[DK], sd[DK];
-    __shared__ float4 sw[RG][CG], sy[RG][CG];
-    __shared__ float skq;
+    // a group's k, q and e^g, and the row-group partials of two tokens in turn
+    __shared__ float sk[KG][DK], sq[VERIFY ? KG : 1][DK], sd[KG][DK];
+    __shared__ float4 sw[2][RG][CG], sy[VERIFY ? 2 : 1][RG][CG];
+    __shared__ float skq[KG];
 
-    const int ch = blockIdx.x;  // sequence * H + head
+    // the value columns of S are independent: (sequence, head) spans DV / CPB
+    // workgroups, each the state's columns cb * CPB ..
+    const int ch = blockIdx.x / (DV / CPB), cb = blockIdx.x % (DV / CPB);  // ch = sequence * H + head
     const int n = ch / H, h = ch - n * H;
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const int col0 = cb * CPB;
     int ntok = K;
     if (!VERIFY) {
         const int na = n_accept[n];
         ntok = na < 0 ? 0 : (na > K ? K : na);
         if (ntok == 0) return;  // nothing accepted: the state stays as it is
     }
-    float *S = state + size_t(ch) * DK * DV;
+    float *S = state + size_t(ch) * DK * DV + col0;
 
     floatx4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
 
-    for (int t = 0; t < ntok; ++t) {
-        const size_t row = (size_t(n) * K + t) * H + h;  // token row of [N][K][H]
-        __syncthreads();  // the previous token's reads of sk/sq/sd/sw/sy are done
-        for (int c = tid; c < DK; c += 256) {
-            sk[c] = to_f32(k[row * DK + c]);
-            if (VERIFY) sq[c] = to_f32(q[row * DK + c]);
-            sd[c] = exp_e(g[row * DK + c]);
+    for (int t0 = 0; t0 < ntok; t0 += KG) {
+        const int nt = min(KG, ntok - t0);
+        __syncthreads();  // the previous group's last reads of sk/sq/sd are done
+        for (int i = tid; i < nt * DK; i += 256) {
+            const int t = i / DK, c = i - t * DK;
+            const size_t row = (size_t(n) * K + t0 + t) * H + h;  // token row of [N][K][H]
+            sk[t][c] = to_f32(k[row * DK + c]);
+            if (VERIFY) sq[t][c] = to_f32(q[row * DK + c]);
+            sd[t][c] = exp_e(g[row * DK + c]);
         }
         __syncthreads();
-        if (VERIFY && tid < 64) {
-            float p = 0.f;
-            for (int c = tid; c < DK; c += 64) p += sk[c] * sq[c];
+        if (VERIFY) {  // k . q of each token: one wave per token
+            for (int t = tid >> 6; t < nt; t += 4) {
+                float p = 0.f;
+                for (int c = tid & 63; c < DK; c += 64) p += sk[t][c] * sq[t][c];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-            if (tid == 0) skq = p;
-        }
-        float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int c = i * RG + rg;
-            const float f = sd[c], kc = sk[c];
-            s[i] *= f;
-            w.x += kc * s[i][0]; w.y += kc * s[i][1]; w.z += kc * s[i][2]; w.w += kc * s[i][3];
-            if (VERIFY) {
-                const float qc = sq[c];
-                y.x += qc * s[i][0]; y.y += qc * s[i][1]; y.z += qc * s[i][2]; y.w += qc * s[i][3];
+                for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+                if ((tid & 63) == 0) skq[t] = p;
             }
         }
-        sw[rg][cg] = w;
-        if (VERIFY) sy[rg][cg] = y;
-        __syncthreads();
-        float4 W = make_float4(0.f, 0.f, 0.f, 0.f), Y = W;
+        for (int t = 0; t < nt; ++t) {
+            const int pb = t & 1;
+            float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            const float4 a = sw[r][cg];
-            W.x += a.x; W.y += a.y; W.z += a.z; W.w += a.w;
-            if (VERIFY) {
-                const float4 b = sy[r][cg];
-                Y.x += b.x; Y.y += b.y; Y.z += b.z; Y.w += b.w;
+            for (int i = 0; i < RPT; ++i) {
+                const int c = i * RG + rg;
+                const float f = sd[t][c], kc = sk[t][c];
+                s[i] *= f;
+                w.x += kc * s[i][0]; w.y += kc * s[i][1]; w.z += kc * s[i][2]; w.w += kc * s[i][3];
+                if (VERIFY) {
+                    const float qc = sq[t][c];
+                    y.x += qc * s[i][0]; y.y += qc * s[i][1]; y.z += qc * s[i][2]; y.w += qc * s[i][3];
+                }
             }
-        }
-        const float bt = beta[row];
-        const T *vp = v + row * DV + 4 * cg;
-        float4 u;
-        u.x = bt * (to_f32(vp[0]) - W.x);
-        u.y = bt * (to_f32(vp[1]) - W.y);
-        u.z = bt * (to_f32(vp[2]) - W.z);
-        u.w = bt * (to_f32(vp[3]) - W.w);
+            sw[pb][rg][cg] = w;
+            if (VERIFY) sy[pb][rg][cg] = y;
+            __syncthreads();  // one barrier per token: the partials of two tokens alternate
+            float4 W = make_float4(0.f, 0.f, 0.f, 0.f), Y = W;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const float kc = sk[i * RG + rg];
-            s[i][0] += kc * u.x; s[i][1] += kc * u.y; s[i][2] += kc * u.z; s[i][3] += kc * u.w;
-        }
-        if (VERIFY && rg == 0) {
-            const float kq = skq;
-            store4(o + row * DV + 4 * cg, Y.x + kq * u.x, Y.y + kq * u.y, Y.z + kq * u.z, Y.w + kq * u.w);
+            for (int r = 0; r < RG; ++r) {
+                const float4 a4 = sw[pb][r][cg];
+                W.x += a4.x; W.y += a4.y; W.z += a4.z; W.w += a4.w;
+                if (VERIFY) {
+                    const float4 b4 = sy[pb][r][cg];
+                    Y.x += b4.x; Y.y += b4.y; Y.z += b4.z; Y.w += b4.w;
+                }
+            }
+            const size_t row = (size_t(n) * K + t0 + t) * H + h;
+            const float bt = beta[row];
+            const T *vp = v + row * DV + col0 + 4 * cg;
+            float4 u;
+            u.x = bt * (to_f32(vp[0]) - W.x);
+            u.y = bt * (to_f32(vp[1]) - W.y);
+            u.z = bt * (to_f32(vp[2]) - W.z);
+            u.w = bt * (to_f32(vp[3]) - W.w);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float kc = sk[t][i * RG + rg];
+                s[i][0] += kc * u.x; s[i][1] += kc * u.y; s[i][2] += kc * u.z; s[i][3] += kc * u.w;
+            }
+            if (VERIFY && rg == 0) {
+                const float kq = skq[t];
+                store4(o + row * DV + col0 + 4 * cg, Y.x + kq * u.x, Y.y + kq * u.y, Y.z + kq * u.z,
+                       Y.w + kq * u.w);
+            }
         }
     }
     if (!VERIFY) {
@@ -199,8 +214,11 @@ static hipError_t launch_multi_t(const void *q, const void *k, const void *v, co
                                  const int32_t *n_accept, float *state, void *o, int N, int K, int H,
                                  hipStream_t s) {
     if (N == 0 || K == 0) return hipSuccess;
+    // all value columns in one workgroup: splitting them repeats the token
+    // staging and doubles the row-group partials each reduction reads (slower)
+    constexpr int CPB = DV;
     prof_begin(s);
-    hipLaunchKernelGGL((kda_decode_multi_kernel<T, DK, DV, VERIFY>), dim3(N * H), dim3(256), 0, s,
+    hipLaunchKernelGGL((kda_decode_multi_kernel<T, DK, DV, CPB, VERIFY>), dim3(N * H * (DV / CPB)), dim3(256), 0, s,
                        static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
                        n_accept, state, static_cast<T *>(o), K, H);
     prof_end(s, VERIFY ? "kda_decode_verify" : "kda_decode_commit");

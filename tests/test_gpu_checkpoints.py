@@ -129,3 +129,17 @@ def test_headline_checkpoints_sampled():
         print(f"[parity]   headline checkpoint {i}: rel-L2 {e:.3e}", flush=True)
         assert e <= TOL_BF16
     assert torch.equal(ck[15], ht[0])  # 8192 = 16 x 512: the last checkpoint is the final state
+
+
+@pytest.mark.parametrize("chunk,stride,T", [(16, 16, 100), (64, 64, 200), (64, 192, 700)])
+def test_checkpoint_every_chunk_and_uneven_strides(chunk, stride, T):
+    """A checkpoint after every chunk, and a stride of three chunks that does
+    not divide the length (the trailing partial stride has no checkpoint)."""
+    spec = Spec(H=2, dk=64, dv=64, T=T, B=2, dtype="bf16", chunk=chunk, h0_std=1.0, g_mode="slow", seed=57)
+    x = workloads.make_prefill(spec)
+    (o, ht, ck), (o2, ht2) = run(x, chunk, stride)
+    assert torch.equal(o, o2) and torch.equal(ht, ht2)
+    ref = ref_checkpoints(x, stride)
+    assert ck.shape[0] == ref.shape[0] == 2 * (T // stride)
+    for i in range(ref.shape[0]):
+        assert rel_l2(to_np64(ck[i]), ref[i]) <= TOL_BF16, f"slot {i}"

@@ -135,3 +135,31 @@ def test_verify_headline_batch_sampled():
     e = rel_l2(o[seqs].double().cpu().numpy(), o_ref)
     print(f"[verify] headline batch K={K}: o {e:.2e}", flush=True)
     assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("K,dtype", [(10, "bf16"), (16, "fp32")])
+def test_verify_and_commit_span_staging_groups(K, dtype):
+    """More drafts than one staging group (8): verify's outputs at every
+    position and commits ending inside the first group, at its edge, inside
+    the second and at K."""
+    import gated_delta_rule_97_amd as kda
+    spec = workloads.DecodeSpec(N=5, H=2, dk=64, dv=128, steps=K, dtype=dtype, state_std=1.0, g_mode="slow",
+                                seed=65)
+    state0 = workloads.make_decode_state(spec)
+    x = workloads.make_decode_drafts(spec, K)
+    d = {key: val.cuda() for key, val in x.items()}
+    st = state0.cuda()
+    o = kda.decode_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], st)
+    n_acc = [3, 8, 9, K, 0]
+    kda.decode_commit(d["k"], d["v"], d["g"], d["beta"], torch.tensor(n_acc, dtype=torch.int32).cuda(), st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_drafts(x, state0, n_acc)
+    tol = TOL_FP32 if dtype == "fp32" else TOL_BF16
+    for t in range(K):
+        assert rel_l2(o[:, t].double().cpu().numpy(), o_ref[:, t]) <= tol, f"draft {t}"
+    got = st.double().cpu().numpy()
+    for n, a in enumerate(n_acc):
+        if a == 0:
+            assert torch.equal(st[n].cpu(), state0[n])
+        else:
+            assert rel_l2(got[n], s_ref[n]) <= tol, f"sequence {n} ({a} accepted)"

@@ -83,7 +83,7 @@ CALIB_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
 
 def ingest_pmc(fetch_dir, write_dir):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE; both with --calibration-copy) into profiles/traffic.json:
+    WRITE_SIZE; both with --headline-only --calibration-copy) into profiles/traffic.json:
     HBM bytes per launch of each KDA kernel, each counter scaled by what it
     reads for the 1 GiB calibration copy."""
     import csv
@@ -112,6 +112,12 @@ def ingest_pmc(fetch_dir, write_dir):
                            "write_scale": round(w_scale, 4)}}
     for k, wl in (("kda_intra", PREFILL_WORKLOAD), ("kda_inter", PREFILL_WORKLOAD), ("kda_decode", DECODE_WORKLOAD)):
         if k in fetch and k in write:
+            for c, vals in (("FETCH_SIZE", fetch[k]), ("WRITE_SIZE", write[k])):
+                # every dispatch must be the one workload: a run that also launched the
+                # kernel on other shapes (the rows beyond the headline) would skew the mean
+                if max(vals) > 1.25 * min(vals) + 64:
+                    raise SystemExit(f"{k}: {c} ranges {min(vals):.0f}..{max(vals):.0f} KiB over {len(vals)} "
+                                     "dispatches; take the counter runs with --headline-only")
             fk, wk = statistics.mean(fetch[k]), statistics.mean(write[k])
             out[k] = {"workload": wl, "source_digest": source_digest(), "dispatches": len(fetch[k]),
                       "fetch_size_kib": round(fk, 1), "write_size_kib": round(wk, 1),
@@ -124,6 +130,34 @@ def ingest_pmc(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def trace_summary(trace_dir):
+    """Markdown table of a rocprofv3 --kernel-trace run of this script, one row
+    per KDA kernel, grid, workgroup size and workload: the same kernel launched
+    on several workloads keeps a row for each instead of one merged average.
+    Persistent kernels keep their grid across workloads, so launches of one
+    shape are further split where the sorted durations jump by more than 2x."""
+    import csv
+    rows = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "kda" not in name:
+                continue
+            key = (name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid | workgroup | calls | avg us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid, wg), ts in sorted(rows.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        groups = []
+        for t in sorted(ts):
+            if groups and t <= 2.0 * groups[-1][0]:
+                groups[-1].append(t)
+            else:
+                groups.append([t])
+        for g in groups:
+            print(f"| `{name}` | {grid} | {wg} | {len(g)} | {sum(g) / len(g):.1f} | {min(g):.1f} | {max(g):.1f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,9 +167,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="finish with a 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run only the headline prefill and decode (counter runs: no other launches of "
+                         "these kernels on other shapes)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print per-launch-shape kernel times of a rocprofv3 --kernel-trace run; no GPU needed")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs; no GPU needed")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc)
         return
@@ -259,89 +301,93 @@ def main():
 
     # ------------------------------------- next rows: verify, checkpoints,
     # long context (each with its own algorithmic bytes and roofline)
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+    def next_rows():
+        def timed(fn, reps):
             fn()
-        e1.record(stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps  # ms
+
+        K = 4
+        drafts = workloads.make_decode_drafts(dspec, K, device=dev)
+        ov = torch.empty((dspec.N, K, dspec.H, dspec.dv), dtype=torch.bfloat16, device=dev)
+        nacc = torch.full((dspec.N,), K, dtype=torch.int32, device=dev)
+        st_v = state0.clone()
+        t_verify = timed(lambda: kda.decode_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"], drafts["beta"],
+                                                   st_v, o=ov), 20)
+        st_c = state0.clone()
+        t_commit = timed(lambda: kda.decode_commit(drafts["k"], drafts["v"], drafts["g"], drafts["beta"], nacc, st_c),
+                         20)
+        nh = dspec.N * dspec.H
+        vbytes = nh * (dspec.dk * dspec.dv * 4 + K * 1540)            # state read once + K tokens' vectors
+        cbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * 1284)        # state read + written, no q or o
+        vgbs = vbytes / (t_verify * 1e-3) / 1e9
+        cgbs = cbytes / (t_commit * 1e-3) / 1e9
+        log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s)")
+        verify = {"workload": f"decode batch N={dspec.N} H={dspec.H} d=128 bf16, {K} draft tokens",
+                  "verify_us": round(t_verify * 1e3, 2), "commit_us": round(t_commit * 1e3, 2),
+                  "draft_tokens_per_s": round(dspec.N * K / (t_verify * 1e-3), 1),
+                  "vs_k_decode_steps": round(K * dec_launch_us / (t_verify * 1e3 + t_commit * 1e3), 3),
+                  "roofline": {"kernel": "kda_decode_verify", "bound": "hbm", "achieved": round(vgbs, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(vgbs / HBM_PEAK_GBS, 4),
+                               "traffic": None, "avg_launch_us": round(t_verify * 1e3, 2),
+                               "algorithmic_bytes_per_launch": vbytes},
+                  "commit_roofline": {"kernel": "kda_decode_commit", "bound": "hbm", "achieved": round(cgbs, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cgbs / HBM_PEAK_GBS, 4),
+                                      "avg_launch_us": round(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes}}
+        del drafts, ov, st_v, st_c
+
+        stride = 512
+        nck = kda.checkpoint_count(T, stride, B)
+        ck = torch.empty((nck, H, dk, dv), dtype=torch.float32, device=dev)
+        t_plain = timed(step, 10)
+        t_ck = timed(lambda: kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=C, o=o,
+                                               ht=ht, workspace=ws, ckpt_stride=stride, ckpt=ck), 10)
+        ckpt = {"workload": f"{workload}, a state checkpoint every {stride} tokens ({nck} per head)",
+                "ms_per_call": round(t_ck, 4), "plain_ms_per_call": round(t_plain, 4),
+                "overhead_frac": round(t_ck / t_plain - 1.0, 4), "checkpoint_bytes": nck * H * dk * dv * 4}
+        log(f"checkpoints: {t_ck * 1e3:.1f} us/call vs {t_plain * 1e3:.1f} plain")
+        del ck
+
+        lspec = workloads.CONFIGS[3]
+        log(f"long context: {lspec.name}")
+        xl = workloads.make_prefill(lspec, device=dev)
+        wl = torch.empty(kda.workspace_bytes(lspec.B, lspec.T, lspec.H, lspec.dk, lspec.dv, lspec.B, lspec.chunk,
+                                             kda.KDA_DTYPE_BF16), dtype=torch.uint8, device=dev)
+        ol = torch.empty((lspec.B, lspec.T, lspec.H, lspec.dv), dtype=torch.bfloat16, device=dev)
+        hl = torch.empty((lspec.B, lspec.H, lspec.dk, lspec.dv), dtype=torch.float32, device=dev)
+
+        def long_step(flags=0):
+            kda.chunk_prefill(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"], None, chunk_size=lspec.chunk, o=ol, ht=hl,
+                              workspace=wl, flags=flags)
+
+        t_single = timed(lambda: long_step(kda.KDA_FLAG_NO_SEGMENTS), 2)
+        long_step()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps  # ms
+        kda.kda_profile_start(64)
+        t_long = timed(long_step, 3)
+        lkt = kda.kda_profile_stop()
+        lth = lspec.B * lspec.T * lspec.H
+        lbytes = BYTES_PER_TOKEN_HEAD * lth + lspec.B * lspec.H * lspec.dk * lspec.dv * 4
+        lgbs = lbytes / (t_long * 1e-3) / 1e9
+        log(f"long context: {t_long:.2f} ms/call segmented, {t_single:.2f} ms single chain")
+        long_ctx = {"workload": lspec.name.replace("long-context prefill ", "prefill ") + " chunk=64",
+                    "ms_per_call": round(t_long, 3), "tokens_per_s": round(lspec.B * lspec.T / (t_long * 1e-3), 1),
+                    "single_chain_ms_per_call": round(t_single, 3),
+                    "kernels_us": {k: round(1e3 * v[1] / v[0], 1) for k, v in lkt.items()},
+                    "path_roofline": {"bound": "hbm", "algorithmic_bytes": lbytes, "achieved_GBps": round(lgbs, 1),
+                                      "hbm_frac": round(lgbs / HBM_PEAK_GBS, 4),
+                                      "hbm_floor_ms": round(lbytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}}
+        del xl, wl, ol, hl
+        torch.cuda.empty_cache()
+        return {"speculative_verify": verify, "checkpoints": ckpt, "long_context": long_ctx}
 
-    K = 4
-    drafts = workloads.make_decode_drafts(dspec, K, device=dev)
-    ov = torch.empty((dspec.N, K, dspec.H, dspec.dv), dtype=torch.bfloat16, device=dev)
-    nacc = torch.full((dspec.N,), K, dtype=torch.int32, device=dev)
-    st_v = state0.clone()
-    t_verify = timed(lambda: kda.decode_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"], drafts["beta"],
-                                               st_v, o=ov), 20)
-    st_c = state0.clone()
-    t_commit = timed(lambda: kda.decode_commit(drafts["k"], drafts["v"], drafts["g"], drafts["beta"], nacc, st_c),
-                     20)
-    nh = dspec.N * dspec.H
-    vbytes = nh * (dspec.dk * dspec.dv * 4 + K * 1540)            # state read once + K tokens' vectors
-    cbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * 1284)        # state read + written, no q or o
-    vgbs = vbytes / (t_verify * 1e-3) / 1e9
-    cgbs = cbytes / (t_commit * 1e-3) / 1e9
-    log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s)")
-    verify = {"workload": f"decode batch N={dspec.N} H={dspec.H} d=128 bf16, {K} draft tokens",
-              "verify_us": round(t_verify * 1e3, 2), "commit_us": round(t_commit * 1e3, 2),
-              "draft_tokens_per_s": round(dspec.N * K / (t_verify * 1e-3), 1),
-              "vs_k_decode_steps": round(K * dec_launch_us / (t_verify * 1e3 + t_commit * 1e3), 3),
-              "roofline": {"kernel": "kda_decode_verify", "bound": "hbm", "achieved": round(vgbs, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(vgbs / HBM_PEAK_GBS, 4),
-                           "traffic": None, "avg_launch_us": round(t_verify * 1e3, 2),
-                           "algorithmic_bytes_per_launch": vbytes},
-              "commit_roofline": {"kernel": "kda_decode_commit", "bound": "hbm", "achieved": round(cgbs, 1),
-                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cgbs / HBM_PEAK_GBS, 4),
-                                  "avg_launch_us": round(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes}}
-    del drafts, ov, st_v, st_c
-
-    stride = 512
-    nck = kda.checkpoint_count(T, stride, B)
-    ck = torch.empty((nck, H, dk, dv), dtype=torch.float32, device=dev)
-    t_plain = timed(step, 10)
-    t_ck = timed(lambda: kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=C, o=o,
-                                           ht=ht, workspace=ws, ckpt_stride=stride, ckpt=ck), 10)
-    ckpt = {"workload": f"{workload}, a state checkpoint every {stride} tokens ({nck} per head)",
-            "ms_per_call": round(t_ck, 4), "plain_ms_per_call": round(t_plain, 4),
-            "overhead_frac": round(t_ck / t_plain - 1.0, 4), "checkpoint_bytes": nck * H * dk * dv * 4}
-    log(f"checkpoints: {t_ck * 1e3:.1f} us/call vs {t_plain * 1e3:.1f} plain")
-    del ck
-
-    lspec = workloads.CONFIGS[3]
-    log(f"long context: {lspec.name}")
-    xl = workloads.make_prefill(lspec, device=dev)
-    wl = torch.empty(kda.workspace_bytes(lspec.B, lspec.T, lspec.H, lspec.dk, lspec.dv, lspec.B, lspec.chunk,
-                                         kda.KDA_DTYPE_BF16), dtype=torch.uint8, device=dev)
-    ol = torch.empty((lspec.B, lspec.T, lspec.H, lspec.dv), dtype=torch.bfloat16, device=dev)
-    hl = torch.empty((lspec.B, lspec.H, lspec.dk, lspec.dv), dtype=torch.float32, device=dev)
-
-    def long_step(flags=0):
-        kda.chunk_prefill(xl["q"], xl["k"], xl["v"], xl["g"], xl["beta"], None, chunk_size=lspec.chunk, o=ol, ht=hl,
-                          workspace=wl, flags=flags)
-
-    t_single = timed(lambda: long_step(kda.KDA_FLAG_NO_SEGMENTS), 2)
-    long_step()
-    torch.cuda.synchronize()
-    kda.kda_profile_start(64)
-    t_long = timed(long_step, 3)
-    lkt = kda.kda_profile_stop()
-    lth = lspec.B * lspec.T * lspec.H
-    lbytes = BYTES_PER_TOKEN_HEAD * lth + lspec.B * lspec.H * lspec.dk * lspec.dv * 4
-    lgbs = lbytes / (t_long * 1e-3) / 1e9
-    log(f"long context: {t_long:.2f} ms/call segmented, {t_single:.2f} ms single chain")
-    long_ctx = {"workload": lspec.name.replace("long-context prefill ", "prefill ") + " chunk=64",
-                "ms_per_call": round(t_long, 3), "tokens_per_s": round(lspec.B * lspec.T / (t_long * 1e-3), 1),
-                "single_chain_ms_per_call": round(t_single, 3),
-                "kernels_us": {k: round(1e3 * v[1] / v[0], 1) for k, v in lkt.items()},
-                "path_roofline": {"bound": "hbm", "algorithmic_bytes": lbytes, "achieved_GBps": round(lgbs, 1),
-                                  "hbm_frac": round(lgbs / HBM_PEAK_GBS, 4),
-                                  "hbm_floor_ms": round(lbytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}}
-    del xl, wl, ol, hl
-    torch.cuda.empty_cache()
+    nxt = None if args.headline_only else next_rows()
 
     # -------------------------------------------- oracle on the host cores
     cpu = None
@@ -353,12 +399,17 @@ def main():
         h0 = x["h0"].numpy().astype(np.float64)
         threads = oracle.max_threads()
         log(f"oracle on the host: full workload, {threads} threads")
-        t0 = time.perf_counter()
-        o_ref, ht_ref = oracle.prefill(q, k, v, g, b, h0)
-        t_cpu = time.perf_counter() - t0
-        cpu = {"value": round(tokens / t_cpu, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        # the whole workload, repeated until about 10 s of wall time have passed
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            o_ref, ht_ref = oracle.prefill(q, k, v, g, b, h0)
+            reps += 1
+            t_cpu = time.perf_counter() - t0
+            if t_cpu >= 10.0 or reps >= 64:
+                break
+        cpu = {"value": round(reps * tokens / t_cpu, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the full headline workload ({T} tokens x {H} heads), fp64 token loop, "
-                         f"{t_cpu:.2f} s wall",
+                         f"{reps} runs in {t_cpu:.2f} s wall",
                "host_cpus": os.cpu_count()}
         step()
         torch.cuda.synchronize()
@@ -366,18 +417,23 @@ def main():
         hn = ht.double().cpu().numpy()
         rel = lambda a, r: float(np.linalg.norm(a - r) / np.linalg.norm(r))
         parity = {"o_rel_l2": rel(on, o_ref), "ht_rel_l2": rel(hn, ht_ref), "tol": 2e-2}
-        log(f"oracle {t_cpu:.2f} s; parity o {parity['o_rel_l2']:.2e} ht {parity['ht_rel_l2']:.2e}")
+        log(f"oracle {reps} x {t_cpu / reps:.2f} s; parity o {parity['o_rel_l2']:.2e} ht {parity['ht_rel_l2']:.2e}")
 
         # decode baseline: the first 4 steps of the decode workload
         ref_state = state0.double().cpu().numpy()
-        t0 = time.perf_counter()
-        for s in range(4):
-            xi = steps_in[s]
+        nd, t0 = 0, time.perf_counter()
+        while nd < dspec.steps:
+            xi = steps_in[nd]
             oracle.decode_step(*(workloads.to_numpy_f32(xi[n]) for n in ("q", "k", "v", "g", "beta")),
                                ref_state)
-        t_dec_cpu = (time.perf_counter() - t0) / 4
+            nd += 1
+            if time.perf_counter() - t0 >= 5.0:
+                break
+        t_dec_cpu = (time.perf_counter() - t0) / nd
         decode["cpu_baseline"] = {"value": round(1.0 / t_dec_cpu, 3), "unit": "steps/s", "cores": threads,
-                                  "kind": "oracle", "sample": "first 4 of the 128 decode steps"}
+                                  "kind": "oracle",
+                                  "sample": f"the first {nd} of the {dspec.steps} decode steps, "
+                                            f"{t_dec_cpu * nd:.2f} s wall"}
 
     if args.calibration_copy:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
@@ -396,7 +452,7 @@ def main():
            "roofline": roofline, "path_roofline": path_roofline,
            "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
            "cpu_baseline": cpu, "parity": parity, "decode": decode,
-           "next": {"speculative_verify": verify, "checkpoints": ckpt, "long_context": long_ctx},
+           "next": nxt,
            "source_digest": source_digest()}
     print(json.dumps(out), flush=True)
 

@@ -430,8 +430,10 @@ int kda_profile_start(int max_launches) {
     if (g_prof.active) return KDA_ERR_SHAPE;
     for (hipEvent_t e : g_prof.evs) (void)hipEventDestroy(e);
     g_prof.evs.assign(2 * size_t(max_launches), nullptr);
+    // timing-only events: without the system-scope fence an event record
+    // costs no cache write-back between the launches it brackets
     for (auto &e : g_prof.evs)
-        if (hipEventCreate(&e) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return KDA_ERR_LAUNCH;
     g_prof.names.assign(size_t(max_launches), std::string());
     g_prof.cap = max_launches;
     g_prof.used = 0;

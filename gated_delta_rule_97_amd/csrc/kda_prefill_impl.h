@@ -147,7 +147,8 @@ struct IntraLds {
     static constexpr int KT_LD = C + PT;        // transposed operands [DK|DV][C]
     static constexpr int A_LD = C + 4;          // fp32 A, L           [C][C]
     static constexpr int P_LD = C + PT;         // P                   [C][C]
-    static constexpr int Y_LD = 20;             // fp32 16x16 scratch
+    static constexpr int Y_LD = 20;             // fp32 16x16 tile of L^T, padded rows
+    static constexpr int NLT = NT * (NT - 1) / 2;  // L^T tiles (K, J), J <= K <= NT - 2
     static constexpr size_t kKK = size_t(2) * C * K_LD * sizeof(T);  // K+ and K-
     static constexpr size_t kAL = size_t(2) * C * A_LD * 4;          // A and L (reuse K+, K-)
     static constexpr size_t oKp = 0;
@@ -159,7 +160,7 @@ struct IntraLds {
     static constexpr size_t oVT = oKT + size_t(DK) * KT_LD * sizeof(T);
     static constexpr size_t oP = oVT + size_t(DV) * KT_LD * sizeof(T);
     static constexpr size_t oY = oP + size_t(C) * P_LD * sizeof(T);
-    static constexpr size_t oTot = oY + size_t(3) * 16 * Y_LD * 4;
+    static constexpr size_t oTot = oY + size_t(NLT > 0 ? NLT : 1) * 16 * Y_LD * 4;
     static constexpr size_t oF = oTot + size_t(NSEG + 1) * DK * 4;
     static constexpr size_t oR = oF + size_t(NOFF > 0 ? NOFF : 1) * DK * 4;
     static constexpr size_t oB = oR + size_t(NT) * DK * 4;
@@ -578,6 +579,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sL[(kTile * b + i) * A_LD + kTile * b + colx] = X[i];
+                if (b <= NT - 2) {  // its transpose, for the off-diagonal products
+                    float *t = sY + ((b * (b + 1)) / 2 + b) * 16 * Y_LD + colx * Y_LD;
+#pragma unroll
+                    for (int i = 0; i < 16; i += 4)
+                        *reinterpret_cast<floatx4 *>(t + i) = floatx4{X[i], X[i + 1], X[i + 2], X[i + 3]};
+                }
             }
         }
         // ---- the next item's inputs go in flight now: the waves the diagonal
@@ -587,37 +594,35 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         //      would wait here ----
         intra_fetch(in, a, loc, nxt_h, tid);
         __syncthreads();
-        // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ
+        // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.
+        // The fp32 16x16x4 products take their k in the order 4 * grp + kk, so
+        // a lane's four A values are one 16-byte row read, its four B values
+        // one 16-byte read of L^T (tile (K, J) of sY holds L_KJ transposed),
+        // and the sum Y itself, as the accumulator leaves it, is the B operand
+        // of the product with L_II: Y never leaves the registers.
         for (int d = 1; d < NT; ++d) {
             const int nb = NT - d;
             if (wid < nb) {
                 const int I = d + wid, J = wid;
                 floatx4 acc = zero4();
                 for (int K = J; K < I; ++K) {
+                    const floatx4 af = *reinterpret_cast<const floatx4 *>(sA + (kTile * I + l16) * A_LD + kTile * K +
+                                                                          4 * grp);
+                    const floatx4 bf = *reinterpret_cast<const floatx4 *>(sY + ((K * (K + 1)) / 2 + J) * 16 * Y_LD +
+                                                                          l16 * Y_LD + 4 * grp);
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const float af = sA[(kTile * I + l16) * A_LD + kTile * K + 4 * kk + grp];
-                        const float bf = sL[(kTile * K + 4 * kk + grp) * A_LD + kTile * J + l16];
-                        acc = mma_f32(af, bf, acc);
-                    }
+                    for (int kk = 0; kk < 4; ++kk) acc = mma_f32(af[kk], bf[kk], acc);
                 }
-                float *Y = sY + wid * 16 * Y_LD;
+                const floatx4 lf = *reinterpret_cast<const floatx4 *>(sL + (kTile * I + l16) * A_LD + kTile * I +
+                                                                      4 * grp);
+                floatx4 out = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Y[(4 * grp + r) * Y_LD + l16] = acc[r];
-            }
-            __syncthreads();
-            if (wid < nb) {
-                const int I = d + wid, J = wid;
-                const float *Y = sY + wid * 16 * Y_LD;
-                floatx4 acc = zero4();
+                for (int kk = 0; kk < 4; ++kk) out = mma_f32(lf[kk], acc[kk], out);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const float af = sL[(kTile * I + l16) * A_LD + kTile * I + 4 * kk + grp];
-                    const float bf = Y[(4 * kk + grp) * Y_LD + l16];
-                    acc = mma_f32(af, bf, acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -acc[r];
+                for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -out[r];
+                if (I <= NT - 2)
+                    *reinterpret_cast<floatx4 *>(sY + ((I * (I + 1)) / 2 + J) * 16 * Y_LD + l16 * Y_LD + 4 * grp) =
+                        floatx4{-out[0], -out[1], -out[2], -out[3]};
             }
             __syncthreads();
         }

@@ -564,8 +564,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         __syncthreads();
 
         // ---- L = (I + A)^-1 by blocked forward substitution (fp32) ----
-        // the NT diagonal 16x16 blocks, one column per lane (wave 0)
-        if (wid == 0) {
+        // the NT diagonal 16x16 blocks, one column per lane, on a wave that
+        // loads no inputs, so the owner waves issue the next item's loads
+        // meanwhile
+        constexpr int kSolveWave = (IntraRoles<T, DK, DV, C>::NG + IntraRoles<T, DK, DV, C>::NV + kWave - 1) / kWave;
+        static_assert(kSolveWave < kIWaves, "a wave with no input role");
+        if (wid == kSolveWave) {
             const int b = lane >> 4, colx = lane & 15;
             if (b < NT) {
                 const float *Ab = sA + (kTile * b) * A_LD + kTile * b;
@@ -587,8 +591,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 }
             }
         }
-        // ---- the next item's inputs go in flight now: the waves the diagonal
-        //      solve leaves idle get here at once, wave 0 after it.  After the
+        // ---- the next item's inputs go in flight now, beside the diagonal
+        //      solve.  After the
         //      last item the loads repeat this item's (and go unused): an
         //      unconditional load keeps the registers free of merges that
         //      would wait here ----

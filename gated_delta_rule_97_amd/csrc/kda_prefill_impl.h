@@ -563,13 +563,15 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         }
         __syncthreads();
 
-        // ---- L = (I + A)^-1 by blocked forward substitution (fp32) ----
-        // the NT diagonal 16x16 blocks, one column per lane, on a wave that
-        // loads no inputs, so the owner waves issue the next item's loads
-        // meanwhile
+        // ---- L = (I + A)^-1 by blocked forward substitution (fp32), all of it
+        //      on one wave that loads no inputs, while the owner waves issue
+        //      the next item's loads: the wave reads back only what it wrote
+        //      itself (its LDS accesses complete in order), so the inverse
+        //      needs no barrier of its own ----
         constexpr int kSolveWave = (IntraRoles<T, DK, DV, C>::NG + IntraRoles<T, DK, DV, C>::NV + kWave - 1) / kWave;
         static_assert(kSolveWave < kIWaves, "a wave with no input role");
         if (wid == kSolveWave) {
+            // the NT diagonal 16x16 blocks, one column per lane
             const int b = lane >> 4, colx = lane & 15;
             if (b < NT) {
                 const float *Ab = sA + (kTile * b) * A_LD + kTile * b;
@@ -590,46 +592,46 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                         *reinterpret_cast<floatx4 *>(t + i) = floatx4{X[i], X[i + 1], X[i + 2], X[i + 3]};
                 }
             }
+            // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.
+            // The fp32 16x16x4 products take their k in the order 4 * grp + kk,
+            // so a lane's four A values are one 16-byte row read, its four B
+            // values one 16-byte read of L^T (tile (K, J) of sY holds L_KJ
+            // transposed), and the sum Y itself, as the accumulator leaves it,
+            // is the B operand of the product with L_II.
+#pragma unroll
+            for (int d = 1; d < NT; ++d) {
+#pragma unroll
+                for (int J = 0; J + d < NT; ++J) {
+                    const int I = J + d;
+                    floatx4 acc = zero4();
+#pragma unroll
+                    for (int K = J; K < I; ++K) {
+                        const floatx4 af = *reinterpret_cast<const floatx4 *>(sA + (kTile * I + l16) * A_LD +
+                                                                              kTile * K + 4 * grp);
+                        const floatx4 bf = *reinterpret_cast<const floatx4 *>(
+                            sY + ((K * (K + 1)) / 2 + J) * 16 * Y_LD + l16 * Y_LD + 4 * grp);
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) acc = mma_f32(af[kk], bf[kk], acc);
+                    }
+                    const floatx4 lf = *reinterpret_cast<const floatx4 *>(sL + (kTile * I + l16) * A_LD + kTile * I +
+                                                                          4 * grp);
+                    floatx4 out = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) out = mma_f32(lf[kk], acc[kk], out);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -out[r];
+                    if (I <= NT - 2)
+                        *reinterpret_cast<floatx4 *>(sY + ((I * (I + 1)) / 2 + J) * 16 * Y_LD + l16 * Y_LD +
+                                                     4 * grp) = floatx4{-out[0], -out[1], -out[2], -out[3]};
+                }
+            }
         }
-        // ---- the next item's inputs go in flight now, beside the diagonal
-        //      solve.  After the
-        //      last item the loads repeat this item's (and go unused): an
-        //      unconditional load keeps the registers free of merges that
-        //      would wait here ----
+        // ---- the next item's inputs go in flight now, beside the inverse.
+        //      After the last item the loads repeat this item's (and go
+        //      unused): an unconditional load keeps the registers free of
+        //      merges that would wait here ----
         intra_fetch(in, a, loc, nxt_h, tid);
         __syncthreads();
-        // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.
-        // The fp32 16x16x4 products take their k in the order 4 * grp + kk, so
-        // a lane's four A values are one 16-byte row read, its four B values
-        // one 16-byte read of L^T (tile (K, J) of sY holds L_KJ transposed),
-        // and the sum Y itself, as the accumulator leaves it, is the B operand
-        // of the product with L_II: Y never leaves the registers.
-        for (int d = 1; d < NT; ++d) {
-            const int nb = NT - d;
-            if (wid < nb) {
-                const int I = d + wid, J = wid;
-                floatx4 acc = zero4();
-                for (int K = J; K < I; ++K) {
-                    const floatx4 af = *reinterpret_cast<const floatx4 *>(sA + (kTile * I + l16) * A_LD + kTile * K +
-                                                                          4 * grp);
-                    const floatx4 bf = *reinterpret_cast<const floatx4 *>(sY + ((K * (K + 1)) / 2 + J) * 16 * Y_LD +
-                                                                          l16 * Y_LD + 4 * grp);
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) acc = mma_f32(af[kk], bf[kk], acc);
-                }
-                const floatx4 lf = *reinterpret_cast<const floatx4 *>(sL + (kTile * I + l16) * A_LD + kTile * I +
-                                                                      4 * grp);
-                floatx4 out = zero4();
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) out = mma_f32(lf[kk], acc[kk], out);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -out[r];
-                if (I <= NT - 2)
-                    *reinterpret_cast<floatx4 *>(sY + ((I * (I + 1)) / 2 + J) * 16 * Y_LD + l16 * Y_LD + 4 * grp) =
-                        floatx4{-out[0], -out[1], -out[2], -out[3]};
-            }
-            __syncthreads();
-        }
 
         // ---- W = L (beta k e^Gam) as W^T = (beta k e^Gam)^T L^T, so that a
         //      lane's output is four consecutive channels of one token;

@@ -646,7 +646,9 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         constexpr int KSTEPS = (C + M::K - 1) / M::K;
         static_assert(kIWaves % NT == 0, "a wave keeps one token tile");
         const int tt = wid % NT;
-        const int ks = min(KSTEPS, (kTile * (tt + 1) + M::K - 1) / M::K);  // L and P are lower triangular
+        // the k-steps past the diagonal tile multiply the zero upper tiles of L
+        // and P: doing them keeps every operand read unconditional, so a wave
+        // issues all its LDS reads before its first product
         // k-fragment kk of a row starting at p; zero past the chunk (when C < K)
         auto frag_at = [&](const T *p, int kk) -> Frag {
             const int kb = kk * M::K + grp * M::KPL;
@@ -668,12 +670,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     const T *ob = sKT + (kTile * (wi / NT) + l16) * KT_LD;
 #pragma unroll
                     for (int kk = 0; kk < KSTEPS; ++kk)
-                        if (kk < ks) acc = M::mma(frag_at(ob, kk), lf[kk], acc);
+                        acc = M::mma(frag_at(ob, kk), lf[kk], acc);
                 } else if (wi < NITEM) {
                     const T *ob = sVT + (kTile * ((wi - NIW) / NT) + l16) * KT_LD;
 #pragma unroll
                     for (int kk = 0; kk < KSTEPS; ++kk)
-                        if (kk < ks) acc = M::mma(lf[kk], frag_at(ob, kk), acc);
+                        acc = M::mma(lf[kk], frag_at(ob, kk), acc);
                 }
                 res[it] = acc;
             }
@@ -720,7 +722,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     const T *ob = sKT + (kTile * cc + l16) * KT_LD;
 #pragma unroll
                     for (int kk = 0; kk < KSTEPS; ++kk)
-                        if (kk < ks) acc = M::mma(frag_at(ob, kk), pf[kk], acc);
+                        acc = M::mma(frag_at(ob, kk), pf[kk], acc);
                     // q e^Gam = Q+ e^{r_I} (token tile tt)
                     const int t = kTile * tt + l16, c0 = kTile * cc + 4 * grp;
                     const T *qp = sQp + t * K_LD + c0;
@@ -732,7 +734,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     const T *ob = sVT + (kTile * n + l16) * KT_LD;
 #pragma unroll
                     for (int kk = 0; kk < KSTEPS; ++kk)
-                        if (kk < ks) acc = M::mma(pf[kk], frag_at(ob, kk), acc);
+                        acc = M::mma(pf[kk], frag_at(ob, kk), acc);
                     store4(Og + quad_off<DV>(tt, n, lane), acc[0], acc[1], acc[2], acc[3]);
                 }
             }

@@ -767,7 +767,10 @@ template <> struct Quad<float> {
 // (ht or a checkpoint).  SUM_B: a segment's end state from a zero start, no
 // outputs.  SUM_M: a segment's transition, the chain applied to an identity
 // block with no value input (U = -W S), no outputs; instanced with DV = DK.
-enum InterMode { kFull = 0, kSumB = 1, kSumM = 2 };
+// kSumBM (accumulator-resident chain only, dk == dv): both segment summaries
+// in one pass, the first half of the waves carrying B and the second half M,
+// all of them on the same staged chunk operands.
+enum InterMode { kFull = 0, kSumB = 1, kSumM = 2, kSumBM = 3 };
 
 template <class T, int DK, int DV, int C, int BV>
 struct InterCfg {
@@ -1169,8 +1172,8 @@ __device__ __forceinline__ void chain_ckpt(const PrefillArgs &a, const floatx4 (
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int C, int NWV, int MODE>
 struct ChainCfg {
-    static constexpr int NTHR = kWave * NWV;
-    static constexpr int BW = kTile * NWV;                  // value columns per workgroup
+    static constexpr int NTHR = kWave * NWV * (MODE == kSumBM ? 2 : 1);
+    static constexpr int BW = kTile * NWV;                  // columns per workgroup (per half in kSumBM)
     static constexpr int NT = C / kTile, MT = DK / kTile;
     static constexpr int NQ = (NT + 1) / 2, MP = MT / 2;    // 32-wide token / dk slices
     static constexpr int CP = kpad<bf16>(C);                // K~^T row length (operand order)
@@ -1198,7 +1201,7 @@ struct ChainStage {
 // order) at this lane's positions.  Bases are uniform (scalar registers).
 template <int DK, int DV, int C, int NWV, int MODE>
 __device__ __forceinline__ void chain_load(ChainStage<DK, DV, C, NWV, MODE> &st, const PrefillArgs &a, int gc, int h,
-                                           int tid, int loff, int nblk) {
+                                           int tid, int loff, int nblk, bool isM) {
     using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
     const size_t slot = size_t(gc) * a.H + h;
     const char *W = static_cast<const char *>(a.W) + slot * Cfg::W_EL * 2;
@@ -1215,7 +1218,7 @@ __device__ __forceinline__ void chain_load(ChainStage<DK, DV, C, NWV, MODE> &st,
         else src = D + (p - Cfg::KB - Cfg::PK) * 16;
         st.stg[i] = *reinterpret_cast<const u32x4 *>(src);
     }
-    if (MODE != kSumM) {
+    if (MODE != kSumM && !(MODE == kSumBM && isM)) {
         // quad order: tile (I, nblk) is 256 values, lane l holds 4 of them
         const char *U = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.Ut) + slot * C * DV + nblk * 256);
         const char *O = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.Oi) + slot * C * DV + nblk * 256);
@@ -1256,12 +1259,12 @@ __device__ __forceinline__ void chain_stage_write(unsigned char *buf, const Chai
 }
 
 template <int DK, int DV, int C, int NWV, int MODE>
-__global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kWave * NWV * (MODE == kSumBM ? 2 : 1)) void kda_chain_kernel(PrefillArgs a) {
     using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
     using Stage = ChainStage<DK, DV, C, NWV, MODE>;
     using M = Mma<bf16>;
     constexpr int NT = Cfg::NT, MT = Cfg::MT, NQ = Cfg::NQ, MP = Cfg::MP, NS = Cfg::NS, NB = DV / Cfg::BW;
-    static_assert(MODE != kSumM || DV == DK, "a transition is dk x dk");
+    static_assert((MODE != kSumM && MODE != kSumBM) || DV == DK, "a transition is dk x dk");
     static_assert(DV % Cfg::BW == 0, "chain blocks");
     __shared__ __align__(16) unsigned char sbuf[2][Cfg::BUF];
 
@@ -1285,7 +1288,9 @@ __global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: column bases stay scalar
     const int grp = lane >> 4, l16 = lane & 15;
-    const int nb = blk * Cfg::BW + kTile * wid;  // this wave's first value column
+    // the transition's waves (all of them in kSumM, the second half in kSumBM)
+    const bool isM = MODE == kSumM || (MODE == kSumBM && wid >= NWV);
+    const int nb = blk * Cfg::BW + kTile * (MODE == kSumBM && isM ? wid - NWV : wid);  // first column
     const int nblk = nb / kTile;
 
     int c_begin, c_end, tok_start, tok_end, lc0 = 0;
@@ -1317,7 +1322,7 @@ __global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
         for (int r = 0; r < 4; ++r) {
             const int row = kTile * m + 4 * grp + r, col = nb + l16;
             float x = 0.f;
-            if (MODE == kSumM) x = (row == col) ? 1.f : 0.f;
+            if (isM) x = (row == col) ? 1.f : 0.f;
             else if (MODE == kFull && a.h0) x = a.h0[sbase + size_t(row) * DV + col];
             S[m][r] = x;
         }
@@ -1333,7 +1338,7 @@ __global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
     if (nchunks > 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c_begin + s, last), h, tid, loff, nblk);
+            chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c_begin + s, last), h, tid, loff, nblk, isM);
         chain_stage_write<DK, DV, C, NWV, MODE>(sbuf[0] + opaque(0), st[0], tid);
     }
     __syncthreads();
@@ -1384,7 +1389,7 @@ __global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     ub[I >> 1][4 * (I & 1) + r] =
-                        static_cast<bf16>((MODE == kSumM ? 0.f : static_cast<float>(cur.ut[I][r])) - xa[r]);
+                        static_cast<bf16>((isM ? 0.f : static_cast<float>(cur.ut[I][r])) - xa[r]);
                 if (MODE == kFull) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -1409,13 +1414,14 @@ __global__ __launch_bounds__(kWave * NWV) void kda_chain_kernel(PrefillArgs a) {
             if (MODE == kFull && active && a.ckpt)
                 chain_ckpt<DK, DV>(a, S, n, h, lc0 + k, tok0 + C <= tok_end, grp, l16, nb);
             // this stage's registers now take chunk c + NS
-            chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c + NS, last), h, tid, loff, nblk);
+            chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c + NS, last), h, tid, loff, nblk, isM);
             __syncthreads();
         }
     }
 
     float *dst = nullptr;
-    if (MODE != kFull) dst = a.ht + sbase;
+    if (MODE == kSumBM) dst = (isM ? a.Mseg : a.Bseg) + sbase;
+    else if (MODE != kFull) dst = a.ht + sbase;
     else if (a.ht && sgi == nseg - 1) dst = a.ht + size_t(n * H + h) * DK * DV;
     if (dst) {
 #pragma unroll
@@ -1464,16 +1470,24 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
             b.h0 = nullptr;
             b.ht = a.Bseg;
             b.ckpt = nullptr;
-            prof_begin(s);
-            hipLaunchKernelGGL((kda_chain_kernel<DK, DV, C, NWV, kSumB>), dim3(nsc * (DV / BWV)), dim3(kWave * NWV), 0,
-                               s, b);
-            prof_end(s, "kda_seg_sum_b");
-            PrefillArgs m = b;
-            m.ht = a.Mseg;
-            prof_begin(s);
-            hipLaunchKernelGGL((kda_chain_kernel<DK, DK, C, NWK, kSumM>), dim3(nsc * (DK / BWK)), dim3(kWave * NWK), 0,
-                               s, m);
-            prof_end(s, "kda_seg_sum_m");
+            if constexpr (DK == DV) {
+                // both summaries in one pass over the chunk operands
+                prof_begin(s);
+                hipLaunchKernelGGL((kda_chain_kernel<DK, DV, C, NWV, kSumBM>), dim3(nsc * (DV / BWV)),
+                                   dim3(2 * kWave * NWV), 0, s, b);
+                prof_end(s, "kda_seg_sum_bm");
+            } else {
+                prof_begin(s);
+                hipLaunchKernelGGL((kda_chain_kernel<DK, DV, C, NWV, kSumB>), dim3(nsc * (DV / BWV)),
+                                   dim3(kWave * NWV), 0, s, b);
+                prof_end(s, "kda_seg_sum_b");
+                PrefillArgs m = b;
+                m.ht = a.Mseg;
+                prof_begin(s);
+                hipLaunchKernelGGL((kda_chain_kernel<DK, DK, C, NWK, kSumM>), dim3(nsc * (DK / BWK)),
+                                   dim3(kWave * NWK), 0, s, m);
+                prof_end(s, "kda_seg_sum_m");
+            }
             prof_begin(s);
             hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3(a.N * a.H * (DV / 8)), dim3(256), 0, s, a);
             prof_end(s, "kda_seg_scan");

@@ -78,6 +78,19 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C
     return out.len > 0;
 }
 
+// Chunk slot of the intra-chunk pass's wc-th (chunk, all heads) group.  The
+// chunks go in descending order of their index within the sequence
+// (sequences interleaved; a packed batch simply reversed), so the operands of
+// every sequence's first chunks are written last: the state pass, which
+// starts there, then finds them still in the last-level cache.
+__device__ __forceinline__ int intra_slot(const PrefillArgs &a, int wc) {
+    if (!a.cu) {
+        const int j = wc / a.N;
+        return (wc - j * a.N) * a.nc_seq + (a.nc_seq - 1 - j);
+    }
+    return a.nc_max - 1 - wc;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layouts.  Every intermediate is stored in the exact order its
 // consumer's wavefront reads it, so that one wave-wide load instruction is
@@ -127,9 +140,10 @@ __device__ __forceinline__ size_t quad_off(int tile_r, int tile_n, int lane) {
 // Kernel 1: intra-chunk work, persistent.  Its LDS footprint allows one
 // workgroup per compute unit, so the workgroup is 16 wavefronts (four per
 // SIMD) to overlap the latencies of its dependent steps.  Each workgroup
-// walks (chunk, head) items in chunk-major order; the raw inputs of its next
-// item are loaded into registers while the current one computes, directly
-// in the layout their first consumer wants ("owner" layout):
+// walks (chunk, head) items chunk-major, last chunks first (intra_slot); the
+// raw inputs of its next item are loaded into registers while the current
+// one computes, directly in the layout their first consumer wants ("owner"
+// layout):
 //   g, k, q: thread (channel group cg of 4, segment sg of 4 tokens)
 //   v:       thread (channel group jg of 8, segment sg of 4 tokens)
 // so the cumulative decay, every decay-factored operand, the transposes and
@@ -369,7 +383,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     // first item of this workgroup with a valid chunk
     int item = blockIdx.x;
     ChunkLoc loc;
-    while (item < nitems && !locate_chunk(a, item / H, C, loc)) item += gridDim.x;
+    while (item < nitems && !locate_chunk(a, intra_slot(a, item / H), C, loc)) item += gridDim.x;
     if (item >= nitems) return;
     In in;
     intra_fetch(in, a, loc, item % H, int(threadIdx.x));
@@ -381,7 +395,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const int tid = opaque(int(threadIdx.x)), lane = tid & 63;
         const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile math stays scalar
         const int grp = lane >> 4, l16 = lane & 15;
-        const int gc = item / H, h = item % H;
+        const int gc = intra_slot(a, item / H), h = item % H;
         const size_t slot = size_t(gc) * H + h;
         // The prefetched registers are consumed from here on, and only from
         // here: without this fence the compiler moves unpacking work up to
@@ -497,7 +511,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         // the next item (its inputs are requested during the inversion below)
         const ChunkLoc cur = loc;
         int nxt = item + gridDim.x;
-        while (nxt < nitems && !locate_chunk(a, nxt / H, C, loc)) nxt += gridDim.x;
+        while (nxt < nitems && !locate_chunk(a, intra_slot(a, nxt / H), C, loc)) nxt += gridDim.x;
         if (nxt >= nitems) loc = cur;
         const int nxt_h = (nxt < nitems ? nxt : item) % H;
         __syncthreads();

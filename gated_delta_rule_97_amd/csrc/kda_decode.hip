@@ -14,40 +14,55 @@
 
 namespace kda {
 
-template <class T, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_decode_kernel(const T *__restrict__ q, const T *__restrict__ k,
+// Threads per workgroup of the single-token step: each thread holds a 4 x 4
+// block of the state (4 rows, one float4 of columns).  Small per-thread
+// slices keep the register count low enough for eight waves per SIMD, so
+// many (sequence, head) states are streaming at once on every compute unit.
+template <int DK, int DV>
+constexpr int decode_threads() {
+    constexpr int n = (DV / 4) * DK / 4;
+    return n < 64 ? 64 : (n > 1024 ? 1024 : n);
+}
+
+template <class T, int DK, int DV, int NTH>
+__global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                         const T *__restrict__ v, const float *__restrict__ g,
                                                         const float *__restrict__ beta, float *__restrict__ state,
                                                         T *__restrict__ o) {
     constexpr int CG = DV / 4;      // float4 column groups
-    constexpr int RG = 256 / CG;    // row groups
+    constexpr int RG = NTH / CG;    // row groups
     constexpr int RPT = DK / RG;    // rows per thread
-    static_assert(RG * CG == 256 && RPT * RG == DK, "decode thread split");
+    constexpr int NW = NTH / kWave; // wavefronts
+    static_assert(RG * CG == NTH && RPT * RG == DK && RPT >= 1, "decode thread split");
+    static_assert(CG <= kWave && kWave % CG == 0, "a wave spans whole row groups");
     __shared__ float sk[DK], sq[DK], sd[DK];
-    __shared__ float4 sw[RG][CG], sy[RG][CG];
+    __shared__ float4 sw[NW][CG], sy[NW][CG];
     __shared__ float skq;
 
     const size_t ch = blockIdx.x;  // sequence * H + head
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
     float *S = state + ch * DK * DV;
 
     floatx4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)  // rows i*RG + rg: a workgroup-wide load is one contiguous span
         s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
-    for (int c = tid; c < DK; c += 256) {
+    for (int c = tid; c < DK; c += NTH) {
         sk[c] = to_f32(k[ch * DK + c]);
         sq[c] = to_f32(q[ch * DK + c]);
         sd[c] = exp_e(g[ch * DK + c]);
     }
     __syncthreads();
-    if (tid < 64) {
+    if (tid < kWave) {
         float p = 0.f;
-        for (int c = tid; c < DK; c += 64) p += sk[c] * sq[c];
+        for (int c = tid; c < DK; c += kWave) p += sk[c] * sq[c];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        for (int off = kWave / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
         if (tid == 0) skq = p;
     }
+    // partial w = S'^T k and y = S'^T q over this thread's rows, then over
+    // the row groups of the wave (lanes CG apart), then over the waves
     float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -57,12 +72,21 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const T *__restrict__ q
         w.x += kc * s[i][0]; w.y += kc * s[i][1]; w.z += kc * s[i][2]; w.w += kc * s[i][3];
         y.x += qc * s[i][0]; y.y += qc * s[i][1]; y.z += qc * s[i][2]; y.w += qc * s[i][3];
     }
-    sw[rg][cg] = w;
-    sy[rg][cg] = y;
+#pragma unroll
+    for (int off = CG; off < kWave; off <<= 1) {
+        w.x += __shfl_xor(w.x, off); w.y += __shfl_xor(w.y, off);
+        w.z += __shfl_xor(w.z, off); w.w += __shfl_xor(w.w, off);
+        y.x += __shfl_xor(y.x, off); y.y += __shfl_xor(y.y, off);
+        y.z += __shfl_xor(y.z, off); y.w += __shfl_xor(y.w, off);
+    }
+    if (lane < CG) {
+        sw[wid][cg] = w;
+        sy[wid][cg] = y;
+    }
     __syncthreads();
     float4 W = make_float4(0.f, 0.f, 0.f, 0.f), Y = W;
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
+    for (int r = 0; r < NW; ++r) {
         const float4 a = sw[r][cg], b = sy[r][cg];
         W.x += a.x; W.y += a.y; W.z += a.z; W.w += a.w;
         Y.x += b.x; Y.y += b.y; Y.z += b.z; Y.w += b.w;
@@ -259,8 +283,9 @@ template <class T, int DK, int DV>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, float *state, void *o, int NH, hipStream_t s) {
     if (NH == 0) return hipSuccess;
+    constexpr int NTH = decode_threads<DK, DV>();
     prof_begin(s);
-    hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV>), dim3(NH), dim3(256), 0, s,
+    hipLaunchKernelGGL((kda_decode_kernel<T, DK, DV, NTH>), dim3(NH), dim3(NTH), 0, s,
                        static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
                        state, static_cast<T *>(o));
     prof_end(s, "kda_decode");

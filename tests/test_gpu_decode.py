@@ -43,6 +43,29 @@ def test_decode_small(dk, dv, dtype):
     assert eo <= tol and es <= tol
 
 
+@pytest.mark.parametrize("mode", ["config", "floor", "zero"])
+def test_decode_decay_modes(mode):
+    """Decode under the configs' fast decay, the bound itself (g = -5 every
+    step, the smallest kept fraction) and no decay at all, over enough steps
+    that the state carries several tokens."""
+    spec = workloads.DecodeSpec(N=7, H=4, dk=128, dv=128, steps=12, dtype="bf16", state_std=1.0,
+                                g_mode=mode, seed=43)
+    eo, es = _run(spec, 12)
+    print(f"[decode] g={mode}: o {eo:.2e} state {es:.2e}", flush=True)
+    assert np.isfinite(eo) and np.isfinite(es)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_decode_single_sequence_head():
+    """The smallest grid: one (sequence, head), fp32, every shape kernel."""
+    for dk, dv in [(32, 32), (128, 128)]:
+        spec = workloads.DecodeSpec(N=1, H=1, dk=dk, dv=dv, steps=3, dtype="fp32", state_std=1.0,
+                                    g_mode="slow", seed=44)
+        eo, es = _run(spec, 3)
+        print(f"[decode] N=H=1 dk={dk} dv={dv}: o {eo:.2e} state {es:.2e}", flush=True)
+        assert eo <= TOL_FP32 and es <= TOL_FP32
+
+
 def test_decode_headline_batch_sampled_steps():
     """The 256-sequence x 32-head decode batch, 8 consecutive steps, every
     output and the whole state checked."""

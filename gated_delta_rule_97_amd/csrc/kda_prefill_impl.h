@@ -1087,6 +1087,270 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel 2, loader-fed variant (bf16, 16-column value blocks, outputs).  The
+// register-fed kernel above stalls for ~1,200 of its ~3,000 cycles per chunk
+// issuing the next chunk's ~52 KiB of operand loads: every wave issues its
+// share at once and the compute unit's vector-memory pipeline takes them at
+// its own rate, while the products wait behind them in the same waves.  Here
+// four loader waves copy each chunk's operands (W, Q', K~^T, e^{Gam_last} and
+// this block's Ut and Oi tiles, already in the order the products read them)
+// into one of two LDS buffers two chunks ahead, and the four compute waves
+// read them from LDS: their only global accesses are the o stores.  Both roles
+// pass the same barriers: one before the chain, then the two of each chunk.
+// Cycle counters per chunk: compute ~1,500 (read 210, S^T 60, X/O 750, state
+// 150, checkpoint tests 150, barriers); the loader's ~830 of vector-memory
+// issue (52.5 KiB at ~64 B/clk) and ~450 of LDS writes split over both
+// windows between the barriers.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int C>
+struct WsBuf {
+    using M = Mma<bf16>;
+    static constexpr int CP = kpad<bf16>(C);
+    static constexpr int NT = C / kTile;
+    // byte offsets inside one buffer
+    static constexpr int oW = 0;
+    static constexpr int oQ = oW + C * DK * 2;
+    static constexpr int oK = oQ + C * DK * 2;
+    static constexpr int oU = oK + DK * CP * 2;   // Ut tiles (I, this block), 256 values each
+    static constexpr int oO = oU + NT * 256 * 2;  // Oi tiles
+    static constexpr int oD = oO + NT * 256 * 2;  // e^{Gam_last}, fp32
+    static constexpr int bytes = oD + DK * 4;
+    static constexpr int units = bytes / 16;       // 16-byte copy units
+    static_assert(oQ % 16 == 0 && oK % 16 == 0 && oU % 16 == 0 && oO % 16 == 0 && oD % 16 == 0 && bytes % 16 == 0,
+                  "16-byte units");
+    static constexpr int kLoaders = kThreads;      // loader threads (four waves)
+    static constexpr int UPT = (units + kLoaders - 1) / kLoaders;  // units per loader thread
+    static constexpr size_t lds_bytes = size_t(2) * bytes;
+};
+
+// Source of copy unit lt + kLoaders * i of chunk slot (gc, h), for value
+// block nn0.  The units run over W, Q', K~^T (each a contiguous span in the
+// workspace; four units of the 256 loader threads each at d = 128, chunk 64),
+// then this block's Ut and Oi tiles (four 512-byte spans each), then
+// e^{Gam_last}.  The category of each step i is fixed at compile time and the
+// mixed steps use selects, so every load is unconditional and the compiler
+// can count the loads in flight exactly.
+template <int DK, int DV, int C, int i>
+__device__ __forceinline__ const char *ws_src(const PrefillArgs &a, size_t slot, int nn0, int lt) {
+    using B = WsBuf<DK, DV, C>;
+    static_assert(B::oQ == 4 * 16 * B::kLoaders && B::oK == 8 * 16 * B::kLoaders && B::oU == 12 * 16 * B::kLoaders &&
+                      B::oD == 13 * 16 * B::kLoaders && B::bytes == B::oD + 32 * 16 && B::UPT == 14,
+                  "unit plan of the d = 128, chunk 64 layout");
+    const unsigned off = unsigned(lt) * 16u + unsigned(i % 4) * 16u * B::kLoaders;
+    if constexpr (i < 4) return static_cast<const char *>(a.W) + slot * (C * DK * 2) + off;
+    else if constexpr (i < 8) return static_cast<const char *>(a.Qp) + slot * (C * DK * 2) + off;
+    else if constexpr (i < 12) return static_cast<const char *>(a.KtT) + slot * (DK * B::CP * 2) + off;
+    else if constexpr (i == 12) {
+        const bool is_u = lt < 128;
+        const unsigned j = unsigned(lt) & 127u;        // unit within the four tiles
+        const unsigned I = j / 32u, w = j % 32u;       // 32 units per 512-byte tile
+        const char *base = static_cast<const char *>(is_u ? a.Ut : a.Oi) + slot * (C * DV * 2);
+        return base + (size_t(I * (DV / 16) + nn0) * 256 + w * 8) * 2;
+    } else {
+        return reinterpret_cast<const char *>(a.D + slot * DK) + unsigned(min(lt, 31)) * 16u;
+    }
+}
+
+// LDS byte offset of copy unit (lt, i) inside one buffer.
+template <int DK, int DV, int C, int i>
+__device__ __forceinline__ unsigned ws_dst(int lt) {
+    using B = WsBuf<DK, DV, C>;
+    if constexpr (i < 13) return (unsigned(lt) + unsigned(i) * B::kLoaders) * 16u;
+    else return unsigned(B::oD) + unsigned(min(lt, 31)) * 16u;
+}
+
+template <int DK, int DV, int C, int i>
+__device__ __forceinline__ void ws_fetch_unit(u32x4 *r, const PrefillArgs &a, size_t slot, int nn0, int lt) {
+    if constexpr (i < WsBuf<DK, DV, C>::UPT) {
+        r[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, i>(a, slot, nn0, lt));
+        ws_fetch_unit<DK, DV, C, i + 1>(r, a, slot, nn0, lt);
+    }
+}
+
+template <int DK, int DV, int C, int i>
+__device__ __forceinline__ void ws_put_unit(const u32x4 *r, unsigned char *dst, int lt) {
+    if constexpr (i < WsBuf<DK, DV, C>::UPT) {
+        *reinterpret_cast<u32x4 *>(dst + ws_dst<DK, DV, C, i>(lt)) = r[i];
+        ws_put_unit<DK, DV, C, i + 1>(r, dst, lt);
+    }
+}
+
+// Units i .. iend - 1 of one staging step: unit i of a chunk already in
+// registers (rp) goes to LDS, then unit i of a later chunk (slot) is
+// requested into rf.  Alternating the two keeps the LDS and the
+// vector-memory pipelines busy together.
+template <int DK, int DV, int C, int i, int iend>
+__device__ __forceinline__ void ws_step(const u32x4 *rp, unsigned char *dst, u32x4 *rf, const PrefillArgs &a,
+                                        size_t slot, int nn0, int lt) {
+    if constexpr (i < iend) {
+        *reinterpret_cast<u32x4 *>(dst + ws_dst<DK, DV, C, i>(lt)) = rp[i];
+        rf[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, i>(a, slot, nn0, lt));
+        ws_step<DK, DV, C, i + 1, iend>(rp, dst, rf, a, slot, nn0, lt);
+    }
+}
+
+template <int DK, int DV, int C>
+__global__ __launch_bounds__(2 * kThreads) void kda_inter_ws_kernel(PrefillArgs a) {
+    constexpr int BV = 16;
+    using Cfg = InterCfg<bf16, DK, DV, C, BV>;
+    using B = WsBuf<DK, DV, C>;
+    using M = Mma<bf16>;
+    constexpr int NRT = Cfg::NRT, NSI = Cfg::NSI, SPW = Cfg::SPW, XPW = Cfg::XPW;
+    constexpr int NB = DV / BV;
+    constexpr int PT = 8;
+    static_assert(Cfg::NCT == 1 && XPW == 1, "one 16-column tile per block, one output tile per wave");
+    __shared__ __align__(16) bf16 sST[BV * (DK + PT)];
+    __shared__ __align__(16) bf16 sUT[BV * (C + PT)];
+    extern __shared__ __align__(16) unsigned char wsbuf[];
+
+    const int H = a.H;
+    const int nchains = a.N * H;
+    const int wg = blockIdx.x;
+    int chain, blk;
+    if ((nchains & 7) == 0) {  // the NB blocks of a chain share an XCD
+        const int xcd = wg & 7, slot = wg >> 3;
+        blk = slot % NB;
+        chain = xcd + 8 * (slot / NB);
+    } else {
+        chain = wg / NB;
+        blk = wg - chain * NB;
+    }
+    const int h = chain % H, n = chain / H;
+    const int tid = threadIdx.x;
+    const int wid_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int jb = blk * BV, nn0 = jb / kTile;
+
+    int c_begin, c_end, tok_start, tok_end;
+    if (!a.cu) {
+        c_begin = n * a.nc_seq;
+        c_end = c_begin + a.nc_seq;
+        tok_start = n * a.T;
+        tok_end = tok_start + a.T;
+    } else {
+        c_begin = min(a.coff[n], a.nc_max);
+        c_end = min(max(a.coff[n + 1], c_begin), a.nc_max);
+        tok_start = clampi(a.cu[n], 0, a.T);
+        tok_end = clampi(a.cu[n + 1], tok_start, a.T);
+    }
+    const int nc = c_end - c_begin;  // chunks of this chain (may be 0)
+
+    if (wid_all >= kWaves) {
+        // ---------------- loader waves ----------------
+        const int lt = tid - kThreads;
+        u32x4 st[3][B::UPT];
+        auto fetch = [&](u32x4 (&r)[B::UPT], int c) {
+            const size_t slot = size_t(c_begin + min(c, nc - 1)) * H + h;
+            ws_fetch_unit<DK, DV, C, 0>(r, a, slot, nn0, lt);
+        };
+        auto put = [&](const u32x4 (&r)[B::UPT], int buf) { ws_put_unit<DK, DV, C, 0>(r, wsbuf + buf * B::bytes, lt); };
+        // chunk x lives in register stage x % 3 and LDS buffer x & 1.  During
+        // chunk c the loader writes chunk c + 2 into buffer c & 1 (read by the
+        // compute waves at the top of chunk c, before the first barrier) and
+        // requests chunk c + 4, half after each of the chunk's two barriers,
+        // so neither half holds a barrier back.
+        constexpr int HALF = B::UPT / 2;
+        auto slot_of = [&](int x) { return size_t(c_begin + min(x, nc - 1)) * H + h; };
+        if (nc > 0) {
+            fetch(st[0], 0);
+            fetch(st[1], 1);
+            fetch(st[2], 2);
+            put(st[0], 0);
+            put(st[1], 1);
+            fetch(st[0], 3);
+        }
+        __syncthreads();  // chunks 0 and 1 staged
+        int c = 0;
+        for (; c + 3 <= nc; c += 3) {
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                unsigned char *dst = wsbuf + ((c + s) & 1) * B::bytes;
+                const size_t sl = slot_of(c + s + 4);
+                __syncthreads();  // A
+                ws_step<DK, DV, C, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                __syncthreads();  // B
+                ws_step<DK, DV, C, HALF, B::UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (c + s < nc) {
+                unsigned char *dst = wsbuf + ((c + s) & 1) * B::bytes;
+                const size_t sl = slot_of(c + s + 4);
+                __syncthreads();
+                ws_step<DK, DV, C, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                __syncthreads();
+                ws_step<DK, DV, C, HALF, B::UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+            }
+        }
+        return;
+    }
+
+    // ---------------- compute waves ----------------
+    const int wid = wid_all, lane = tid & 63;
+    const int grp = lane >> 4, l16 = lane & 15;
+    floatx4 S[SPW];
+    const size_t sbase = size_t(chain) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int item = wid + kWaves * i;
+        S[i] = zero4();
+        if (item < NSI && a.h0) {
+            const int m = item % NRT, nn = item / NRT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[i][r] = a.h0[sbase + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16];
+        }
+    }
+    bf16 *og = static_cast<bf16 *>(a.o);
+    bf16 *dummy = static_cast<bf16 *>(a.dummy) + tid;
+    __syncthreads();  // chunk 0 staged
+    for (int c = 0; c < nc; ++c) {
+        const unsigned char *buf = wsbuf + (c & 1) * B::bytes;
+        InterStage<bf16, DK, DV, C, BV> cur;
+        const int I = wid % Cfg::NT;
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSD; ++kk) {
+            const int off = ((I * Cfg::KSD + kk) * (16 * M::K) + lane * M::KPL) * 2;
+            cur.w[kk] = *reinterpret_cast<const bf16x8 *>(buf + B::oW + off);
+            cur.q[kk] = *reinterpret_cast<const bf16x8 *>(buf + B::oQ + off);
+        }
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int item = wid + kWaves * i;
+            if (item < NSI) {
+                const int m = item % NRT;
+#pragma unroll
+                for (int kk = 0; kk < Cfg::KSC; ++kk) {
+                    const int kb = kk * M::K + grp * M::KPL;
+                    cur.kt[i][kk] = (kb < C) ? *reinterpret_cast<const bf16x8 *>(
+                                                   buf + B::oK + ((m * Cfg::KSC + kk) * (16 * M::K) + lane * M::KPL) * 2)
+                                             : bf16x8{};
+                }
+                cur.d[i] = *reinterpret_cast<const floatx4 *>(buf + B::oD + (kTile * m + 4 * grp) * 4);
+            }
+        }
+        cur.ut[0].load(reinterpret_cast<const bf16 *>(buf + B::oU) + I * 256 + lane * 4);
+        cur.oi[0].load(reinterpret_cast<const bf16 *>(buf + B::oO) + I * 256 + lane * 4);
+        const int tok0 = tok_start + c * C;
+        inter_chunk<bf16, DK, DV, C, BV, kFull>(cur, S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
+                                                grp, l16, jb);
+        inter_ckpt<bf16, DK, DV, C, BV>(a, S, n, h, c, tok0 + C <= tok_end, wid, grp, l16, jb);
+    }
+    if (a.ht) {
+        float *dst = a.ht + size_t(n * H + h) * DK * DV;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int item = wid + kWaves * i;
+            if (item < NSI) {
+                const int m = item % NRT, nn = item / NRT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
+            }
+        }
+    }
+}
+
 // Segment scan: the state entering segment j + 1 of (sequence n, head h) is
 // Sin_{j+1} = M_j Sin_j + B_j, Sin_0 = h0 (or zero), in fp32, serially over
 // the segments.  The serial steps are short when each thread owns little:
@@ -1545,6 +1809,23 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         return hipGetLastError();
     }
     const int nwg = a.N * a.H * (DV / BV);
+    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && C == 64 && BV == 16) {
+        // loader-fed state chain (one chain per (sequence, head), no segments)
+        using WB = WsBuf<DK, DV, C>;
+        static bool ws_attr = false;
+        if (!ws_attr) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(WB::lds_bytes));
+            if (e != hipSuccess) return e;
+            ws_attr = true;
+        }
+        if (nwg > 0) {
+            prof_begin(s);
+            hipLaunchKernelGGL((kda_inter_ws_kernel<DK, DV, C>), dim3(nwg), dim3(2 * kThreads), WB::lds_bytes, s, a);
+            prof_end(s, "kda_inter");
+        }
+        return hipGetLastError();
+    }
     if (nwg > 0) {
         prof_begin(s);
         hipLaunchKernelGGL((kda_inter_kernel<T, DK, DV, C, BV, kFull>), dim3(nwg), dim3(kThreads), 0, s, a);

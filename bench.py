@@ -96,7 +96,8 @@ def ingest_pmc(fetch_dir, write_dir):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                key = ("kda_intra" if "kda_intra_kernel" in name else "kda_inter" if "kda_inter_kernel" in name
+                key = ("kda_intra" if "kda_intra_kernel" in name
+                       else "kda_inter" if ("kda_inter_kernel" in name or "kda_inter_ws_kernel" in name)
                        else "kda_decode" if "kda_decode_kernel" in name
                        else "copy" if "copy" in name.lower() and float(r["Counter_Value"]) > 0 else None)
                 if key:

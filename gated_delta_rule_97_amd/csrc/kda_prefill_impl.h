@@ -211,7 +211,6 @@ __device__ __forceinline__ int role_tid(int tid) {
 template <class T, int DK, int DV, int C>
 struct IntraIn {
     u32x4 raw[IntraRoles<T, DK, DV, C>::RAW];  // 16 bytes each, as loaded
-    float b[kSR];
     int len;  // valid tokens of the chunk; rows at or past it are zeroed on use
 };
 
@@ -279,7 +278,6 @@ __device__ __forceinline__ void intra_fetch(IntraIn<T, DK, DV, C> &in, const Pre
             const char *pq = is_g ? reinterpret_cast<const char *>(static_cast<const T *>(a.q) + row * DK + 4 * cgrp)
                                   : pv;
             in.raw[r] = *reinterpret_cast<const u32x4 *>(p16);
-            in.b[r] = a.beta[row];
             if constexpr (sizeof(T) == 2) {  // k and q: 8 bytes each, packed into one register
                 const u32x2 kk = *reinterpret_cast<const u32x2 *>(pk);
                 const u32x2 qq = *reinterpret_cast<const u32x2 *>(pq);
@@ -305,12 +303,6 @@ __device__ __forceinline__ void intra_fence(IntraIn<T, DK, DV, C> &in, int tid) 
     using R = IntraRoles<T, DK, DV, C>;
 #pragma unroll
     for (int i = 0; i < R::RAW; ++i) asm volatile("" : "+v"(in.raw[i]));
-#pragma unroll
-    for (int r = 0; r < kSR; ++r) {
-        float b = in.b[r];
-        asm volatile("" : "+v"(b));
-        in.b[r] = b;
-    }
     bool is_g;
     int cgrp, sg;
     owner_coords<T, DK, DV, C>(tid, is_g, cgrp, sg);
@@ -320,7 +312,6 @@ __device__ __forceinline__ void intra_fence(IntraIn<T, DK, DV, C> &in, int tid) 
         zero_unless(in.raw[r], ok);
         zero_unless(in.raw[kSR + r], ok);
         if constexpr (sizeof(T) == 4) zero_unless(in.raw[2 * kSR + r], ok);
-        in.b[r] = ok ? in.b[r] : 0.f;
     }
 }
 
@@ -387,6 +378,19 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     if (item >= nitems) return;
     In in;
     intra_fetch(in, a, loc, item % H, int(threadIdx.x));
+    // beta of the chunk: one value per lane of the last wave (which loads no
+    // other input), staged in LDS at the top of each item
+    constexpr int kBetaWave = kIWaves - 1;
+    static_assert(kBetaWave * kWave >= R::NG + R::NV + DK, "the beta wave has no other input or scan role");
+    static_assert(C <= kWave, "one beta value per lane");
+    const bool beta_wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6) == kBetaWave;
+    float bnx = 0.f;
+    int blen = 0;
+    if (beta_wave) {
+        const int t = min(int(threadIdx.x & 63), loc.len - 1);
+        bnx = a.beta[size_t(loc.tok0 + t) * H + item % H];
+        blen = loc.len;
+    }
 
     while (item < nitems) {
         // thread coordinates pass through an opaque copy each iteration, so
@@ -402,6 +406,10 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         // the loads at the end of the previous item, which then must wait
         // for them there and the prefetch hides no latency.
         intra_fence(in, tid);
+        if (beta_wave) {
+            asm volatile("" : "+v"(bnx));
+            if (lane < C) sB[lane] = lane < blen ? bnx : 0.f;
+        }
 
         // ---- cumulative log-decay: per-thread partial sums over kSR tokens ----
         const int rt = role_tid<T, DK, DV, C>(tid);
@@ -445,10 +453,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             bool is_g;
             int jg, sg;
             owner_coords<T, DK, DV, C>(tid, is_g, jg, sg);
+            static_assert(kSR == 4, "four tokens' beta per owner");
+            const float4 b4 = *reinterpret_cast<const float4 *>(sB + kSR * sg);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, in.b[0] * v_get(in, 0, j), in.b[1] * v_get(in, 1, j),
-                       in.b[2] * v_get(in, 2, j), in.b[3] * v_get(in, 3, j));
+                store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, b4.x * v_get(in, 0, j), b4.y * v_get(in, 1, j),
+                       b4.z * v_get(in, 2, j), b4.w * v_get(in, 3, j));
         }
         __syncthreads();
 
@@ -468,6 +478,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             const float base[4] = {off4.x - rI4.x, off4.y - rI4.y, off4.z - rI4.z, off4.w - rI4.w};
             const float glr[4] = {gl4.x - rI4.x, gl4.y - rI4.y, gl4.z - rI4.z, gl4.w - rI4.w};
             const float er[4] = {er4.x, er4.y, er4.z, er4.w};
+            const float4 b4 = *reinterpret_cast<const float4 *>(sB + kSR * sg);
+            const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
             // per channel: four tokens' beta k e^Gam and K~, for the column stores
             Col4<T> bke[4], ktv[4];
             float run[4] = {base[0], base[1], base[2], base[3]};  // Gam - r_I, token by token
@@ -487,13 +499,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     kp[c] = kv * e;
                     qp[c] = qv * e;
                     km[c] = kv * ei;
-                    bke[c].set(r, in.b[r] * er[c] * kp[c]);
+                    bke[c].set(r, bt[r] * er[c] * kp[c]);
                     ktv[c].set(r, kv * exp_e(glr[c] - x));  // <= 1
                 }
                 store4(sKp + t * K_LD + c0, kp[0], kp[1], kp[2], kp[3]);
                 store4(sKm + t * K_LD + c0, km[0], km[1], km[2], km[3]);
                 store4(sQp + t * K_LD + c0, qp[0], qp[1], qp[2], qp[3]);
-                if (cg == 0) sB[t] = in.b[r];
             }
             // channels: (beta k e^Gam)^T to LDS and K~^T to HBM, 4 tokens per store
             T *KtT = static_cast<T *>(a.KtT) + slot * DK * kpad<T>(C);
@@ -577,14 +588,19 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         }
         __syncthreads();
 
-        // ---- L = (I + A)^-1 by blocked forward substitution (fp32), all of it
-        //      on one wave that loads no inputs, while the owner waves issue
-        //      the next item's loads: the wave reads back only what it wrote
-        //      itself (its LDS accesses complete in order), so the inverse
-        //      needs no barrier of its own ----
+        // ---- L = (I + A)^-1 by blocked forward substitution (fp32) on the
+        //      waves that load no inputs, while the owner waves issue the next
+        //      item's loads.  Wave kSolveWave + J owns block column J: it
+        //      computes all diagonal blocks (the same values on every such
+        //      wave), then L_IJ for I > J from its own column.  Each wave reads
+        //      back only what it wrote itself (its LDS accesses complete in
+        //      order), so the inverse needs no barrier of its own, and the
+        //      longest chain is column 0 instead of the whole triangle ----
         constexpr int kSolveWave = (IntraRoles<T, DK, DV, C>::NG + IntraRoles<T, DK, DV, C>::NV + kWave - 1) / kWave;
-        static_assert(kSolveWave < kIWaves, "a wave with no input role");
-        if (wid == kSolveWave) {
+        constexpr int kSolveWaves = NT > 1 ? NT - 1 : 1;
+        static_assert(kSolveWave + kSolveWaves <= kIWaves, "waves with no input role");
+        if (wid >= kSolveWave && wid < kSolveWave + kSolveWaves) {
+            const int Jw = wid - kSolveWave;  // this wave's block column
             // the NT diagonal 16x16 blocks, one column per lane
             const int b = lane >> 4, colx = lane & 15;
             if (b < NT) {
@@ -606,17 +622,18 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                         *reinterpret_cast<floatx4 *>(t + i) = floatx4{X[i], X[i + 1], X[i + 2], X[i + 3]};
                 }
             }
-            // off-diagonal blocks by distance d: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.
+            // off-diagonal blocks of column Jw, top to bottom:
+            // L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.
             // The fp32 16x16x4 products take their k in the order 4 * grp + kk,
             // so a lane's four A values are one 16-byte row read, its four B
             // values one 16-byte read of L^T (tile (K, J) of sY holds L_KJ
             // transposed), and the sum Y itself, as the accumulator leaves it,
             // is the B operand of the product with L_II.
 #pragma unroll
-            for (int d = 1; d < NT; ++d) {
-#pragma unroll
-                for (int J = 0; J + d < NT; ++J) {
-                    const int I = J + d;
+            for (int I = 1; I < NT; ++I) {
+                {
+                    const int J = Jw;
+                    if (I <= J) continue;
                     floatx4 acc = zero4();
 #pragma unroll
                     for (int K = J; K < I; ++K) {
@@ -645,6 +662,11 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         //      unused): an unconditional load keeps the registers free of
         //      merges that would wait here ----
         intra_fetch(in, a, loc, nxt_h, tid);
+        if (beta_wave) {
+            const int t = min(lane, loc.len - 1);
+            bnx = a.beta[size_t(loc.tok0 + t) * H + nxt_h];
+            blen = loc.len;
+        }
         __syncthreads();
 
         // ---- W = L (beta k e^Gam) as W^T = (beta k e^Gam)^T L^T, so that a

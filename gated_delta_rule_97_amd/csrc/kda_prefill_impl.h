@@ -279,9 +279,16 @@ __device__ __forceinline__ void intra_fetch(IntraIn<T, DK, DV, C> &in, const Pre
                                   : pv;
             in.raw[r] = *reinterpret_cast<const u32x4 *>(p16);
             if constexpr (sizeof(T) == 2) {  // k and q: 8 bytes each, packed into one register
-                const u32x2 kk = *reinterpret_cast<const u32x2 *>(pk);
-                const u32x2 qq = *reinterpret_cast<const u32x2 *>(pq);
-                in.raw[kSR + r] = u32x4{kk[0], kk[1], qq[0], qq[1]};
+                // the v owners hold their 8 values in raw[r] alone: when roles
+                // cover whole waves their k/q slots are never read, so those
+                // waves skip the two loads (a wave-uniform branch)
+                if (!R::ALIGNED || role_tid<T, DK, DV, C>(tid) < R::NG) {
+                    const u32x2 kk = *reinterpret_cast<const u32x2 *>(pk);
+                    const u32x2 qq = *reinterpret_cast<const u32x2 *>(pq);
+                    in.raw[kSR + r] = u32x4{kk[0], kk[1], qq[0], qq[1]};
+                } else {
+                    in.raw[kSR + r] = u32x4{0u, 0u, 0u, 0u};
+                }
             } else {
                 in.raw[kSR + r] = *reinterpret_cast<const u32x4 *>(pk);
                 in.raw[2 * kSR + r] = *reinterpret_cast<const u32x4 *>(pq);
@@ -605,13 +612,23 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             const int b = lane >> 4, colx = lane & 15;
             if (b < NT) {
                 const float *Ab = sA + (kTile * b) * A_LD + kTile * b;
+                // right-looking: once X[j] is final it is taken out of every
+                // later row, so each row's sum runs over j in the same order as
+                // X[i] = e_i - sum_{j<i} A_ij X[j] (the same rounding), but the
+                // A values are two-column row pieces read ahead of their use
+                // and the serial dependency is one FMA per row
                 float X[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = (i == colx) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) X[i] = (i == colx) ? 1.f : 0.f;
 #pragma unroll
-                    for (int j = 0; j < i; ++j) acc -= Ab[i * A_LD + j] * X[j];
-                    X[i] = acc;
+                for (int jb = 0; jb < 16; jb += 2) {
+                    float2 ar[16];
+#pragma unroll
+                    for (int i = jb + 1; i < 16; ++i) ar[i] = *reinterpret_cast<const float2 *>(Ab + i * A_LD + jb);
+#pragma unroll
+                    for (int i = jb + 1; i < 16; ++i) X[i] -= ar[i].x * X[jb];
+#pragma unroll
+                    for (int i = jb + 2; i < 16; ++i) X[i] -= ar[i].y * X[jb + 1];
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sL[(kTile * b + i) * A_LD + kTile * b + colx] = X[i];

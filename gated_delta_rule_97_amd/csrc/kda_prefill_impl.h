@@ -348,6 +348,40 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
     store4(p + 4, x[4], x[5], x[6], x[7]);
 }
 
+// Off-diagonal blocks of block column J of L = (I + A)^-1 (fp32, one wave),
+// top to bottom: L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.  The fp32 16x16x4
+// products take their k in the order 4 * grp + kk, so a lane's four A values
+// are one 16-byte row read and its four B values are rows 4 grp .. 4 grp + 3
+// of L_KJ's column l16: for K = J one 16-byte read of the transposed
+// diagonal tile in sY, for K > J exactly what the lane holds of -L_KJ from
+// the product that made it (the accumulator layout), so the column's blocks
+// stay in registers.  The sum Y, as the accumulator leaves it, is likewise
+// the B operand of the product with L_II.
+template <int J, int NT, int A_LD, int Y_LD>
+__device__ __forceinline__ void inverse_column(const float *sA, float *sL, const float *sY, int grp, int l16) {
+    floatx4 Lc[NT];  // rows 4 grp + r of column l16 of L_KJ, K > J
+#pragma unroll
+    for (int I = J + 1; I < NT; ++I) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int K = J; K < I; ++K) {
+            const floatx4 af = *reinterpret_cast<const floatx4 *>(sA + (kTile * I + l16) * A_LD + kTile * K + 4 * grp);
+            const floatx4 bf = (K == J) ? *reinterpret_cast<const floatx4 *>(sY + ((J * (J + 1)) / 2 + J) * 16 * Y_LD +
+                                                                              l16 * Y_LD + 4 * grp)
+                                        : Lc[K];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mma_f32(af[kk], bf[kk], acc);
+        }
+        const floatx4 lf = *reinterpret_cast<const floatx4 *>(sL + (kTile * I + l16) * A_LD + kTile * I + 4 * grp);
+        floatx4 out = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) out = mma_f32(lf[kk], acc[kk], out);
+        Lc[I] = floatx4{-out[0], -out[1], -out[2], -out[3]};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -out[r];
+    }
+}
+
 template <class T, int DK, int DV, int C>
 __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     using Ly = IntraLds<T, DK, DV, C>;
@@ -639,39 +673,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                         *reinterpret_cast<floatx4 *>(t + i) = floatx4{X[i], X[i + 1], X[i + 2], X[i + 3]};
                 }
             }
-            // off-diagonal blocks of column Jw, top to bottom:
-            // L_IJ = -L_II * sum_{K=J}^{I-1} A_IK L_KJ.
-            // The fp32 16x16x4 products take their k in the order 4 * grp + kk,
-            // so a lane's four A values are one 16-byte row read, its four B
-            // values one 16-byte read of L^T (tile (K, J) of sY holds L_KJ
-            // transposed), and the sum Y itself, as the accumulator leaves it,
-            // is the B operand of the product with L_II.
-#pragma unroll
-            for (int I = 1; I < NT; ++I) {
-                {
-                    const int J = Jw;
-                    if (I <= J) continue;
-                    floatx4 acc = zero4();
-#pragma unroll
-                    for (int K = J; K < I; ++K) {
-                        const floatx4 af = *reinterpret_cast<const floatx4 *>(sA + (kTile * I + l16) * A_LD +
-                                                                              kTile * K + 4 * grp);
-                        const floatx4 bf = *reinterpret_cast<const floatx4 *>(
-                            sY + ((K * (K + 1)) / 2 + J) * 16 * Y_LD + l16 * Y_LD + 4 * grp);
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) acc = mma_f32(af[kk], bf[kk], acc);
-                    }
-                    const floatx4 lf = *reinterpret_cast<const floatx4 *>(sL + (kTile * I + l16) * A_LD + kTile * I +
-                                                                          4 * grp);
-                    floatx4 out = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) out = mma_f32(lf[kk], acc[kk], out);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sL[(kTile * I + 4 * grp + r) * A_LD + kTile * J + l16] = -out[r];
-                    if (I <= NT - 2)
-                        *reinterpret_cast<floatx4 *>(sY + ((I * (I + 1)) / 2 + J) * 16 * Y_LD + l16 * Y_LD +
-                                                     4 * grp) = floatx4{-out[0], -out[1], -out[2], -out[3]};
-                }
+            // off-diagonal blocks of column Jw, top to bottom
+            if constexpr (NT > 1) {
+                if (Jw == 0) inverse_column<0, NT, A_LD, Y_LD>(sA, sL, sY, grp, l16);
+                if constexpr (NT > 2) if (Jw == 1) inverse_column<1, NT, A_LD, Y_LD>(sA, sL, sY, grp, l16);
+                if constexpr (NT > 3) if (Jw == 2) inverse_column<2, NT, A_LD, Y_LD>(sA, sL, sY, grp, l16);
+                static_assert(NT <= 4, "three block columns at most");
             }
         }
         // ---- the next item's inputs go in flight now, beside the inverse.

@@ -41,6 +41,19 @@ def test_fp32_shapes(dk, dv, chunk):
     check_prefill(spec, label=f"fp32 dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("T", [33, 64, 128, 130, 192, 300, 384])
+@pytest.mark.parametrize("B,H", [(1, 3), (2, 4)])
+def test_bf16_chunk_counts(T, B, H):
+    """d = 128, chunk 64 (the loader-fed state chain): 1 to 6 chunks per
+    sequence, full and ragged last chunks, so the chain's staging runs its
+    prologue alone, its three-chunk groups and both tail lengths; B * H = 3
+    and 8 chains take the two workgroup-to-chain mappings.  Slow decay and
+    h0 ~ N(0, 1), so the carried state matters in every chunk."""
+    spec = Spec(H=H, dk=128, dv=128, T=T, B=B, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow",
+                seed=35 + T)
+    check_prefill(spec, label=f"bf16 T={T} B={B} H={H}")
+
+
 @pytest.mark.parametrize("mode", ["config", "slow", "floor", "zero"])
 def test_bf16_decay_modes(mode):
     spec = Spec(H=4, dk=128, dv=128, T=1000, dtype="bf16", chunk=64, h0_std=1.0, g_mode=mode, seed=33)

@@ -953,7 +953,7 @@ __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     T *dst = (t0 + r < len) ? og + (size_t(tok0 + t0 + r) * H + h) * DV + j : dummy;
-                    *dst = from_f32<T>(cur.oi[i][r] + ao[r]);
+                    __builtin_nontemporal_store(from_f32<T>(cur.oi[i][r] + ao[r]), dst);
                 }
             }
         }

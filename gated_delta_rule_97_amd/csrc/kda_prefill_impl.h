@@ -1508,7 +1508,12 @@ struct ChainCfg {
     static constexpr int P = KB + PK + PD;
     static constexpr int PPT = (P + NTHR - 1) / NTHR;       // pieces per thread
     static constexpr int BUF = PPT * NTHR * 16;             // bytes per LDS buffer (padded)
-    static constexpr int NS = PPT > 16 ? 2 : 4;             // register stages (fewer when each holds more)
+    // d = 128 output chains: one LDS buffer and two register stages, so that
+    // two workgroups share a compute unit (the chain is latency-bound at one
+    // wave per SIMD); the buffer is rewritten between two barriers
+    static constexpr bool ONE = MODE == kFull && DK == 128 && DV == 128 && C == 64 && NWV == 4;
+    static constexpr int NBUF = ONE ? 1 : 2;
+    static constexpr int NS = ONE || PPT > 16 ? 2 : 4;      // register stages (fewer when each holds more)
     static_assert(NS % 2 == 0, "the LDS buffer of a chunk is its index mod 2");
     static_assert(DK % 32 == 0 && NTHR % kWave == 0, "chain shapes");
 };
@@ -1583,14 +1588,16 @@ __device__ __forceinline__ void chain_stage_write(unsigned char *buf, const Chai
 }
 
 template <int DK, int DV, int C, int NWV, int MODE>
-__global__ __launch_bounds__(kWave * NWV * (MODE == kSumBM ? 2 : 1)) void kda_chain_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kWave * NWV * (MODE == kSumBM ? 2 : 1), (ChainCfg<DK, DV, C, NWV, MODE>::ONE ? 2 : 1))
+void kda_chain_kernel(PrefillArgs a) {
     using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
     using Stage = ChainStage<DK, DV, C, NWV, MODE>;
     using M = Mma<bf16>;
     constexpr int NT = Cfg::NT, MT = Cfg::MT, NQ = Cfg::NQ, MP = Cfg::MP, NS = Cfg::NS, NB = DV / Cfg::BW;
+    constexpr bool ONE = Cfg::ONE;
     static_assert((MODE != kSumM && MODE != kSumBM) || DV == DK, "a transition is dk x dk");
     static_assert(DV % Cfg::BW == 0, "chain blocks");
-    __shared__ __align__(16) unsigned char sbuf[2][Cfg::BUF];
+    __shared__ __align__(16) unsigned char sbuf[Cfg::NBUF][Cfg::BUF];
 
     const int H = a.H;
     const bool segmented = a.seg_len > 0;
@@ -1676,9 +1683,12 @@ __global__ __launch_bounds__(kWave * NWV * (MODE == kSumBM ? 2 : 1)) void kda_ch
             const bool active = k < nchunks;
             // stage chunk c + 1 into the other buffer (opaque per-chunk bases
             // keep the compiler from holding every LDS address in a register)
-            chain_stage_write<DK, DV, C, NWV, MODE>(sbuf[0] + opaque(((s + 1) & 1) * Cfg::BUF), st[(s + 1) % NS], tid);
-            const unsigned char *ra = sbuf[0] + opaque((s & 1) * Cfg::BUF + 16 * lane);
-            const unsigned char *rd = sbuf[0] + opaque((s & 1) * Cfg::BUF + (Cfg::KB + Cfg::PK) * 16 + 16 * grp);
+            if (!ONE)
+                chain_stage_write<DK, DV, C, NWV, MODE>(sbuf[0] + opaque(((s + 1) & 1) * Cfg::BUF), st[(s + 1) % NS],
+                                                        tid);
+            const int bsel = ONE ? 0 : (s & 1);
+            const unsigned char *ra = sbuf[0] + opaque(bsel * Cfg::BUF + 16 * lane);
+            const unsigned char *rd = sbuf[0] + opaque(bsel * Cfg::BUF + (Cfg::KB + Cfg::PK) * 16 + 16 * grp);
             const Stage &cur = st[s];
 
             // B operands from the state: tiles 2p, 2p + 1
@@ -1740,6 +1750,10 @@ __global__ __launch_bounds__(kWave * NWV * (MODE == kSumBM ? 2 : 1)) void kda_ch
             // this stage's registers now take chunk c + NS
             chain_load<DK, DV, C, NWV, MODE>(st[s], a, min(c + NS, last), h, tid, loff, nblk, isM);
             __syncthreads();
+            if (ONE) {  // every read of chunk c is done: the buffer takes chunk c + 1
+                chain_stage_write<DK, DV, C, NWV, MODE>(sbuf[0] + opaque(0), st[(s + 1) % NS], tid);
+                __syncthreads();
+            }
         }
     }
 

@@ -40,6 +40,10 @@ CASES = [
                            seed=74), 64),
     ("bf16 decay floor", Spec(H=1, dk=128, dv=128, T=4096, B=1, dtype="bf16", chunk=64, h0_std=1.0,
                               g_mode="floor", seed=75), 64),
+    # 73 chunks in 9 segments of 9 (the last holds one chunk of 5 tokens):
+    # 9 chains, not a multiple of the 8 XCDs, take the plain block mapping
+    ("bf16 d128 nine segments", Spec(H=1, dk=128, dv=128, T=72 * 64 + 5, B=1, dtype="bf16", chunk=64, h0_std=1.0,
+                                     g_mode="slow", seed=80), 64),
     # v = 0: o and ht come only from h0 through every segment's transition;
     # 1024 tokens (8 segments of 128 at chunk 16) keep that state well above
     # underflow (over 8192 tokens it decays to ~1e-30)

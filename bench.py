@@ -194,7 +194,7 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
-    spec = workloads.CONFIGS[1]
+    spec = workloads.PREFILL_H32_T8K
     B, T, H, dk, dv, C = spec.B, spec.T, spec.H, spec.dk, spec.dv, spec.chunk
     log(f"generating {spec.name}")
     x = workloads.make_prefill(spec)
@@ -355,7 +355,7 @@ def main():
         log(f"checkpoints: {t_ck * 1e3:.1f} us/call vs {t_plain * 1e3:.1f} plain")
         del ck
 
-        lspec = workloads.CONFIGS[3]
+        lspec = workloads.LONG_CONTEXT_1M
         log(f"long context: {lspec.name}")
         xl = workloads.make_prefill(lspec, device=dev)
         wl = torch.empty(kda.workspace_bytes(lspec.B, lspec.T, lspec.H, lspec.dk, lspec.dv, lspec.B, lspec.chunk,

@@ -117,7 +117,7 @@ def test_resume_from_checkpoint():
 def test_headline_checkpoints_sampled():
     """The headline prefill (H=32, T=8192, d=128, bf16, chunk 64) with a
     checkpoint every 512 tokens: 16 per head; the oracle checks three."""
-    spec = workloads.CONFIGS[1]
+    spec = workloads.PREFILL_H32_T8K
     x = workloads.make_prefill(spec)
     (o, ht, ck), (o2, ht2) = run(x, 64, 512)
     assert torch.equal(o, o2) and torch.equal(ht, ht2)

@@ -22,7 +22,7 @@ Spec = workloads.PrefillSpec
 
 def test_tiny_fp32_config():
     """The tiny fp32 workload: B=1, H=2, T=64, d=32, chunk 16."""
-    check_prefill(workloads.CONFIGS[0], label="tiny fp32")
+    check_prefill(workloads.TINY_FP32, label="tiny fp32")
 
 
 @pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
@@ -145,7 +145,7 @@ def test_prefill_equals_decode_steps():
 def test_headline_config_full_size():
     """The headline workload at full size (B=1, H=32, T=8192, d=128, bf16,
     chunk 64, h0 ~ N(0, 0.02)) against the oracle on every output."""
-    check_prefill(workloads.CONFIGS[1], label="headline prefill H=32 T=8192")
+    check_prefill(workloads.PREFILL_H32_T8K, label="headline prefill H=32 T=8192")
 
 
 def _sample_sequences(x, seqs):
@@ -160,7 +160,7 @@ def test_varlen_full_size_sampled(mode, h0_std):
     """The packed workload at full size (64 sequences of U[256, 4096] tokens,
     H=16, d=128, bf16, per-sequence h0, chunk 64); the oracle checks seven
     whole sequences (first, last, shortest, longest and three others)."""
-    spec = workloads.CONFIGS[2].replace(g_mode=mode, h0_std=h0_std)
+    spec = workloads.VARLEN_64_SEQS.replace(g_mode=mode, h0_std=h0_std)
     x = workloads.make_prefill(spec)
     print(f"[parity] varlen full size g={mode}: T={spec.total_tokens}", flush=True)
     o, ht = gpu_prefill(x, 64)
@@ -182,7 +182,7 @@ def test_long_context_full_size_sampled():
     the final state of the full sequence must agree between chunk 16 and
     chunk 64 (a property at any size) and be finite."""
     import gated_delta_rule_97_amd as kda
-    spec = workloads.CONFIGS[3].replace(g_mode="slow")
+    spec = workloads.LONG_CONTEXT_1M.replace(g_mode="slow")
     dev = torch.device("cuda")
     print("[parity] 1M tokens: generating on the GPU", flush=True)
     x = workloads.make_prefill(spec, device=dev)

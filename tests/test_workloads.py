@@ -5,12 +5,12 @@ import torch
 import workloads
 
 
-def test_configs_shapes():
-    c1 = workloads.CONFIGS[1]
+def test_workload_shapes():
+    c1 = workloads.PREFILL_H32_T8K
     assert (c1.H, c1.dk, c1.dv, c1.T, c1.chunk) == (32, 128, 128, 8192, 64)
-    c2 = workloads.CONFIGS[2]
+    c2 = workloads.VARLEN_64_SEQS
     assert len(c2.seqlens) == 64 and min(c2.seqlens) >= 256 and max(c2.seqlens) <= 4096
-    assert workloads.CONFIGS[3].T == 1 << 20
+    assert workloads.LONG_CONTEXT_1M.T == 1 << 20
     d = workloads.DECODE
     assert (d.N, d.H, d.dk, d.steps) == (256, 32, 128, 128)
 

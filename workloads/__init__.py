@@ -86,18 +86,17 @@ def varlen_lengths(n: int, lo: int, hi: int, seed: int) -> tuple:
 # The five workloads: a tiny fp32 case, the headline prefill, packed
 # variable-length prefill with per-sequence initial states, 1M-token prefill,
 # and 256-stream decode.
-CONFIGS = {
-    0: PrefillSpec(H=2, dk=32, dv=32, T=64, dtype="fp32", chunk=16, seed=0,
-                   name="tiny fp32 prefill H=2 T=64 d=32 chunk=16"),
-    1: PrefillSpec(H=32, dk=128, dv=128, T=8192, dtype="bf16", chunk=64,
-                   h0_std=0.02, seed=1,
-                   name="prefill B=1 H=32 T=8192 d=128 bf16"),
-    2: PrefillSpec(H=16, dk=128, dv=128, seqlens=varlen_lengths(64, 256, 4096, 2),
-                   dtype="bf16", chunk=64, h0_std=0.02, seed=2,
-                   name="varlen prefill 64 seqs U[256,4096] H=16 d=128 bf16"),
-    3: PrefillSpec(H=8, dk=128, dv=128, T=1 << 20, dtype="bf16", chunk=64, seed=3,
-                   name="long-context prefill B=1 H=8 T=1048576 d=128 bf16"),
-}
+TINY_FP32 = PrefillSpec(H=2, dk=32, dv=32, T=64, dtype="fp32", chunk=16, seed=0,
+                        name="tiny fp32 prefill H=2 T=64 d=32 chunk=16")
+PREFILL_H32_T8K = PrefillSpec(H=32, dk=128, dv=128, T=8192, dtype="bf16", chunk=64,
+                              h0_std=0.02, seed=1,
+                              name="prefill B=1 H=32 T=8192 d=128 bf16")
+VARLEN_64_SEQS = PrefillSpec(H=16, dk=128, dv=128, seqlens=varlen_lengths(64, 256, 4096, 2),
+                             dtype="bf16", chunk=64, h0_std=0.02, seed=2,
+                             name="varlen prefill 64 seqs U[256,4096] H=16 d=128 bf16")
+LONG_CONTEXT_1M = PrefillSpec(H=8, dk=128, dv=128, T=1 << 20, dtype="bf16", chunk=64, seed=3,
+                              name="long-context prefill B=1 H=8 T=1048576 d=128 bf16")
+PREFILL_WORKLOADS = (TINY_FP32, PREFILL_H32_T8K, VARLEN_64_SEQS, LONG_CONTEXT_1M)
 DECODE = DecodeSpec(N=256, H=32, dk=128, dv=128, steps=128, dtype="bf16",
                     state_std=0.02, seed=4,
                     name="decode N=256 H=32 d=128 bf16, 128 steps")

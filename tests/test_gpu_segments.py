@@ -77,9 +77,11 @@ def test_segmented_equals_single_chain():
     assert rel_l2(to_np64(h1), to_np64(h2)) <= TOL_BF16
 
 
-def test_segmented_with_checkpoints():
+# dv = 128 takes the single-LDS-buffer output chain, dv = 64 the double-buffered one
+@pytest.mark.parametrize("dv", [64, 128])
+def test_segmented_with_checkpoints(dv):
     from test_gpu_checkpoints import ref_checkpoints
-    spec = Spec(H=2, dk=128, dv=64, T=8192, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow", seed=78)
+    spec = Spec(H=2, dk=128, dv=dv, T=8192, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow", seed=78)
     x = workloads.make_prefill(spec)
     (o, ht, ck), kt = run(x, 64, ckpt_stride=1024)
     assert "kda_seg_scan" in kt

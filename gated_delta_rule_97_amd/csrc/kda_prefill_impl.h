@@ -564,7 +564,10 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const ChunkLoc cur = loc;
         int nxt = item + gridDim.x;
         while (nxt < nitems && !locate_chunk(a, intra_slot(a, nxt / H), C, loc)) nxt += gridDim.x;
-        if (nxt >= nitems) loc = cur;
+        if (nxt >= nitems) {  // no next item: the prefetch below (never used) reads one row
+            loc = cur;
+            loc.len = 1;
+        }
         const int nxt_h = (nxt < nitems ? nxt : item) % H;
         __syncthreads();
 

@@ -1494,7 +1494,7 @@ __device__ __forceinline__ void chain_ckpt(const PrefillArgs &a, const floatx4 (
 // Q', K~^T — are staged per chunk in LDS in the same permuted order (one
 // 16-byte read per operand), with e^{Gam_last}, double-buffered, from a
 // ring of NS register stages loaded NS - 1 chunks ahead; one barrier per
-// chunk.  The loop runs whole NS-chunk groups; chunks past the chain's end
+// chunk (the d = 128 output chains: one buffer, two barriers, see ONE).  The loop runs whole NS-chunk groups; chunks past the chain's end
 // are inactive (state kept, nothing stored): branch-free, static ring indices.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int C, int NWV, int MODE>

@@ -41,11 +41,11 @@ def test_fp32_shapes(dk, dv, chunk):
     check_prefill(spec, label=f"fp32 dk={dk} dv={dv}")
 
 
-@pytest.mark.parametrize("T", [33, 64, 128, 130, 192, 300, 384])
+@pytest.mark.parametrize("T", [1, 17, 33, 64, 128, 130, 192, 300, 384])
 @pytest.mark.parametrize("B,H", [(1, 3), (2, 4)])
 def test_bf16_chunk_counts(T, B, H):
     """d = 128, chunk 64 (the loader-fed state chain): 1 to 6 chunks per
-    sequence, full and ragged last chunks, so the chain's staging runs its
+    sequence, full and ragged last chunks (down to one token), so the chain's staging runs its
     prologue alone, its three-chunk groups and both tail lengths; B * H = 3
     and 8 chains take the two workgroup-to-chain mappings.  Slow decay and
     h0 ~ N(0, 1), so the carried state matters in every chunk."""

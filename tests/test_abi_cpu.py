@@ -59,6 +59,25 @@ def test_workspace_size():
     assert e.value.status == kda.KDA_ERR_SHAPE
 
 
+
+def test_workspace_segment_states_follow_the_plan():
+    """1M tokens x 8 heads (32 chains of 32 columns, long) runs segment-parallel
+    with 32 segments per head: the workspace adds three fp32 dk x dv states per
+    (segment, head), the two summaries and the scanned incoming state.  The
+    H = 32, T = 8192 call (128 chains) and a sequence under 64 chunks run one
+    chain per head and add none."""
+    per_slot = 5 * 64 * 128 * 2 + 128 * 4
+    st = 128 * 128 * 4
+
+    def extra(T, H):
+        w = kda.kda_chunk_prefill_workspace_size(1, T, H, 128, 128, 1, 64, BF16)
+        return w - (T // 64 + 1) * H * per_slot
+
+    assert 3 * 32 * 8 * st <= extra(1 << 20, 8) < 3 * 32 * 8 * st + (1 << 20)
+    assert 0 <= extra(8192, 32) < st
+    assert 0 <= extra(63 * 64, 1) < st
+
+
 # fake, never-dereferenced device addresses (validation fails before use)
 A = 1 << 32
 

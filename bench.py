@@ -7,15 +7,23 @@ beta and states, chunk 64, h0 ~ N(0, 0.02).  One step = one kda_chunk_prefill
 call over the whole batch (all of its kernels), inputs resident in HBM.
 value = tokens/s = B*T / (time per call).
 
+The K timed calls carry one event between consecutive calls and none
+inside a call: ms_per_step is their mean, "timing" their median and
+p10/p90.  Per-kernel durations come from a second timed pass of K calls
+with HIP events around every launch on its stream; "roofline" charges the
+longest kernel with the whole call's algorithmic bytes (1,540 B per
+token-head plus the states), "kernel_scoped" with its own, "path_roofline"
+gives the whole call's fraction.
+
 Also measured and reported in the same JSON line: decode (256 sequences x 32
-heads, d = 128, 128 consecutive in-place steps); under "next": speculative
-verify/commit of 4 draft tokens on that batch, the headline prefill with a
-state checkpoint every 512 tokens, and the 1M-token x 8-head prefill
-(segment-parallel chain, and the single chain for comparison); per-kernel durations from
-HIP events recorded around every launch on the launch stream, roofline
-fractions against MI355X peaks (HBM 8 TB/s; bf16 MFMA 2.5 PFLOP/s), and the
-fp64 oracle timed on the host cores on the same inputs (a reported baseline,
-with a parity check of the benchmarked output).
+heads, d = 128, 128 consecutive in-place steps); packed variable-length
+prefill (64 sequences of U[256, 4096] tokens, H = 16); under "next":
+speculative verify/commit of 4 draft tokens on the decode batch, the
+headline prefill with a state checkpoint every 512 tokens, and the 1M-token
+x 8-head prefill (segment-parallel chain, and the single chain for
+comparison); roofline fractions against MI355X peaks (HBM 8 TB/s; bf16 MFMA
+2.5 PFLOP/s), and the fp64 oracle timed on the host cores on the same inputs
+(a reported baseline, with a parity check of the benchmarked output).
 
 Progress goes to stderr; stdout carries exactly one JSON line.
 """
@@ -53,6 +61,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def source_digest():
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_97_amd", "csrc", "*"))):
@@ -78,6 +98,8 @@ def load_traffic(kernel, workload):
 
 PREFILL_WORKLOAD = "prefill B=1 H=32 T=8192 d=128 bf16 chunk=64"
 DECODE_WORKLOAD = "decode N=256 H=32 d=128 bf16"
+VERIFY_WORKLOAD = "verify N=256 H=32 d=128 bf16, 4 draft tokens"
+VERIFY_K = 4
 CALIB_BYTES = 1 << 30  # the calibration copy moves 1 GiB each way
 
 
@@ -99,6 +121,7 @@ def ingest_pmc(fetch_dir, write_dir):
                 key = ("kda_intra" if "kda_intra_kernel" in name
                        else "kda_inter" if ("kda_inter_kernel" in name or "kda_inter_ws_kernel" in name)
                        else "kda_decode" if "kda_decode_kernel" in name
+                       else "kda_decode_verify" if "kda_decode_multi_kernel" in name
                        else "copy" if "copy" in name.lower() and float(r["Counter_Value"]) > 0 else None)
                 if key:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -111,7 +134,8 @@ def ingest_pmc(fetch_dir, write_dir):
     out = {"calibration": {"copy_bytes": CALIB_BYTES, "fetch_size_kib": max(fetch["copy"]),
                            "write_size_kib": max(write["copy"]), "fetch_scale": round(f_scale, 4),
                            "write_scale": round(w_scale, 4)}}
-    for k, wl in (("kda_intra", PREFILL_WORKLOAD), ("kda_inter", PREFILL_WORKLOAD), ("kda_decode", DECODE_WORKLOAD)):
+    for k, wl in (("kda_intra", PREFILL_WORKLOAD), ("kda_inter", PREFILL_WORKLOAD), ("kda_decode", DECODE_WORKLOAD),
+                  ("kda_decode_verify", VERIFY_WORKLOAD)):
         if k in fetch and k in write:
             for c, vals in (("FETCH_SIZE", fetch[k]), ("WRITE_SIZE", write[k])):
                 # every dispatch must be the one workload: a run that also launched the
@@ -214,46 +238,73 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    def timed_calls(fn, n):
+        """n back-to-back calls with one event between consecutive calls (no
+        event inside a call); returns the per-call times in ms."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(n):
+            fn()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+
+    def spread(ts):
+        s = sorted(ts)
+        pick = lambda f: s[min(len(s) - 1, max(0, int(round(f * (len(s) - 1)))))]
+        return {"median_us": round(1e3 * pick(0.5), 2), "p10_us": round(1e3 * pick(0.1), 2),
+                "p90_us": round(1e3 * pick(0.9), 2), "calls": len(s)}
+
     log(f"prefill timed x{args.steps}")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    kda.kda_profile_start(8 * args.steps + 8)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    call_ms = timed_calls(step, args.steps)
     wall = time.perf_counter() - w0
-    kt = kda.kda_profile_stop()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = sum(call_ms) / args.steps
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
-    log(f"prefill {ms_step * 1e3:.1f} us/call -> {value / 1e6:.2f} M tokens/s (wall {wall * 1e3 / args.steps:.1f} us)")
+    headline_spread = spread(call_ms)
+    log(f"prefill {ms_step * 1e3:.1f} us/call (median {headline_spread['median_us']:.1f}, p10 "
+        f"{headline_spread['p10_us']:.1f}, p90 {headline_spread['p90_us']:.1f}) -> {value / 1e6:.2f} M tokens/s "
+        f"(host wall {wall * 1e3 / args.steps:.3f} ms/call)")
+
+    # per-kernel durations: a second timed pass of the same calls, every
+    # launch bracketed by events on its stream (kept out of the pass above)
+    kda.kda_profile_start(8 * args.steps + 8)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = kda.kda_profile_stop()
 
     per_kernel_us = {name: 1e3 * tot / n for name, (n, tot) in kt.items()}
     th = B * T * H
     state_bytes = 2 * B * H * dk * dv * 4
+    path_bytes = BYTES_PER_TOKEN_HEAD * th + state_bytes
     kernel_bytes = {"kda_intra": INTRA_BYTES_PER_TOKEN_HEAD * th,
                     "kda_inter": INTER_BYTES_PER_TOKEN_HEAD * th + state_bytes}
     dom = max(per_kernel_us, key=per_kernel_us.get)
     dom_us = per_kernel_us[dom]
-    achieved = kernel_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
+    achieved = path_bytes / (dom_us * 1e-6) / 1e9
+    own = kernel_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
     workload = PREFILL_WORKLOAD
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(dom, workload),
                 "avg_launch_us": round(dom_us, 2),
-                "algorithmic_bytes_per_launch": kernel_bytes.get(dom, 0)}
-    path_bytes = BYTES_PER_TOKEN_HEAD * th + state_bytes
+                "algorithmic_bytes_per_launch": path_bytes,
+                "kernel_scoped": {"bytes_per_launch": kernel_bytes.get(dom, 0), "achieved": round(own, 1),
+                                  "frac": round(own / HBM_PEAK_GBS, 4)}}
     path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
     path_tflops = FLOPS_PER_TOKEN_HEAD * th / (ms_step * 1e-3) / 1e12
+    floor_us = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
     path_roofline = {"bound": "hbm", "algorithmic_bytes": path_bytes,
                      "achieved_GBps": round(path_gbs, 1), "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_flops": FLOPS_PER_TOKEN_HEAD * th,
                      "achieved_TFLOPs": round(path_tflops, 2),
                      "mfma_frac": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "hbm_floor_us": round(path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
+                     "attainable_frac": round(floor_us / (ms_step * 1e3), 4),
+                     "hbm_floor_us": round(floor_us, 2)}
 
     # ---------------------------------------------------------------- decode
     dspec = workloads.DECODE
@@ -270,6 +321,7 @@ def main():
 
     decode_pass()  # warmup
     torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = []
     dec_kt = {}
     for p in range(args.decode_passes):
@@ -300,21 +352,21 @@ def main():
                            "avg_launch_us": round(dec_launch_us, 2),
                            "algorithmic_bytes_per_launch": dec_bytes}}
 
-    # ------------------------------------- next rows: verify, checkpoints,
-    # long context (each with its own algorithmic bytes and roofline)
-    def next_rows():
-        def timed(fn, reps):
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
             fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / reps  # ms
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
 
-        K = 4
+    # ----------------------------- speculative verify / commit on the decode
+    # batch (also in --headline-only runs, so its counters can be taken)
+    def verify_row(with_commit):
+        K = VERIFY_K
         drafts = workloads.make_decode_drafts(dspec, K, device=dev)
         ov = torch.empty((dspec.N, K, dspec.H, dspec.dv), dtype=torch.bfloat16, device=dev)
         nacc = torch.full((dspec.N,), K, dtype=torch.int32, device=dev)
@@ -322,27 +374,33 @@ def main():
         t_verify = timed(lambda: kda.decode_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"], drafts["beta"],
                                                    st_v, o=ov), 20)
         st_c = state0.clone()
-        t_commit = timed(lambda: kda.decode_commit(drafts["k"], drafts["v"], drafts["g"], drafts["beta"], nacc, st_c),
-                         20)
+        t_commit = (timed(lambda: kda.decode_commit(drafts["k"], drafts["v"], drafts["g"], drafts["beta"], nacc,
+                                                    st_c), 20) if with_commit else float("nan"))
         nh = dspec.N * dspec.H
         vbytes = nh * (dspec.dk * dspec.dv * 4 + K * 1540)            # state read once + K tokens' vectors
         cbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * 1284)        # state read + written, no q or o
         vgbs = vbytes / (t_verify * 1e-3) / 1e9
         cgbs = cbytes / (t_commit * 1e-3) / 1e9
         log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s)")
+        r = lambda x, nd: None if x != x else round(x, nd)  # NaN (not measured) -> null
         verify = {"workload": f"decode batch N={dspec.N} H={dspec.H} d=128 bf16, {K} draft tokens",
-                  "verify_us": round(t_verify * 1e3, 2), "commit_us": round(t_commit * 1e3, 2),
+                  "verify_us": round(t_verify * 1e3, 2), "commit_us": r(t_commit * 1e3, 2),
                   "draft_tokens_per_s": round(dspec.N * K / (t_verify * 1e-3), 1),
-                  "vs_k_decode_steps": round(K * dec_launch_us / (t_verify * 1e3 + t_commit * 1e3), 3),
+                  "vs_k_decode_steps": r(K * dec_launch_us / (t_verify * 1e3 + t_commit * 1e3), 3),
                   "roofline": {"kernel": "kda_decode_verify", "bound": "hbm", "achieved": round(vgbs, 1),
                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(vgbs / HBM_PEAK_GBS, 4),
-                               "traffic": None, "avg_launch_us": round(t_verify * 1e3, 2),
+                               "traffic": load_traffic("kda_decode_verify", VERIFY_WORKLOAD),
+                               "avg_launch_us": round(t_verify * 1e3, 2),
                                "algorithmic_bytes_per_launch": vbytes},
-                  "commit_roofline": {"kernel": "kda_decode_commit", "bound": "hbm", "achieved": round(cgbs, 1),
-                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cgbs / HBM_PEAK_GBS, 4),
-                                      "avg_launch_us": round(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes}}
+                  "commit_roofline": {"kernel": "kda_decode_commit", "bound": "hbm", "achieved": r(cgbs, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r(cgbs / HBM_PEAK_GBS, 4),
+                                      "avg_launch_us": r(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes}}
         del drafts, ov, st_v, st_c
+        return verify
 
+    # ------------------------------------- next rows: verify, checkpoints,
+    # long context (each with its own algorithmic bytes and roofline)
+    def next_rows():
         stride = 512
         nck = kda.checkpoint_count(T, stride, B)
         ck = torch.empty((nck, H, dk, dv), dtype=torch.float32, device=dev)
@@ -386,9 +444,52 @@ def main():
                                       "hbm_floor_ms": round(lbytes / (HBM_PEAK_GBS * 1e9) * 1e3, 3)}}
         del xl, wl, ol, hl
         torch.cuda.empty_cache()
-        return {"speculative_verify": verify, "checkpoints": ckpt, "long_context": long_ctx}
+        return {"checkpoints": ckpt, "long_context": long_ctx}
 
+    verify = verify_row(with_commit=not args.headline_only)
+
+    # ------------------------- packed variable-length prefill (64 sequences)
+    def varlen_row():
+        vspec = workloads.VARLEN_64_SEQS
+        log(f"varlen: {vspec.name}")
+        xv = workloads.make_prefill(vspec, device=dev)
+        Tv, Hv, Nv = vspec.total_tokens, vspec.H, vspec.num_seqs
+        ov = torch.empty((1, Tv, Hv, vspec.dv), dtype=torch.bfloat16, device=dev)
+        hv = torch.empty((Nv, Hv, vspec.dk, vspec.dv), dtype=torch.float32, device=dev)
+        wv = torch.empty(kda.workspace_bytes(1, Tv, Hv, vspec.dk, vspec.dv, Nv, vspec.chunk, kda.KDA_DTYPE_BF16),
+                         dtype=torch.uint8, device=dev)
+
+        def vstep():
+            kda.chunk_prefill(xv["q"], xv["k"], xv["v"], xv["g"], xv["beta"], xv["h0"], xv["cu_seqlens"],
+                              chunk_size=vspec.chunk, o=ov, ht=hv, workspace=wv)
+
+        for _ in range(3):
+            vstep()
+        ts = timed_calls(vstep, 20)
+        sp = spread(ts)
+        t_med = sp["median_us"] * 1e-6
+        vbytes = BYTES_PER_TOKEN_HEAD * Tv * Hv + 2 * Nv * Hv * vspec.dk * vspec.dv * 4
+        gbs = vbytes / t_med / 1e9
+        kda.kda_profile_start(64)
+        for _ in range(5):
+            vstep()
+        torch.cuda.synchronize()
+        vkt = kda.kda_profile_stop()
+        log(f"varlen: {sp['median_us']:.1f} us/call (median) -> {Tv / t_med / 1e6:.2f} M tokens/s, {gbs:.0f} GB/s")
+        row = {"workload": f"{vspec.name} chunk=64, h0 N(0,0.02), T={Tv}",
+               "tokens_per_s": round(Tv / t_med, 1), "timing": sp,
+               "kernels_us": {k: round(1e3 * v[1] / v[0], 1) for k, v in vkt.items()},
+               "path_roofline": {"bound": "hbm", "algorithmic_bytes": vbytes, "achieved_GBps": round(gbs, 1),
+                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                 "hbm_floor_us": round(vbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}}
+        del xv, ov, hv, wv
+        torch.cuda.empty_cache()
+        return row
+
+    varlen = None if args.headline_only else varlen_row()
     nxt = None if args.headline_only else next_rows()
+    if nxt is not None:
+        nxt["speculative_verify"] = verify
 
     # -------------------------------------------- oracle on the host cores
     cpu = None
@@ -411,7 +512,7 @@ def main():
         cpu = {"value": round(reps * tokens / t_cpu, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the full headline workload ({T} tokens x {H} heads), fp64 token loop, "
                          f"{reps} runs in {t_cpu:.2f} s wall",
-               "host_cpus": os.cpu_count()}
+               "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
         step()
         torch.cuda.synchronize()
         on = o[0].double().cpu().numpy()
@@ -450,10 +551,10 @@ def main():
            "data": "synthetic (seeded generators: unit-norm q/k, N(0,1) v, sigmoid beta, g=-5*sigmoid(N(0,1)))",
            "config": {"workload": workload, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
                       "h0": "N(0,0.02)"},
-           "roofline": roofline, "path_roofline": path_roofline,
+           "roofline": roofline, "path_roofline": path_roofline, "timing": headline_spread,
            "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
-           "cpu_baseline": cpu, "parity": parity, "decode": decode,
-           "next": nxt,
+           "cpu_baseline": cpu, "parity": parity, "decode": decode, "varlen": varlen,
+           "next": nxt if nxt is not None else {"speculative_verify": verify},
            "source_digest": source_digest()}
     print(json.dumps(out), flush=True)
 

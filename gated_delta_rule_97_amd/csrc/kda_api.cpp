@@ -59,6 +59,8 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
     off = align_up(off + sch * dk * dv * sizeof(float), 256);
     L.dummy = off;
     off += 1024;
+    L.flag = off;  // result word of the checked mode
+    off += 256;
     L.total = off;
     return L;
 }
@@ -239,13 +241,18 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return KDA_ERR_ALIAS;
     }
 
-    if (flags & KDA_FLAG_CHECK_DECAY) {
-        unsigned flag = 0;
-        if (run_checks(g, rows * H * dk, cu_seqlens, N, T, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
-        if (flag & 2u) return KDA_ERR_SHAPE;
-        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    if (N == 0) {
+        // nothing to compute (the workspace may be absent); the checked mode
+        // still screens the inputs, with the device's shared result word
+        if (flags & KDA_FLAG_CHECK_DECAY) {
+            unsigned flag = 0;
+            if (run_checks(g, rows * H * dk, cu_seqlens, N, T, nullptr, stream, &flag) != hipSuccess)
+                return KDA_ERR_LAUNCH;
+            if (flag & 2u) return KDA_ERR_SHAPE;
+            if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+        }
+        return KDA_OK;
     }
-    if (N == 0) return KDA_OK;
 
     const SegPlan sp = (flags & KDA_FLAG_NO_SEGMENTS) ? SegPlan{1, 0}
                                                      : seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
@@ -254,6 +261,15 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     const SegPlan sp_ws = seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
     const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb, sp_ws.nseg);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        // the result word is this call's own (in its workspace)
+        unsigned flag = 0;
+        if (run_checks(g, rows * H * dk, cu_seqlens, N, T, reinterpret_cast<unsigned *>(ws + L.flag), stream,
+                       &flag) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+        if (flag & 2u) return KDA_ERR_SHAPE;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
     PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0;
     a.cu = cu_seqlens;
@@ -351,7 +367,7 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *g,
     if (overlap(state, nstate, o, no)) return KDA_ERR_ALIAS;
     if (flags & KDA_FLAG_CHECK_DECAY) {
         unsigned flag = 0;
-        if (run_checks(g, nh * dk, nullptr, 0, 0, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (run_checks(g, nh * dk, nullptr, 0, 0, nullptr, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
         if (flag & 1u) return KDA_ERR_DECAY_BOUND;
     }
     hipError_t e = launch_decode(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, N, H, dk, dv, stream);
@@ -390,7 +406,7 @@ int kda_decode_verify(const void *q, const void *k, const void *v, const float *
         if (overlap(o, no, b.p, b.n)) return KDA_ERR_ALIAS;
     if (flags & KDA_FLAG_CHECK_DECAY) {
         unsigned flag = 0;
-        if (run_checks(g, rows * dk, nullptr, 0, 0, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (run_checks(g, rows * dk, nullptr, 0, 0, nullptr, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
         if (flag & 1u) return KDA_ERR_DECAY_BOUND;
     }
     hipError_t e = launch_decode_verify(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, N, K, H, dk,
@@ -417,7 +433,7 @@ int kda_decode_commit(const void *k, const void *v, const float *g, const float 
         if (overlap(state, nstate, b.p, b.n)) return KDA_ERR_ALIAS;
     if (flags & KDA_FLAG_CHECK_DECAY) {
         unsigned flag = 0;
-        if (run_checks(g, rows * dk, nullptr, 0, 0, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (run_checks(g, rows * dk, nullptr, 0, 0, nullptr, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
         if (flag & 1u) return KDA_ERR_DECAY_BOUND;
     }
     hipError_t e = launch_decode_commit(dtype == KDA_DTYPE_BF16 ? 1 : 0, k, v, g, beta, n_accept, state, N, K, H,

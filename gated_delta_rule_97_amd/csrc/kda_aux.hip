@@ -67,46 +67,54 @@ hipError_t launch_chunk_offsets(const int32_t *cu, int N, int T, int C, int nc_m
 }
 
 // ---- debug checks (KDA_FLAG_CHECK_DECAY) ----
+// The result word lives where the caller says: the prefill passes a word of
+// its own workspace, so checked prefills on different streams never share
+// it; the decode calls (which take no workspace) share this one per device.
 __device__ unsigned int g_kda_check_flag;
 
-__global__ void kda_flag_reset_kernel() { g_kda_check_flag = 0u; }
+__global__ void kda_flag_reset_kernel(unsigned *flag) { *flag = 0u; }
 
-__global__ void kda_check_decay_kernel(const float *__restrict__ g, size_t n) {
+__global__ void kda_check_decay_kernel(const float *__restrict__ g, size_t n, unsigned *flag) {
     unsigned bad = 0;
     const size_t stride = size_t(gridDim.x) * blockDim.x;
     for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
         const float x = g[i];
         if (!(x >= -5.f && x <= 0.f)) bad = 1u;  // NaN fails both comparisons
     }
-    if (bad) atomicOr(&g_kda_check_flag, 1u);
+    if (bad) atomicOr(flag, 1u);
 }
 
-__global__ void kda_check_cu_kernel(const int32_t *__restrict__ cu, int N, int T) {
+__global__ void kda_check_cu_kernel(const int32_t *__restrict__ cu, int N, int T, unsigned *flag) {
     unsigned bad = 0;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < N; i += gridDim.x * blockDim.x)
         if (cu[i + 1] < cu[i]) bad = 2u;
     if (blockIdx.x == 0 && threadIdx.x == 0 && (cu[0] != 0 || cu[N] != T)) bad = 2u;
-    if (bad) atomicOr(&g_kda_check_flag, bad);
+    if (bad) atomicOr(flag, bad);
 }
 
-hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N, int T, hipStream_t s,
+hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N, int T, unsigned *flag_dev, hipStream_t s,
                       unsigned *flag_out) {
-    hipLaunchKernelGGL(kda_flag_reset_kernel, dim3(1), dim3(1), 0, s);
+    if (!flag_dev) {
+        hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&flag_dev), HIP_SYMBOL(g_kda_check_flag));
+        if (e != hipSuccess) return e;
+    }
+    // a fill kernel, not a memset node: safe inside a captured graph
+    hipLaunchKernelGGL(kda_flag_reset_kernel, dim3(1), dim3(1), 0, s, flag_dev);
     if (n > 0) {
         size_t blocks = (n + 255) / 256;
         if (blocks > 4096) blocks = 4096;
-        hipLaunchKernelGGL(kda_check_decay_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, g, n);
+        hipLaunchKernelGGL(kda_check_decay_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, g, n, flag_dev);
     }
     if (cu) {
         const int blocks = N / 256 + 1 > 1024 ? 1024 : N / 256 + 1;
-        hipLaunchKernelGGL(kda_check_cu_kernel, dim3(blocks), dim3(256), 0, s, cu, N, T);
+        hipLaunchKernelGGL(kda_check_cu_kernel, dim3(blocks), dim3(256), 0, s, cu, N, T, flag_dev);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return e;
     unsigned flag = 0;
-    e = hipMemcpyFromSymbol(&flag, HIP_SYMBOL(g_kda_check_flag), sizeof(flag), 0, hipMemcpyDeviceToHost);
+    e = hipMemcpyAsync(&flag, flag_dev, sizeof(flag), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return e;
+    e = hipStreamSynchronize(s);
     if (e != hipSuccess) return e;
     *flag_out = flag;
     return hipSuccess;

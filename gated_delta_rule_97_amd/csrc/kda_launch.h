@@ -57,7 +57,7 @@ SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq);
 
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {
-    size_t coff, ckoff, W, Qp, KtT, Ut, Oi, D, Mseg, Bseg, Sin, dummy, total;
+    size_t coff, ckoff, W, Qp, KtT, Ut, Oi, D, Mseg, Bseg, Sin, dummy, flag, total;
 };
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
                              size_t elem_bytes, int nseg);
@@ -97,10 +97,12 @@ hipError_t launch_decode_commit(int dtype, const void *k, const void *v,
                                 const float *g, const float *beta,
                                 const int32_t *n_accept, float *state, int N,
                                 int K, int H, int dk, int dv, hipStream_t s);
-// Debug checks: set a device flag when g leaves [-5, 0] (bit 0) or when
-// cu_seqlens is malformed (bit 1), then read it back synchronously.
+// Debug checks: set the device word flag_dev (null: one word shared per
+// device) when g leaves [-5, 0] (bit 0) or when cu_seqlens is malformed
+// (bit 1), then read it back synchronously into *flag_out.
 hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N,
-                      int T, hipStream_t s, unsigned *flag_out);
+                      int T, unsigned *flag_dev, hipStream_t s,
+                      unsigned *flag_out);
 
 // Whether a dtype / size combination has kernels built (fp32 with chunk 64
 // needs dk, dv <= 64 to fit the intra-chunk kernel in LDS).

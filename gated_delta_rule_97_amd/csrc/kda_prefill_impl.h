@@ -165,15 +165,30 @@ struct IntraLds {
     static constexpr int NLT = NT * (NT - 1) / 2;  // L^T tiles (K, J), J <= K <= NT - 2
     static constexpr size_t kKK = size_t(2) * C * K_LD * sizeof(T);  // K+ and K-
     static constexpr size_t kAL = size_t(2) * C * A_LD * 4;          // A and L (reuse K+, K-)
+    static constexpr size_t sQp = size_t(C) * K_LD * sizeof(T);
+    static constexpr size_t sKT = size_t(DK) * KT_LD * sizeof(T);
+    static constexpr size_t sVT = size_t(DV) * KT_LD * sizeof(T);
+    static constexpr size_t sP = size_t(C) * P_LD * sizeof(T);
+    static constexpr size_t sTail = size_t(NLT > 0 ? NLT : 1) * 16 * Y_LD * 4 + size_t(NSEG + 1) * DK * 4 +
+                                    size_t(NOFF > 0 ? NOFF : 1) * DK * 4 + size_t(NT) * DK * 4 + size_t(C) * 4;
+    static constexpr size_t kKA = kKK > kAL ? kKK : kAL;
+    // Compact placement, for the shapes whose plain layout exceeds the 160
+    // KiB of a compute unit (fp32 with a 64-token chunk and dk or dv = 128):
+    // (beta v)^T is staged after the A/P products, into the dead K+/K- space
+    // behind A and L, and P is stored into A's space once the inverse has
+    // read A.  Same products, same values; two phases hold them longer.
+    static constexpr bool COMPACT = kKA + sQp + sKT + sVT + sP + sTail > size_t(160) * 1024;
+    static constexpr size_t kReg = COMPACT ? (kKK > kAL + sVT ? kKK : kAL + sVT) : kKA;
     static constexpr size_t oKp = 0;
     static constexpr size_t oKm = oKp + size_t(C) * K_LD * sizeof(T);
     static constexpr size_t oA = 0;
     static constexpr size_t oL = oA + size_t(C) * A_LD * 4;
-    static constexpr size_t oQp = (kKK > kAL ? kKK : kAL);
-    static constexpr size_t oKT = oQp + size_t(C) * K_LD * sizeof(T);
-    static constexpr size_t oVT = oKT + size_t(DK) * KT_LD * sizeof(T);
-    static constexpr size_t oP = oVT + size_t(DV) * KT_LD * sizeof(T);
-    static constexpr size_t oY = oP + size_t(C) * P_LD * sizeof(T);
+    static constexpr size_t oQp = kReg;
+    static constexpr size_t oKT = oQp + sQp;
+    static constexpr size_t oVT = COMPACT ? kAL : oKT + sKT;
+    static constexpr size_t oP = COMPACT ? oA : oVT + sVT;
+    static constexpr size_t oY = COMPACT ? oKT + sKT : oP + sP;
+    static_assert(!COMPACT || sP <= size_t(C) * A_LD * 4, "P fits in A's space");
     static constexpr size_t oTot = oY + size_t(NLT > 0 ? NLT : 1) * 16 * Y_LD * 4;
     static constexpr size_t oF = oTot + size_t(NSEG + 1) * DK * 4;
     static constexpr size_t oR = oF + size_t(NOFF > 0 ? NOFF : 1) * DK * 4;
@@ -382,6 +397,22 @@ __device__ __forceinline__ void inverse_column(const float *sA, float *sL, const
     }
 }
 
+// (beta v)^T of the chunk from a role V thread's registers: its 8 value
+// columns, 4 tokens each.
+template <class T, int DK, int DV, int C>
+__device__ __forceinline__ void stage_bv(T *sVT, const float *sB, const IntraIn<T, DK, DV, C> &in, int tid) {
+    constexpr int KT_LD = IntraLds<T, DK, DV, C>::KT_LD;
+    bool is_g;
+    int jg, sg;
+    owner_coords<T, DK, DV, C>(tid, is_g, jg, sg);
+    static_assert(kSR == 4, "four tokens' beta per owner");
+    const float4 b4 = *reinterpret_cast<const float4 *>(sB + kSR * sg);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, b4.x * v_get(in, 0, j), b4.y * v_get(in, 1, j),
+               b4.z * v_get(in, 2, j), b4.w * v_get(in, 3, j));
+}
+
 template <class T, int DK, int DV, int C>
 __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     using Ly = IntraLds<T, DK, DV, C>;
@@ -490,16 +521,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     for (int J2 = 0; J2 < I2; ++J2) sF[(I2 * (I2 - 1) / 2 + J2) * DK + c] = exp_e(rr[I2] - rr[J2]);
                 }
             }
-        } else if (rt >= R::NG) {
-            bool is_g;
-            int jg, sg;
-            owner_coords<T, DK, DV, C>(tid, is_g, jg, sg);
-            static_assert(kSR == 4, "four tokens' beta per owner");
-            const float4 b4 = *reinterpret_cast<const float4 *>(sB + kSR * sg);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                store4(sVT + (8 * jg + j) * KT_LD + kSR * sg, b4.x * v_get(in, 0, j), b4.y * v_get(in, 1, j),
-                       b4.z * v_get(in, 2, j), b4.w * v_get(in, 3, j));
+        } else if (!Ly::COMPACT && rt >= R::NG) {
+            stage_bv(sVT, sB, in, tid);
         }
         __syncthreads();
 
@@ -606,17 +629,34 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         }
         __syncthreads();  // K+ and K- are dead: their LDS becomes A and L
         static_assert(NT * NT <= kIWaves, "one tile of A/P or of the zero upper part per wave");
+        // P (lower, with the zero upper tiles) into its LDS space: here, or,
+        // in the compact layout where P takes A's space, after the inverse
+        auto store_p = [&]() {
+            if (wid >= NPAIR && wid < NT * NT) {
+                int I = 1, rem = wid - NPAIR;
+                while (rem >= I) { rem -= I; ++I; }
+                const int J = rem, col = kTile * I + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sP[(kTile * J + 4 * grp + r) * P_LD + col] = from_f32<T>(0.f);
+            }
+            if (wid < NPAIR) {
+                int I = 0, rem = wid;
+                while (rem > I) { rem -= I + 1; ++I; }
+                const int col = kTile * rem + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = kTile * I + 4 * grp + r;
+                    sP[t * P_LD + col] = from_f32<T>((col <= t) ? accP[r] : 0.f);
+                }
+            }
+        };
         if (wid >= NPAIR && wid < NT * NT) {
-            // tile (row J, column I), J < I, is zero in L and P
+            // tile (row J, column I), J < I, is zero in L (and P)
             int I = 1, rem = wid - NPAIR;
             while (rem >= I) { rem -= I; ++I; }
             const int J = rem, col = kTile * I + l16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = kTile * J + 4 * grp + r;
-                sL[t * A_LD + col] = 0.f;
-                sP[t * P_LD + col] = from_f32<T>(0.f);
-            }
+            for (int r = 0; r < 4; ++r) sL[(kTile * J + 4 * grp + r) * A_LD + col] = 0.f;
         }
         if (wid < NPAIR) {
             int I = 0, rem = wid;
@@ -627,9 +667,10 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int t = kTile * I + 4 * grp + r;
                 sA[t * A_LD + col] = (col < t) ? sB[t] * accA[r] : 0.f;
-                sP[t * P_LD + col] = from_f32<T>((col <= t) ? accP[r] : 0.f);
             }
         }
+        if constexpr (!Ly::COMPACT) store_p();
+        else if (rt >= R::NG && rt < R::NG + R::NV) stage_bv(sVT, sB, in, tid);  // into the K+/K- space
         __syncthreads();
 
         // ---- L = (I + A)^-1 by blocked forward substitution (fp32) on the
@@ -766,6 +807,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 }
             }
         }
+        if constexpr (Ly::COMPACT) store_p();  // A's space: the inverse has read A
         __syncthreads();
 
         // ---- Q' = q e^Gam - P W (as (P W)^T = W^T P^T, four channels of one
@@ -1706,7 +1748,10 @@ void kda_chain_kernel(PrefillArgs a) {
             const int tok0 = tok_start + k * C;
             const int len = active ? min(C, tok_end - tok0) : 0;
             // o rows of this chunk through a buffer resource whose range ends
-            // at row len: stores of rows past the sequence's end are dropped
+            // at row len: stores of rows past the sequence's end are dropped.
+            // The whole byte offset goes in the per-lane (VGPR) offset: the
+            // range check of a raw buffer access covers that offset only, not
+            // the scalar one.
             __amdgpu_buffer_rsrc_t orsrc;
             if (MODE == kFull)
                 orsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<bf16 *>(a.o) + (size_t(tok0) * H + h) * DV + nb,
@@ -1732,8 +1777,7 @@ void kda_chain_kernel(PrefillArgs a) {
                     for (int r = 0; r < 4; ++r) {
                         const bf16 v = static_cast<bf16>(static_cast<float>(cur.oi[I][r]) + oa[r]);
                         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), orsrc,
-                                                              (4 * grp * H * DV + l16) * 2,
-                                                              (kTile * I + r) * H * DV * 2, 0);
+                                                              ((kTile * I + 4 * grp + r) * H * DV + l16) * 2, 0, 0);
                     }
                 }
             }

@@ -61,7 +61,10 @@ enum {
  * and return KDA_ERR_DECAY_BOUND (launching nothing else) if any g is
  * outside [-5, 0] or NaN.  For a packed batch it also checks that cu_seqlens
  * starts at 0, never decreases and ends at T (KDA_ERR_SHAPE otherwise).
- * This breaks the no-host-sync rule on purpose. */
+ * This breaks the no-host-sync rule on purpose.  A checked prefill keeps its
+ * result word in its own workspace; the checked decode calls (and a prefill
+ * with no sequences) share one word per device, so two of those in flight
+ * at once on different streams may report each other's result. */
 #define KDA_FLAG_CHECK_DECAY 1u
 /* Prefill: keep one state chain per (sequence, head) even when the sizes
  * would split long sequences into segments computed in parallel (the

@@ -1,24 +1,30 @@
 """Shared helpers for the parity tests: run the HIP path and the oracle on the
-same seeded inputs and compare with relative L2."""
+same seeded inputs and compare with relative L2, over the whole tensors and
+over every (sequence, head) block on its own."""
 import numpy as np
 import torch
 
 import oracle
 import workloads
-from helpers import TOL_BF16, TOL_FP32, rel_l2
+from helpers import TOL_BF16, TOL_FP32, rel_l2, rel_l2_per_seq_head, rel_l2_per_state, worst
 
 
 def tol_for(dtype_name):
     return TOL_FP32 if dtype_name == "fp32" else TOL_BF16
 
 
+def seq_offsets(x):
+    """Sequence offsets [N+1] into the packed rows of a prefill batch."""
+    B, T = x["q"].shape[:2]
+    return (x["cu_seqlens"].cpu().numpy().astype(np.int64) if x["cu_seqlens"] is not None
+            else np.arange(B + 1, dtype=np.int64) * T)
+
+
 def packed_view(x):
     """(q, k, v, g, beta, cu) as packed [rows, H, d] float32 numpy arrays."""
     B, T = x["q"].shape[:2]
     f = lambda t: workloads.to_numpy_f32(t).reshape((B * T,) + tuple(t.shape[2:]))
-    cu = (x["cu_seqlens"].cpu().numpy().astype(np.int64) if x["cu_seqlens"] is not None
-          else np.arange(B + 1, dtype=np.int64) * T)
-    return f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(x["beta"]), cu
+    return f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(x["beta"]), seq_offsets(x)
 
 
 def oracle_prefill(x, seqs=None):
@@ -48,19 +54,32 @@ def to_np64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def check_prefill(spec, chunk=None, label=""):
-    """GPU vs oracle on the whole output and final state; returns the errors."""
+def gate(o, o_ref, ht, ht_ref, cu, tol, what=""):
+    """Whole-tensor and per-(sequence, head) rel-L2 of o [rows, H, dv] and ht
+    [N, H, dk, dv] against the oracle; asserts every figure <= tol and
+    returns (o, ht, worst o block, worst ht block)."""
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht)), f"{what}: non-finite output"
+    eo, eh = rel_l2(o, o_ref), rel_l2(ht, ht_ref)
+    wo = worst(rel_l2_per_seq_head(o, o_ref, cu))
+    wh = worst(rel_l2_per_state(ht, ht_ref))
+    print(f"[parity]   {what} rel-L2 o={eo:.3e} ht={eh:.3e}; worst (sequence, head) o={wo:.3e} "
+          f"ht={wh:.3e} (tol {tol:g})", flush=True)
+    assert eo <= tol, f"o rel-L2 {eo:.3e} > {tol}"
+    assert eh <= tol, f"ht rel-L2 {eh:.3e} > {tol}"
+    assert wo <= tol, f"worst (sequence, head) o rel-L2 {wo:.3e} > {tol}"
+    assert wh <= tol, f"worst (sequence, head) ht rel-L2 {wh:.3e} > {tol}"
+    return eo, eh, wo, wh
+
+
+def check_prefill(spec, chunk=None, label="", **kw):
+    """GPU vs oracle on the whole output and final state and on every
+    (sequence, head) block; returns the four errors."""
     x = workloads.make_prefill(spec)
     chunk = chunk or spec.chunk
     print(f"[parity] {label or spec} chunk={chunk}", flush=True)
-    o, ht = gpu_prefill(x, chunk)
+    o, ht = gpu_prefill(x, chunk, **kw)
     o_ref, ht_ref = oracle_prefill(x)
     B, T = x["q"].shape[:2]
-    eo = rel_l2(to_np64(o).reshape(o_ref.shape), o_ref)
-    eh = rel_l2(to_np64(ht), ht_ref)
-    tol = tol_for(spec.dtype)
-    print(f"[parity]   rel-L2 o={eo:.3e} ht={eh:.3e} (tol {tol:g})", flush=True)
-    assert np.all(np.isfinite(to_np64(o))) and np.all(np.isfinite(to_np64(ht)))
-    assert eo <= tol, f"o rel-L2 {eo:.3e} > {tol}"
-    assert eh <= tol, f"ht rel-L2 {eh:.3e} > {tol}"
-    return eo, eh
+    o_ref = o_ref.reshape((B * T,) + o_ref.shape[-2:])
+    return gate(to_np64(o).reshape(o_ref.shape), o_ref, to_np64(ht), ht_ref, seq_offsets(x), tol_for(spec.dtype),
+                label)

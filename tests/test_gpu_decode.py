@@ -66,11 +66,11 @@ def test_decode_single_sequence_head():
         assert eo <= TOL_FP32 and es <= TOL_FP32
 
 
-def test_decode_headline_batch_sampled_steps():
-    """The 256-sequence x 32-head decode batch, 8 consecutive steps, every
-    output and the whole state checked."""
+def test_decode_headline_batch_all_steps():
+    """The 256-sequence x 32-head decode batch, all 128 consecutive in-place
+    steps, every output of every step and the whole final state checked."""
     spec = workloads.DECODE
-    eo, es = _run(spec, 8)
+    eo, es = _run(spec, spec.steps)
     print(f"[decode] headline: o {eo:.2e} state {es:.2e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16
 

@@ -2,7 +2,8 @@
 
 Inputs follow the workload recipe (workloads/); the oracle consumes the exact
 bf16 / fp32 values the GPU sees.  Gates: relative L2 <= 1e-4 (fp32 inputs),
-<= 2e-2 (bf16 inputs with fp32 accumulation), on o and on the final state.
+<= 2e-2 (bf16 inputs with fp32 accumulation), on o and on the final state,
+over the whole tensors and over every (sequence, head) block on its own.
 Stress variants (slow decay, state isolation, g at the -5 floor, no decay)
 run because at the configs' own decay the state remembers only a few
 tokens, so a broken inter-chunk carry would otherwise pass.
@@ -140,67 +141,3 @@ def test_prefill_equals_decode_steps():
     od = torch.stack(outs, dim=1)
     assert rel_l2(to_np64(od), to_np64(o)) <= TOL_BF16
     assert rel_l2(to_np64(state), to_np64(ht)) <= TOL_BF16
-
-
-def test_headline_config_full_size():
-    """The headline workload at full size (B=1, H=32, T=8192, d=128, bf16,
-    chunk 64, h0 ~ N(0, 0.02)) against the oracle on every output."""
-    check_prefill(workloads.PREFILL_H32_T8K, label="headline prefill H=32 T=8192")
-
-
-def _sample_sequences(x, seqs):
-    """GPU output rows and final states of some packed sequences."""
-    cu = x["cu_seqlens"].cpu().numpy()
-    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in seqs])
-    return rows
-
-
-@pytest.mark.parametrize("mode,h0_std", [("config", 0.02), ("slow", 1.0)])
-def test_varlen_full_size_sampled(mode, h0_std):
-    """The packed workload at full size (64 sequences of U[256, 4096] tokens,
-    H=16, d=128, bf16, per-sequence h0, chunk 64); the oracle checks seven
-    whole sequences (first, last, shortest, longest and three others)."""
-    spec = workloads.VARLEN_64_SEQS.replace(g_mode=mode, h0_std=h0_std)
-    x = workloads.make_prefill(spec)
-    print(f"[parity] varlen full size g={mode}: T={spec.total_tokens}", flush=True)
-    o, ht = gpu_prefill(x, 64)
-    lens = np.array(spec.seqlens)
-    seqs = sorted({0, 63, int(lens.argmin()), int(lens.argmax()), 17, 31, 48})
-    o_ref, ht_ref = oracle_prefill(x, seqs)
-    rows = _sample_sequences(x, seqs)
-    o_gpu = to_np64(o)[0][rows]
-    eo = rel_l2(o_gpu, o_ref)
-    eh = rel_l2(to_np64(ht)[seqs], ht_ref)
-    print(f"[parity]   rel-L2 o={eo:.3e} ht={eh:.3e}", flush=True)
-    assert eo <= TOL_BF16 and eh <= TOL_BF16
-
-
-def test_long_context_full_size_sampled():
-    """1M tokens x 8 heads, d=128, bf16, slow decay (long memory), chunk 64:
-    the whole sequence runs on the GPU.  The oracle recomputes the first
-    131,072 tokens of two heads (outputs there depend only on that prefix);
-    the final state of the full sequence must agree between chunk 16 and
-    chunk 64 (a property at any size) and be finite."""
-    import gated_delta_rule_97_amd as kda
-    spec = workloads.LONG_CONTEXT_1M.replace(g_mode="slow")
-    dev = torch.device("cuda")
-    print("[parity] 1M tokens: generating on the GPU", flush=True)
-    x = workloads.make_prefill(spec, device=dev)
-    o, ht = kda.chunk_prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], None, chunk_size=64)
-    torch.cuda.synchronize()
-    assert torch.isfinite(ht).all() and torch.isfinite(o.float()).all()
-    Tp = 1 << 17
-    heads = [0, 5]
-    f = lambda t: t[0, :Tp, heads].float().cpu().numpy()
-    print("[parity] 1M tokens: oracle on the prefix of two heads", flush=True)
-    import oracle
-    o_ref, _ = oracle.prefill(f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]),
-                              x["beta"][0, :Tp, heads].cpu().numpy(), None)
-    eo = rel_l2(o[0, :Tp, heads].double().cpu().numpy(), o_ref)
-    print(f"[parity]   prefix rel-L2 o={eo:.3e}", flush=True)
-    assert eo <= TOL_BF16
-    o16, ht16 = kda.chunk_prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], None, chunk_size=16)
-    torch.cuda.synchronize()
-    e16 = rel_l2(to_np64(ht16), to_np64(ht))
-    print(f"[parity]   chunk 16 vs 64 final state rel-L2={e16:.3e}", flush=True)
-    assert e16 <= TOL_BF16

@@ -68,7 +68,6 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
 bool prefill_supported(int dtype, int dk, int dv, int C) {
     auto okd = [](int d) { return d == 32 || d == 64 || d == 128; };
     if (!okd(dk) || !okd(dv) || (C != 16 && C != 64)) return false;
-    if (dtype == KDA_DTYPE_F32 && C == 64 && (dk > 64 || dv > 64)) return false;
     return dtype == KDA_DTYPE_F32 || dtype == KDA_DTYPE_BF16;
 }
 

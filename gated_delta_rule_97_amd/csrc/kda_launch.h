@@ -104,8 +104,7 @@ hipError_t run_checks(const float *g, size_t n, const int32_t *cu, int N,
                       int T, unsigned *flag_dev, hipStream_t s,
                       unsigned *flag_out);
 
-// Whether a dtype / size combination has kernels built (fp32 with chunk 64
-// needs dk, dv <= 64 to fit the intra-chunk kernel in LDS).
+// Whether a dtype / size combination has kernels built.
 bool prefill_supported(int dtype, int dk, int dv, int C);
 
 }  // namespace kda

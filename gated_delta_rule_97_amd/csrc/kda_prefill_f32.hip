@@ -1,5 +1,5 @@
-// fp32 instances of the chunked prefill kernels.  With chunk 64 the
-// intra-chunk kernel's fp32 operands fit in LDS only for dk, dv <= 64.
+// fp32 instances of the chunked prefill kernels.  With chunk 64 and dk or
+// dv = 128 the intra-chunk kernel takes its compact LDS placement.
 #include "kda_prefill_impl.h"
 
 namespace kda {
@@ -18,7 +18,9 @@ hipError_t launch_prefill_f32(const PrefillArgs &a, int dk, int dv, int C, int b
     KDA_PF16(32, 32) KDA_PF16(32, 64) KDA_PF16(32, 128)
     KDA_PF16(64, 32) KDA_PF16(64, 64) KDA_PF16(64, 128)
     KDA_PF16(128, 32) KDA_PF16(128, 64) KDA_PF16(128, 128)
-    KDA_PF64(32, 32) KDA_PF64(32, 64) KDA_PF64(64, 32) KDA_PF64(64, 64)
+    KDA_PF64(32, 32) KDA_PF64(32, 64) KDA_PF64(32, 128)
+    KDA_PF64(64, 32) KDA_PF64(64, 64) KDA_PF64(64, 128)
+    KDA_PF64(128, 32) KDA_PF64(128, 64) KDA_PF64(128, 128)
 #undef KDA_PF16
 #undef KDA_PF64
     return hipErrorInvalidValue;

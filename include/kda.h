@@ -99,7 +99,7 @@ int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv,
  *              never an out-of-bounds access (checked with the flag above).
  *   num_seqs   N (B when cu_seqlens is NULL)
  *   chunk_size 16 or 64 (a multiple of the 16-token tile); results are the
- *              same up to rounding.  float32 with chunk 64 needs dk, dv <= 64.
+ *              same up to rounding.
  *   o          [B, T, H, dv]  dtype, written
  *   ht         [N, H, dk, dv] float32 final state per sequence, or NULL.
  *              ht may be exactly h0 (in-place resume); partial overlap of ht

@@ -54,24 +54,26 @@ def to_np64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def gate(o, o_ref, ht, ht_ref, cu, tol, what=""):
+def gate(o, o_ref, ht, ht_ref, cu, tol, what="", block_tol=None):
     """Whole-tensor and per-(sequence, head) rel-L2 of o [rows, H, dv] and ht
-    [N, H, dk, dv] against the oracle; asserts every figure <= tol and
-    returns (o, ht, worst o block, worst ht block)."""
+    [N, H, dk, dv] against the oracle; asserts the whole-tensor figures <=
+    tol and every block's <= block_tol (tol unless a case states a looser
+    one), and returns (o, ht, worst o block, worst ht block)."""
+    block_tol = tol if block_tol is None else block_tol
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht)), f"{what}: non-finite output"
     eo, eh = rel_l2(o, o_ref), rel_l2(ht, ht_ref)
     wo = worst(rel_l2_per_seq_head(o, o_ref, cu))
     wh = worst(rel_l2_per_state(ht, ht_ref))
     print(f"[parity]   {what} rel-L2 o={eo:.3e} ht={eh:.3e}; worst (sequence, head) o={wo:.3e} "
-          f"ht={wh:.3e} (tol {tol:g})", flush=True)
+          f"ht={wh:.3e} (tol {tol:g}, per block {block_tol:g})", flush=True)
     assert eo <= tol, f"o rel-L2 {eo:.3e} > {tol}"
     assert eh <= tol, f"ht rel-L2 {eh:.3e} > {tol}"
-    assert wo <= tol, f"worst (sequence, head) o rel-L2 {wo:.3e} > {tol}"
-    assert wh <= tol, f"worst (sequence, head) ht rel-L2 {wh:.3e} > {tol}"
+    assert wo <= block_tol, f"worst (sequence, head) o rel-L2 {wo:.3e} > {block_tol}"
+    assert wh <= block_tol, f"worst (sequence, head) ht rel-L2 {wh:.3e} > {block_tol}"
     return eo, eh, wo, wh
 
 
-def check_prefill(spec, chunk=None, label="", **kw):
+def check_prefill(spec, chunk=None, label="", block_tol=None, **kw):
     """GPU vs oracle on the whole output and final state and on every
     (sequence, head) block; returns the four errors."""
     x = workloads.make_prefill(spec)
@@ -82,4 +84,4 @@ def check_prefill(spec, chunk=None, label="", **kw):
     B, T = x["q"].shape[:2]
     o_ref = o_ref.reshape((B * T,) + o_ref.shape[-2:])
     return gate(to_np64(o).reshape(o_ref.shape), o_ref, to_np64(ht), ht_ref, seq_offsets(x), tol_for(spec.dtype),
-                label)
+                label, block_tol)

@@ -47,9 +47,16 @@ def test_headline_shape_state_isolation():
     128 chunks of every head.  With no decay, so that the final state stays
     inside fp32's range: the erase steps alone shrink h0's share to about
     1e-10 over 8192 tokens, while slow decay would take it to ~e^-164, which
-    underflows (the oracle's fp64 keeps it, the GPU's fp32 state cannot)."""
+    underflows (the oracle's fp64 keeps it, the GPU's fp32 state cannot).
+
+    The whole tensors keep the 2e-2 gate.  Each head's final state is gated
+    at a stated 3e-2: in this pure carry every chunk rounds the carried
+    state and U to bf16 for its products (relative 2^-9 each) and nothing
+    decays the earlier roundings away, so they add up like a random walk
+    over the 128 chunks, about sqrt(128) * 2^-9 ~ 2e-2, and single heads
+    scatter around that (measured: whole 1.7e-2, worst head 2.1e-2)."""
     spec = workloads.PREFILL_H32_T8K.replace(g_mode="zero", h0_std=1.0, v_zero=True, seed=102)
-    check_prefill(spec, label="headline shape, state isolation")
+    check_prefill(spec, label="headline shape, state isolation", block_tol=3e-2)
 
 
 @pytest.mark.parametrize("mode,h0_std", [("config", 0.02), ("slow", 1.0)])

@@ -35,8 +35,11 @@ def test_bf16_shapes_ragged(dk, dv, chunk):
 
 
 @pytest.mark.parametrize("dk,dv,chunk", [(32, 32, 64), (64, 64, 64), (64, 32, 16), (128, 128, 16),
-                                         (32, 128, 16)])
+                                         (32, 128, 16), (128, 128, 64), (128, 64, 64), (64, 128, 64),
+                                         (128, 32, 64)])
 def test_fp32_shapes(dk, dv, chunk):
+    """fp32 at the 1e-4 gate; chunk 64 with dk or dv = 128 takes the
+    intra-chunk kernel's compact LDS placement."""
     spec = Spec(H=2, dk=dk, dv=dv, T=150, B=2, dtype="fp32", chunk=chunk, h0_std=1.0, g_mode="slow",
                 seed=32)
     check_prefill(spec, label=f"fp32 dk={dk} dv={dv}")
@@ -141,3 +144,13 @@ def test_prefill_equals_decode_steps():
     od = torch.stack(outs, dim=1)
     assert rel_l2(to_np64(od), to_np64(o)) <= TOL_BF16
     assert rel_l2(to_np64(state), to_np64(ht)) <= TOL_BF16
+
+
+def test_fp32_chunk64_d128_packed_and_decay_floor():
+    """fp32, d = 128, chunk 64 on packed sequences (empty, one-token and
+    ragged) and at the decay bound itself (g = -5: the e^80 column operand)."""
+    spec = Spec(H=2, dk=128, dv=128, seqlens=(70, 0, 1, 129, 64), dtype="fp32", chunk=64, h0_std=1.0,
+                g_mode="slow", seed=42)
+    check_prefill(spec, label="fp32 d128 chunk 64 packed")
+    spec = Spec(H=2, dk=128, dv=128, T=333, dtype="fp32", chunk=64, h0_std=1.0, g_mode="floor", seed=43)
+    check_prefill(spec, label="fp32 d128 chunk 64 g=-5")

@@ -36,6 +36,8 @@ CASES = [
                                   g_mode="slow", seed=72), 64),
     ("fp32 chunk16", Spec(H=2, dk=32, dv=32, T=2048, B=1, dtype="fp32", chunk=16, h0_std=1.0, g_mode="slow",
                           seed=73), 16),
+    ("fp32 d128 chunk64", Spec(H=1, dk=128, dv=128, T=64 * 64 + 21, B=1, dtype="fp32", chunk=64, h0_std=1.0,
+                               g_mode="zero", seed=84), 64),
     ("bf16 no decay", Spec(H=1, dk=128, dv=64, T=4096, B=1, dtype="bf16", chunk=64, h0_std=1.0, g_mode="zero",
                            seed=74), 64),
     ("bf16 decay floor", Spec(H=1, dk=128, dv=128, T=4096, B=1, dtype="bf16", chunk=64, h0_std=1.0,

@@ -5,7 +5,7 @@ kernels behind the C ABI declared in ``include/kda.h``.  PyTorch supplies
 device memory and the current stream; nothing here computes KDA.
 
 Low-level functions carry the C names (``kda_chunk_prefill``,
-``kda_decode_step``, ``kda_chunk_prefill_workspace_size``,
+``kda_chunk_prefill_noalloc``, ``kda_decode_step``, ``kda_chunk_prefill_workspace_size``,
 ``kda_status_string``, ``kda_profile_start``, ``kda_profile_stop``) and take
 raw integer device addresses.  ``chunk_prefill`` and ``decode_step`` wrap
 them for torch tensors.
@@ -45,6 +45,8 @@ KDA_ERR_ALIGN = -5
 KDA_ERR_ALIAS = -6
 KDA_ERR_LAUNCH = -7
 KDA_ERR_DECAY_BOUND = -8
+KDA_ERR_TOO_LARGE = -9
+NOALLOC_SCRATCH_BYTES = 128 << 20
 KDA_FLAG_CHECK_DECAY = 1
 KDA_FLAG_NO_SEGMENTS = 2
 KDA_DTYPE_F32 = 0
@@ -62,6 +64,9 @@ _lib.kda_chunk_prefill_workspace_size.restype = _i
 _lib.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _u,
                                    _vp, _vp, _vp, _sz, _vp]
 _lib.kda_chunk_prefill.restype = _i
+_lib.kda_chunk_prefill_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _u,
+                                           _vp, _vp, _vp]
+_lib.kda_chunk_prefill_noalloc.restype = _i
 _lib.kda_chunk_prefill_checkpointed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                                 _i, _u, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
 _lib.kda_chunk_prefill_checkpointed.restype = _i
@@ -105,6 +110,14 @@ def kda_chunk_prefill(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seq
     return _lib.kda_chunk_prefill(q or None, k or None, v or None, g or None, beta or None, h0 or None,
                                   cu_seqlens or None, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags,
                                   o or None, ht or None, workspace or None, workspace_bytes, stream or None)
+
+
+def kda_chunk_prefill_noalloc(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size, dtype,
+                              flags, o, ht, stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_chunk_prefill_noalloc(q or None, k or None, v or None, g or None, beta or None, h0 or None,
+                                          cu_seqlens or None, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags,
+                                          o or None, ht or None, stream or None)
 
 
 def kda_chunk_prefill_checkpointed(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size,

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -124,6 +125,35 @@ static bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 static size_t dtype_bytes(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
 
+// ---------------------------------------------------------------------------
+// Scratch of kda_chunk_prefill_noalloc: a static device array, one copy per
+// GPU, held until the process ends.  In host code its name is only a
+// host-side stand-in: the device address of each GPU's copy is looked up
+// once per device (with that device current) and used everywhere instead.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// This device's copy of the scratch array (status KDA_OK), looked up on the
+// first call made with the device current.
+static int device_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KDA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
 extern "C" {
 
 const char *kda_status_string(int status) {
@@ -137,6 +167,7 @@ const char *kda_status_string(int status) {
     case KDA_ERR_ALIAS: return "buffers overlap in a way that is not allowed";
     case KDA_ERR_LAUNCH: return "the HIP runtime reported an error";
     case KDA_ERR_DECAY_BOUND: return "a log-decay value is outside [-5, 0]";
+    case KDA_ERR_TOO_LARGE: return "the sizes need more scratch than the static buffer holds";
     default: return "unknown status";
     }
 }
@@ -342,6 +373,28 @@ int kda_chunk_prefill_checkpointed(const void *q, const void *k, const void *v, 
     if (num_ckpt > 0 && !ckpt) return KDA_ERR_NULL;
     return prefill_impl(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags, o,
                         ht, workspace, workspace_bytes, stream, CkptReq{ckpt, ckpt_stride, num_ckpt});
+}
+
+int kda_chunk_prefill_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                              const float *h0, const int32_t *cu_seqlens, int B, int T, int H, int dk, int dv,
+                              int num_seqs, int chunk_size, kda_dtype dtype, unsigned flags, void *o, float *ht,
+                              hipStream_t stream) {
+    // the shape errors of kda_chunk_prefill first, then the scratch limit,
+    // both before the device is touched
+    int nc_max = 0, N = 0;
+    int st = prefill_shape(B, T, H, dk, dv, num_seqs, chunk_size, dtype, cu_seqlens != nullptr, &nc_max, &N);
+    if (st != KDA_OK) return st;
+    size_t need = 0;
+    st = kda_chunk_prefill_workspace_size(B, T, H, dk, dv, num_seqs, chunk_size, dtype, &need);
+    if (st != KDA_OK) return st;
+    if (need > size_t(KDA_NOALLOC_SCRATCH_BYTES)) return KDA_ERR_TOO_LARGE;
+    void *ws = nullptr;
+    st = device_scratch(&ws);
+    if (st != KDA_OK) return st;
+    // nothing in the scratch needs to start at zero: every word a kernel
+    // reads there is written earlier in the same call
+    return prefill_impl(q, k, v, g, beta, h0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size, dtype, flags, o,
+                        ht, ws, size_t(KDA_NOALLOC_SCRATCH_BYTES), stream, CkptReq{nullptr, 0, 0});
 }
 
 int kda_decode_step(const void *q, const void *k, const void *v, const float *g, const float *beta,

@@ -54,7 +54,9 @@ enum {
     KDA_ERR_ALIGN = -5,       /* a pointer is not suitably aligned              */
     KDA_ERR_ALIAS = -6,       /* buffers overlap in a way that is not allowed   */
     KDA_ERR_LAUNCH = -7,      /* the HIP runtime reported an error              */
-    KDA_ERR_DECAY_BOUND = -8  /* KDA_FLAG_CHECK_DECAY found g outside [-5, 0]   */
+    KDA_ERR_DECAY_BOUND = -8, /* KDA_FLAG_CHECK_DECAY found g outside [-5, 0]   */
+    KDA_ERR_TOO_LARGE = -9    /* kda_chunk_prefill_noalloc: the sizes need more
+                                 scratch than its static buffer holds          */
 };
 
 /* Debug flag: before computing, scan g on the device, synchronize the stream
@@ -117,6 +119,29 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v,
                       int dv, int num_seqs, int chunk_size, kda_dtype dtype,
                       unsigned flags, void *o, float *ht, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace.  The library keeps the
+ * scratch in a static device array of KDA_NOALLOC_SCRATCH_BYTES (128 MiB)
+ * that every GPU it runs on holds until the process ends; the call itself
+ * allocates nothing.  Sizes whose workspace (kda_chunk_prefill_workspace_size)
+ * exceeds it return KDA_ERR_TOO_LARGE before anything is enqueued; at d = 128
+ * and chunk 64 that is about 1,600 (chunk, head) slots, e.g. 2048 tokens x 32
+ * heads.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (different streams or host threads) race and give
+ * undefined results.  Nothing in the array needs to start at zero.  Every
+ * other argument, error and result is that of kda_chunk_prefill.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int kda_chunk_prefill_noalloc(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta,
+                              const float *h0, const int32_t *cu_seqlens,
+                              int B, int T, int H, int dk, int dv,
+                              int num_seqs, int chunk_size, kda_dtype dtype,
+                              unsigned flags, void *o, float *ht,
+                              hipStream_t stream);
 
 /*
  * kda_chunk_prefill that also writes strided state checkpoints, for a

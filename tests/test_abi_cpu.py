@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = kda.kda_status_string(code)
         assert s and s != "unknown status"
     assert kda.kda_status_string(-99) == "unknown status"
@@ -223,3 +223,33 @@ def test_verify_commit_empty():
     assert _verify(N=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
     assert _verify(K=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
     assert _commit(N=0, k=0, v=0, g=0, beta=0, n_accept=0, state=0) == kda.KDA_OK
+
+
+def _noalloc(**kw):
+    args = dict(q=A, k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24), h0=0,
+                cu_seqlens=0, B=1, T=64, H=2, dk=32, dv=32, num_seqs=1, chunk_size=16, dtype=F32,
+                flags=0, o=A + (5 << 24), ht=A + (6 << 24), stream=0)
+    args.update(kw)
+    return kda.kda_chunk_prefill_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk_size=32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(H=0), kda.KDA_ERR_SHAPE),
+    (dict(num_seqs=2), kda.KDA_ERR_SHAPE),
+    # the headline prefill (H=32, T=8192, d=128) needs ~340 MB of workspace
+    (dict(T=8192, H=32, dk=128, dv=128, chunk_size=64, dtype=BF16), kda.KDA_ERR_TOO_LARGE),
+    (dict(B=4, num_seqs=4, T=4096, H=16, dk=128, dv=128, chunk_size=64, dtype=BF16), kda.KDA_ERR_TOO_LARGE),
+])
+def test_noalloc_validation(kw, status):
+    """Shape errors and sizes beyond the static scratch are refused on the
+    host, before the device (or its scratch array) is touched."""
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_limit_matches_the_workspace_size():
+    lim = kda.NOALLOC_SCRATCH_BYTES
+    assert kda.kda_chunk_prefill_workspace_size(1, 2048, 32, 128, 128, 1, 64, BF16) <= lim
+    assert kda.kda_chunk_prefill_workspace_size(1, 4096, 32, 128, 128, 1, 64, BF16) > lim
+

@@ -40,7 +40,15 @@
 extern "C" {
 #endif
 
+/* The element type of q, k, v and o.  Any int may arrive here from a C
+ * caller; C++ gets the enumeration a fixed int underlying type, so every
+ * such value is a valid kda_dtype there and the library's check of it
+ * (KDA_ERR_UNSUPPORTED) is well defined.  Either way the type is an int. */
+#ifdef __cplusplus
+typedef enum kda_dtype : int {
+#else
 typedef enum kda_dtype {
+#endif
     KDA_DTYPE_F32 = 0,  /* IEEE float32 */
     KDA_DTYPE_BF16 = 1  /* bfloat16 (outputs rounded to nearest even) */
 } kda_dtype;

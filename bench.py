@@ -121,7 +121,7 @@ def ingest_pmc(fetch_dir, write_dir):
                 key = ("kda_intra" if "kda_intra_kernel" in name
                        else "kda_inter" if ("kda_inter_kernel" in name or "kda_inter_ws_kernel" in name)
                        else "kda_decode" if "kda_decode_kernel" in name
-                       else "kda_decode_verify" if "kda_decode_multi_kernel" in name
+                       else "kda_decode_verify" if "kda_decode_wave_kernel" in name
                        else "copy" if "copy" in name.lower() and float(r["Counter_Value"]) > 0 else None)
                 if key:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))

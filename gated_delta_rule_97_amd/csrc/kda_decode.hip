@@ -117,135 +117,213 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
 // (speculative decoding, serving-stack section of the blog post: drafted
 // tokens are checked against the committed state, then the accepted ones
 // are committed).  Inputs are [N][K][H][d] (token t of sequence n at row
-// n * K + t).  VERIFY: all K tokens, o written per token, the state only
-// read.  COMMIT: the first n_accept[n] (clamped to [0, K]) tokens of
+// n * K + t).  kVerify: all K tokens, o written per token, the state only
+// read.  kCommit: the first n_accept[n] (clamped to [0, K]) tokens of
 // sequence n, no o, the state written back once (not at all when zero
-// tokens are accepted).  Same per-token arithmetic as kda_decode_kernel.
+// tokens are accepted).  kStep: one token, o and the state (a decode step).
+//
+// Every value column of the state evolves on its own: w = S'^T k, u, the
+// update k u^T and o = S^T q are all per column, and only k, q, e^g and beta
+// are shared.  So one wavefront holds CW value columns x all DK rows of one
+// (sequence, head) and needs no other wave: each lane owns RPT consecutive
+// rows of one float4 of columns, and the reductions over dk sum a lane's
+// rows and then its row groups by xor shuffles.  No LDS, no barrier.
 // ---------------------------------------------------------------------------
-template <class T, int DK, int DV, int CPB, bool VERIFY>
-__global__ __launch_bounds__(256) void kda_decode_multi_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                                 const T *__restrict__ v, const float *__restrict__ g,
-                                                                 const float *__restrict__ beta,
-                                                                 const int32_t *__restrict__ n_accept,
-                                                                 float *__restrict__ state, T *__restrict__ o, int K,
-                                                                 int H) {
-    constexpr int CG = CPB / 4;   // float4 column groups of this workgroup's CPB value columns
-    constexpr int RG = 256 / CG;
-    constexpr int RPT = DK / RG;
-    constexpr int KG = 8;  // draft tokens staged in LDS at once
-    static_assert(DV % CPB == 0, "column blocks");
-    static_assert(RG * CG == 256 && RPT * RG == DK, "decode thread split");
-    // a group's k, q and e^g, and the row-group partials of two tokens in turn
-    __shared__ float sk[KG][DK], sq[VERIFY ? KG : 1][DK], sd[KG][DK];
-    __shared__ float4 sw[2][RG][CG], sy[VERIFY ? 2 : 1][RG][CG];
-    __shared__ float skq[KG];
+enum DecodeMode { kVerify = 0, kCommit = 1, kStep = 2 };
 
-    // the value columns of S are independent: (sequence, head) spans DV / CPB
-    // workgroups, each the state's columns cb * CPB ..
-    const int ch = blockIdx.x / (DV / CPB), cb = blockIdx.x % (DV / CPB);  // ch = sequence * H + head
+template <int DV>
+constexpr int wave_columns() { return DV < 32 ? DV : 32; }
+
+// R consecutive values of T (R a multiple of 4, p aligned to 4 values)
+template <int R>
+__device__ __forceinline__ void load_vec(const bf16 *p, float (&x)[R]) {
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p + i);
+        x[i] = static_cast<float>(v[0]); x[i + 1] = static_cast<float>(v[1]);
+        x[i + 2] = static_cast<float>(v[2]); x[i + 3] = static_cast<float>(v[3]);
+    }
+}
+template <int R>
+__device__ __forceinline__ void load_vec(const float *p, float (&x)[R]) {
+#pragma unroll
+    for (int i = 0; i < R; i += 4) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(p + i);
+        x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
+    }
+}
+
+// Per-token vectors of a group of KG tokens are staged once per wave in the
+// wave's own LDS region (one 16-byte unit per lane and load, e^g taken once
+// per element) and each lane reads its rows from there: read by every lane
+// straight from memory they would cost one load per 16-byte unit per lane,
+// and eight lanes share each row group.  The region belongs to one wave, and
+// a wave's LDS accesses complete in order, so no barrier is needed.
+constexpr int kWaveKG = 4;   // tokens staged at once
+constexpr int kWavePB = 4;   // waves per workgroup
+
+template <int DK>
+__device__ __forceinline__ int wave_vec_idx(int c) { return c + (c >> 4) * 4; }  // 4-float pad per 16: row groups hit distinct banks
+
+template <class T, int DK, int DV, int MODE>
+__global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, const int32_t *__restrict__ n_accept, float *__restrict__ state,
+    T *__restrict__ o, int K, int H, int nwaves) {
+    constexpr int CW = wave_columns<DV>();  // value columns of one wave
+    constexpr int CG = CW / 4;              // float4 column groups: lanes cg = lane % CG
+    constexpr int RG = kWave / CG;          // row groups: lanes rg = lane / CG
+    constexpr int RPT = DK / RG;            // consecutive rows per lane
+    constexpr int NB = DV / CW;             // waves per (sequence, head)
+    constexpr bool OUT = MODE != kCommit, WRITE = MODE != kVerify;
+    static_assert(CG * RG == kWave && RPT * RG == DK && RPT % 4 == 0 && DV % CW == 0, "decode wave split");
+    constexpr int NVEC = OUT ? 3 : 2;                   // staged per token: k, e^g (, q), as fp32
+    constexpr int DKP = DK + DK / 4;                    // padded row of one vector
+    constexpr int EPU = 16 / int(sizeof(T));            // values of T per 16-byte unit
+    constexpr int KU = DK / EPU, GU = DK / 4;           // 16-byte units of k (and q), of g
+    constexpr int UT = KU * (OUT ? 2 : 1) + GU;         // units per token
+    constexpr int ITER = (kWaveKG * UT + kWave - 1) / kWave;
+    __shared__ __align__(16) float sv[kWavePB][kWaveKG][NVEC][DKP];
+
+    const int wv = blockIdx.x * kWavePB + int(threadIdx.x / kWave);
+    if (wv >= nwaves) return;  // no barrier anywhere: a wave past the end simply leaves
+    const int ch = wv / NB, cb = wv - ch * NB;  // ch = sequence * H + head
     const int n = ch / H, h = ch - n * H;
-    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
-    const int col0 = cb * CPB;
+    const int lane = threadIdx.x & (kWave - 1), cg = lane % CG, rg = lane / CG;
+    const int r0 = rg * RPT, col = cb * CW + 4 * cg;
+    float(*my)[NVEC][DKP] = sv[threadIdx.x / kWave];
     int ntok = K;
-    if (!VERIFY) {
+    if (MODE == kCommit) {
         const int na = n_accept[n];
         ntok = na < 0 ? 0 : (na > K ? K : na);
         if (ntok == 0) return;  // nothing accepted: the state stays as it is
     }
-    float *S = state + size_t(ch) * DK * DV + col0;
+    float *S = state + size_t(ch) * DK * DV + col;
 
     floatx4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(r0 + i) * DV));
 
-    for (int t0 = 0; t0 < ntok; t0 += KG) {
-        const int nt = min(KG, ntok - t0);
-        __syncthreads();  // the previous group's last reads of sk/sq/sd are done
-        for (int i = tid; i < nt * DK; i += 256) {
-            const int t = i / DK, c = i - t * DK;
-            const size_t row = (size_t(n) * K + t0 + t) * H + h;  // token row of [N][K][H]
-            sk[t][c] = to_f32(k[row * DK + c]);
-            if (VERIFY) sq[t][c] = to_f32(q[row * DK + c]);
-            sd[t][c] = exp_e(g[row * DK + c]);
-        }
-        __syncthreads();
-        if (VERIFY) {  // k . q of each token: one wave per token
-            for (int t = tid >> 6; t < nt; t += 4) {
-                float p = 0.f;
-                for (int c = tid & 63; c < DK; c += 64) p += sk[t][c] * sq[t][c];
+    for (int t0 = 0; t0 < ntok; t0 += kWaveKG) {
+        const int nt = min(kWaveKG, ntok - t0);
+        // ---- stage the group's k, e^g (and q): unit j of token tt ----
+        u32x4 raw[ITER];
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-                if ((tid & 63) == 0) skq[t] = p;
-            }
+        for (int it = 0; it < ITER; ++it) {
+            const int u = min(lane + kWave * it, nt * UT - 1);  // past the group: a repeated (unused) load
+            const int tt = u / UT, j = u - tt * UT;
+            const size_t row = (size_t(n) * K + t0 + tt) * H + h;
+            const char *src = (j < KU) ? reinterpret_cast<const char *>(k + row * DK) + 16 * j
+                              : (OUT && j < 2 * KU) ? reinterpret_cast<const char *>(q + row * DK) + 16 * (j - KU)
+                                                    : reinterpret_cast<const char *>(g + row * DK) +
+                                                          16 * (j - (OUT ? 2 : 1) * KU);
+            raw[it] = *reinterpret_cast<const u32x4 *>(src);
         }
-        for (int t = 0; t < nt; ++t) {
-            const int pb = t & 1;
-            float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int c = i * RG + rg;
-                const float f = sd[t][c], kc = sk[t][c];
-                s[i] *= f;
-                w.x += kc * s[i][0]; w.y += kc * s[i][1]; w.z += kc * s[i][2]; w.w += kc * s[i][3];
-                if (VERIFY) {
-                    const float qc = sq[t][c];
-                    y.x += qc * s[i][0]; y.y += qc * s[i][1]; y.z += qc * s[i][2]; y.w += qc * s[i][3];
+        for (int it = 0; it < ITER; ++it) {
+            const int u = lane + kWave * it;
+            if (u < nt * UT) {
+                const int tt = u / UT, j = u - tt * UT;
+                if (j < (OUT ? 2 : 1) * KU) {  // k or q: EPU values of T
+                    const int vi = j < KU ? 0 : 2, c0 = EPU * (j < KU ? j : j - KU);
+                    float *d = &my[tt][vi][wave_vec_idx<DK>(c0)];
+                    if constexpr (sizeof(T) == 2) {
+                        float f[8];
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            f[2 * e2] = __uint_as_float(raw[it][e2] << 16);
+                            f[2 * e2 + 1] = __uint_as_float(raw[it][e2] & 0xffff0000u);
+                        }
+                        *reinterpret_cast<floatx4 *>(d) = floatx4{f[0], f[1], f[2], f[3]};
+                        *reinterpret_cast<floatx4 *>(d + 4) = floatx4{f[4], f[5], f[6], f[7]};
+                    } else {
+                        *reinterpret_cast<u32x4 *>(d) = raw[it];
+                    }
+                } else {  // g: four values, stored as e^g
+                    const int c0 = 4 * (j - (OUT ? 2 : 1) * KU);
+                    *reinterpret_cast<floatx4 *>(&my[tt][1][wave_vec_idx<DK>(c0)]) =
+                        floatx4{exp_e(__uint_as_float(raw[it][0])), exp_e(__uint_as_float(raw[it][1])),
+                                exp_e(__uint_as_float(raw[it][2])), exp_e(__uint_as_float(raw[it][3]))};
                 }
             }
-            sw[pb][rg][cg] = w;
-            if (VERIFY) sy[pb][rg][cg] = y;
-            __syncthreads();  // one barrier per token: the partials of two tokens alternate
-            float4 W = make_float4(0.f, 0.f, 0.f, 0.f), Y = W;
+        }
+        // ---- the group's tokens, one after the other ----
+        for (int tt = 0; tt < nt; ++tt) {
+            const size_t row = (size_t(n) * K + t0 + tt) * H + h;  // token row of [N][K][H]
+            const float *kv = &my[tt][0][wave_vec_idx<DK>(r0)];
+            const float *ev = &my[tt][1][wave_vec_idx<DK>(r0)];
+            float kf[RPT];
+            floatx4 w = zero4(), y = zero4();
+            float kq = 0.f;
 #pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                const float4 a4 = sw[pb][r][cg];
-                W.x += a4.x; W.y += a4.y; W.z += a4.z; W.w += a4.w;
-                if (VERIFY) {
-                    const float4 b4 = sy[pb][r][cg];
-                    Y.x += b4.x; Y.y += b4.y; Y.z += b4.z; Y.w += b4.w;
+            for (int i = 0; i < RPT; i += 4) {
+                const floatx4 k4 = *reinterpret_cast<const floatx4 *>(kv + i);
+                const floatx4 e4 = *reinterpret_cast<const floatx4 *>(ev + i);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kf[i + j] = k4[j];
+                    s[i + j] *= e4[j];  // decay, then the partial sum of w = S'^T k
+                    w += k4[j] * s[i + j];
                 }
             }
-            const size_t row = (size_t(n) * K + t0 + t) * H + h;
+            if constexpr (OUT) {  // y = S'^T q and k . q
+                const float *qv = &my[tt][2][wave_vec_idx<DK>(r0)];
+#pragma unroll
+                for (int i = 0; i < RPT; i += 4) {
+                    const floatx4 q4 = *reinterpret_cast<const floatx4 *>(qv + i);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        y += q4[j] * s[i + j];
+                        kq += kf[i + j] * q4[j];
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = CG; off < kWave; off <<= 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] += __shfl_xor(w[j], off);
+                if constexpr (OUT) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y[j] += __shfl_xor(y[j], off);
+                    kq += __shfl_xor(kq, off);
+                }
+            }
             const float bt = beta[row];
-            const T *vp = v + row * DV + col0 + 4 * cg;
-            float4 u;
-            u.x = bt * (to_f32(vp[0]) - W.x);
-            u.y = bt * (to_f32(vp[1]) - W.y);
-            u.z = bt * (to_f32(vp[2]) - W.z);
-            u.w = bt * (to_f32(vp[3]) - W.w);
+            float vf[4];
+            load_vec<4>(v + row * DV + col, vf);
+            const floatx4 u = floatx4{bt * (vf[0] - w[0]), bt * (vf[1] - w[1]), bt * (vf[2] - w[2]),
+                                      bt * (vf[3] - w[3])};
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const float kc = sk[t][i * RG + rg];
-                s[i][0] += kc * u.x; s[i][1] += kc * u.y; s[i][2] += kc * u.z; s[i][3] += kc * u.w;
-            }
-            if (VERIFY && rg == 0) {
-                const float kq = skq[t];
-                store4(o + row * DV + col0 + 4 * cg, Y.x + kq * u.x, Y.y + kq * u.y, Y.z + kq * u.z,
-                       Y.w + kq * u.w);
+            for (int i = 0; i < RPT; ++i) s[i] += kf[i] * u;
+            if constexpr (OUT) {
+                // o = S^T q after the update = y + (k . q) u
+                if (rg == 0)
+                    store4(o + row * DV + col, y[0] + kq * u[0], y[1] + kq * u[1], y[2] + kq * u[2],
+                           y[3] + kq * u[3]);
             }
         }
     }
-    if (!VERIFY) {
+    if constexpr (WRITE) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-            __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
+            __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4 *>(S + size_t(r0 + i) * DV));
     }
 }
 
-template <class T, int DK, int DV, bool VERIFY>
-static hipError_t launch_multi_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                                 const int32_t *n_accept, float *state, void *o, int N, int K, int H,
-                                 hipStream_t s) {
+template <class T, int DK, int DV, int MODE>
+static hipError_t launch_wave_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                                const int32_t *n_accept, float *state, void *o, int N, int K, int H, hipStream_t s,
+                                const char *name) {
     if (N == 0 || K == 0) return hipSuccess;
-    // all value columns in one workgroup: splitting them repeats the token
-    // staging and doubles the row-group partials each reduction reads (slower)
-    constexpr int CPB = DV;
+    constexpr int NB = DV / wave_columns<DV>();
+    const int nwaves = N * H * NB;
+    constexpr int WPB = kWavePB;  // the column blocks of one (sequence, head) share a CU at DV = 128
     prof_begin(s);
-    hipLaunchKernelGGL((kda_decode_multi_kernel<T, DK, DV, CPB, VERIFY>), dim3(N * H * (DV / CPB)), dim3(256), 0, s,
-                       static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
-                       n_accept, state, static_cast<T *>(o), K, H);
-    prof_end(s, VERIFY ? "kda_decode_verify" : "kda_decode_commit");
+    hipLaunchKernelGGL((kda_decode_wave_kernel<T, DK, DV, MODE>), dim3((nwaves + WPB - 1) / WPB), dim3(WPB * kWave),
+                       0, s, static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
+                       n_accept, state, static_cast<T *>(o), K, H, nwaves);
+    prof_end(s, name);
     return hipGetLastError();
 }
 
@@ -253,9 +331,12 @@ template <class T, bool VERIFY>
 static hipError_t multi_dispatch(int dk, int dv, const void *q, const void *k, const void *v, const float *g,
                                  const float *beta, const int32_t *n_accept, float *state, void *o, int N, int K,
                                  int H, hipStream_t s) {
-#define KDA_MUL(DK_, DV_) \
-    if (dk == DK_ && dv == DV_) \
-        return launch_multi_t<T, DK_, DV_, VERIFY>(q, k, v, g, beta, n_accept, state, o, N, K, H, s);
+#define KDA_MUL(DK_, DV_)                                                                                          \
+    if (dk == DK_ && dv == DV_)                                                                                    \
+        return VERIFY ? launch_wave_t<T, DK_, DV_, kVerify>(q, k, v, g, beta, n_accept, state, o, N, K, H, s,      \
+                                                            "kda_decode_verify")                                   \
+                      : launch_wave_t<T, DK_, DV_, kCommit>(q, k, v, g, beta, n_accept, state, o, N, K, H, s,      \
+                                                            "kda_decode_commit");
     KDA_MUL(32, 32) KDA_MUL(32, 64) KDA_MUL(32, 128)
     KDA_MUL(64, 32) KDA_MUL(64, 64) KDA_MUL(64, 128)
     KDA_MUL(128, 32) KDA_MUL(128, 64) KDA_MUL(128, 128)

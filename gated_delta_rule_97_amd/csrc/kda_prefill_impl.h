@@ -34,6 +34,7 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
+
 namespace kda {
 
 constexpr int kThreads = 256;  // 4 wavefronts
@@ -1184,17 +1185,19 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
 // issuing the next chunk's ~52 KiB of operand loads: every wave issues its
 // share at once and the compute unit's vector-memory pipeline takes them at
 // its own rate, while the products wait behind them in the same waves.  Here
-// four loader waves copy each chunk's operands (W, Q', K~^T, e^{Gam_last} and
-// this block's Ut and Oi tiles, already in the order the products read them)
-// into one of two LDS buffers two chunks ahead, and the four compute waves
-// read them from LDS: their only global accesses are the o stores.  Both roles
+// loader waves copy each chunk's operands (W, Q', K~^T, e^{Gam_last} and this
+// block's Ut and Oi tiles, already in the order the products read them) into
+// one of two LDS buffers two chunks ahead, and the four compute waves read
+// them from LDS: their only global accesses are the o stores.  Both roles
 // pass the same barriers: one before the chain, then the two of each chunk.
-// Cycle counters per chunk: compute ~1,500 (read 210, S^T 60, X/O 750, state
-// 150, checkpoint tests 150, barriers); the loader's ~830 of vector-memory
-// issue (52.5 KiB at ~64 B/clk) and ~450 of LDS writes split over both
-// windows between the barriers.
+// Twelve loader waves: a compute unit issues 16-byte loads faster the more
+// waves issue them (~41 B/clk from four waves, ~56 from sixteen), and with
+// twelve each loader thread holds five units a stage, so the kernel fits 128
+// VGPRs with no spill.  What bounds the chain is then the compute waves' own
+// latency per chunk (reads, S^T, X/O, state update, two barriers).
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int C>
+constexpr int kWsLoaderWaves = 12;
+template <int DK, int DV, int C, int NLW>
 struct WsBuf {
     using M = Mma<bf16>;
     static constexpr int CP = kpad<bf16>(C);
@@ -1207,63 +1210,54 @@ struct WsBuf {
     static constexpr int oO = oU + NT * 256 * 2;  // Oi tiles
     static constexpr int oD = oO + NT * 256 * 2;  // e^{Gam_last}, fp32
     static constexpr int bytes = oD + DK * 4;
-    static constexpr int units = bytes / 16;       // 16-byte copy units
+    static constexpr int units = bytes / 16;       // 16-byte copy units, laid end to end as above
     static_assert(oQ % 16 == 0 && oK % 16 == 0 && oU % 16 == 0 && oO % 16 == 0 && oD % 16 == 0 && bytes % 16 == 0,
                   "16-byte units");
-    static constexpr int kLoaders = kThreads;      // loader threads (four waves)
+    static constexpr int kLoaders = kWave * NLW;   // loader threads
     static constexpr int UPT = (units + kLoaders - 1) / kLoaders;  // units per loader thread
     static constexpr size_t lds_bytes = size_t(2) * bytes;
 };
 
-// Source of copy unit lt + kLoaders * i of chunk slot (gc, h), for value
-// block nn0.  The units run over W, Q', K~^T (each a contiguous span in the
-// workspace; four units of the 256 loader threads each at d = 128, chunk 64),
-// then this block's Ut and Oi tiles (four 512-byte spans each), then
-// e^{Gam_last}.  The category of each step i is fixed at compile time and the
-// mixed steps use selects, so every load is unconditional and the compiler
-// can count the loads in flight exactly.
-template <int DK, int DV, int C, int i>
-__device__ __forceinline__ const char *ws_src(const PrefillArgs &a, size_t slot, int nn0, int lt) {
-    using B = WsBuf<DK, DV, C>;
-    static_assert(B::oQ == 4 * 16 * B::kLoaders && B::oK == 8 * 16 * B::kLoaders && B::oU == 12 * 16 * B::kLoaders &&
-                      B::oD == 13 * 16 * B::kLoaders && B::bytes == B::oD + 32 * 16 && B::UPT == 14,
-                  "unit plan of the d = 128, chunk 64 layout");
-    const unsigned off = unsigned(lt) * 16u + unsigned(i % 4) * 16u * B::kLoaders;
-    if constexpr (i < 4) return static_cast<const char *>(a.W) + slot * (C * DK * 2) + off;
-    else if constexpr (i < 8) return static_cast<const char *>(a.Qp) + slot * (C * DK * 2) + off;
-    else if constexpr (i < 12) return static_cast<const char *>(a.KtT) + slot * (DK * B::CP * 2) + off;
-    else if constexpr (i == 12) {
-        const bool is_u = lt < 128;
-        const unsigned j = unsigned(lt) & 127u;        // unit within the four tiles
-        const unsigned I = j / 32u, w = j % 32u;       // 32 units per 512-byte tile
-        const char *base = static_cast<const char *>(is_u ? a.Ut : a.Oi) + slot * (C * DV * 2);
-        return base + (size_t(I * (DV / 16) + nn0) * 256 + w * 8) * 2;
-    } else {
-        return reinterpret_cast<const char *>(a.D + slot * DK) + unsigned(min(lt, 31)) * 16u;
-    }
+// Source of copy unit u (< units) of chunk slot (gc, h), for value block
+// nn0.  The units run over W, Q', K~^T (contiguous spans of the workspace),
+// then this block's Ut and Oi tiles (512-byte spans: 32 units a tile), then
+// e^{Gam_last}.  Selects, not branches, so every load is unconditional and
+// the compiler can count the loads in flight exactly.
+template <int DK, int DV, int C, int NLW>
+__device__ __forceinline__ const char *ws_src(const PrefillArgs &a, size_t slot, int nn0, int u) {
+    using B = WsBuf<DK, DV, C, NLW>;
+    constexpr int UW = C * DK * 2 / 16, UK = DK * B::CP * 2 / 16, UT = B::NT * 32;
+    const char *wq = static_cast<const char *>(u < UW ? a.W : a.Qp) + slot * (C * DK * 2) +
+                     size_t(u < UW ? u : u - UW) * 16;
+    const char *kt = static_cast<const char *>(a.KtT) + slot * (DK * B::CP * 2) + size_t(u - 2 * UW) * 16;
+    const int j = u - 2 * UW - UK;               // unit within this block's Ut, Oi tiles
+    const int jt = j < UT ? j : j - UT;
+    const char *uo = static_cast<const char *>(j < UT ? a.Ut : a.Oi) + slot * (C * DV * 2) +
+                     (size_t((jt / 32) * (DV / 16) + nn0) * 256 + (jt % 32) * 8) * 2;
+    const char *d = reinterpret_cast<const char *>(a.D + slot * DK) + size_t(min(j - 2 * UT, DK / 4 - 1)) * 16;
+    return u < 2 * UW ? wq : (u < 2 * UW + UK ? kt : (j < 2 * UT ? uo : d));
 }
 
-// LDS byte offset of copy unit (lt, i) inside one buffer.
-template <int DK, int DV, int C, int i>
-__device__ __forceinline__ unsigned ws_dst(int lt) {
-    using B = WsBuf<DK, DV, C>;
-    if constexpr (i < 13) return (unsigned(lt) + unsigned(i) * B::kLoaders) * 16u;
-    else return unsigned(B::oD) + unsigned(min(lt, 31)) * 16u;
+// Copy unit lt + kLoaders * i of a chunk; units past the end repeat the last.
+template <int DK, int DV, int C, int NLW, int i>
+__device__ __forceinline__ int ws_unit(int lt) {
+    using B = WsBuf<DK, DV, C, NLW>;
+    return min(lt + B::kLoaders * i, B::units - 1);
 }
 
-template <int DK, int DV, int C, int i>
+template <int DK, int DV, int C, int NLW, int i>
 __device__ __forceinline__ void ws_fetch_unit(u32x4 *r, const PrefillArgs &a, size_t slot, int nn0, int lt) {
-    if constexpr (i < WsBuf<DK, DV, C>::UPT) {
-        r[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, i>(a, slot, nn0, lt));
-        ws_fetch_unit<DK, DV, C, i + 1>(r, a, slot, nn0, lt);
+    if constexpr (i < WsBuf<DK, DV, C, NLW>::UPT) {
+        r[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, NLW>(a, slot, nn0, ws_unit<DK, DV, C, NLW, i>(lt)));
+        ws_fetch_unit<DK, DV, C, NLW, i + 1>(r, a, slot, nn0, lt);
     }
 }
 
-template <int DK, int DV, int C, int i>
+template <int DK, int DV, int C, int NLW, int i>
 __device__ __forceinline__ void ws_put_unit(const u32x4 *r, unsigned char *dst, int lt) {
-    if constexpr (i < WsBuf<DK, DV, C>::UPT) {
-        *reinterpret_cast<u32x4 *>(dst + ws_dst<DK, DV, C, i>(lt)) = r[i];
-        ws_put_unit<DK, DV, C, i + 1>(r, dst, lt);
+    if constexpr (i < WsBuf<DK, DV, C, NLW>::UPT) {
+        *reinterpret_cast<u32x4 *>(dst + ws_unit<DK, DV, C, NLW, i>(lt) * 16) = r[i];
+        ws_put_unit<DK, DV, C, NLW, i + 1>(r, dst, lt);
     }
 }
 
@@ -1271,21 +1265,22 @@ __device__ __forceinline__ void ws_put_unit(const u32x4 *r, unsigned char *dst, 
 // registers (rp) goes to LDS, then unit i of a later chunk (slot) is
 // requested into rf.  Alternating the two keeps the LDS and the
 // vector-memory pipelines busy together.
-template <int DK, int DV, int C, int i, int iend>
+template <int DK, int DV, int C, int NLW, int i, int iend>
 __device__ __forceinline__ void ws_step(const u32x4 *rp, unsigned char *dst, u32x4 *rf, const PrefillArgs &a,
                                         size_t slot, int nn0, int lt) {
     if constexpr (i < iend) {
-        *reinterpret_cast<u32x4 *>(dst + ws_dst<DK, DV, C, i>(lt)) = rp[i];
-        rf[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, i>(a, slot, nn0, lt));
-        ws_step<DK, DV, C, i + 1, iend>(rp, dst, rf, a, slot, nn0, lt);
+        const int u = ws_unit<DK, DV, C, NLW, i>(lt);
+        *reinterpret_cast<u32x4 *>(dst + u * 16) = rp[i];
+        rf[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, NLW>(a, slot, nn0, u));
+        ws_step<DK, DV, C, NLW, i + 1, iend>(rp, dst, rf, a, slot, nn0, lt);
     }
 }
 
-template <int DK, int DV, int C>
-__global__ __launch_bounds__(2 * kThreads) void kda_inter_ws_kernel(PrefillArgs a) {
+template <int DK, int DV, int C, int NLW>
+__global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(PrefillArgs a) {
     constexpr int BV = 16;
     using Cfg = InterCfg<bf16, DK, DV, C, BV>;
-    using B = WsBuf<DK, DV, C>;
+    using B = WsBuf<DK, DV, C, NLW>;
     using M = Mma<bf16>;
     constexpr int NRT = Cfg::NRT, NSI = Cfg::NSI, SPW = Cfg::SPW, XPW = Cfg::XPW;
     constexpr int NB = DV / BV;
@@ -1329,18 +1324,19 @@ __global__ __launch_bounds__(2 * kThreads) void kda_inter_ws_kernel(PrefillArgs 
     if (wid_all >= kWaves) {
         // ---------------- loader waves ----------------
         const int lt = tid - kThreads;
-        u32x4 st[3][B::UPT];
-        auto fetch = [&](u32x4 (&r)[B::UPT], int c) {
+        constexpr int UPT = B::UPT;
+        u32x4 st[3][UPT];
+        auto fetch = [&](u32x4 (&r)[UPT], int c) {
             const size_t slot = size_t(c_begin + min(c, nc - 1)) * H + h;
-            ws_fetch_unit<DK, DV, C, 0>(r, a, slot, nn0, lt);
+            ws_fetch_unit<DK, DV, C, NLW, 0>(r, a, slot, nn0, lt);
         };
-        auto put = [&](const u32x4 (&r)[B::UPT], int buf) { ws_put_unit<DK, DV, C, 0>(r, wsbuf + buf * B::bytes, lt); };
+        auto put = [&](const u32x4 (&r)[UPT], int buf) { ws_put_unit<DK, DV, C, NLW, 0>(r, wsbuf + buf * B::bytes, lt); };
         // chunk x lives in register stage x % 3 and LDS buffer x & 1.  During
         // chunk c the loader writes chunk c + 2 into buffer c & 1 (read by the
         // compute waves at the top of chunk c, before the first barrier) and
         // requests chunk c + 4, half after each of the chunk's two barriers,
         // so neither half holds a barrier back.
-        constexpr int HALF = B::UPT / 2;
+        constexpr int HALF = UPT / 2;
         auto slot_of = [&](int x) { return size_t(c_begin + min(x, nc - 1)) * H + h; };
         if (nc > 0) {
             fetch(st[0], 0);
@@ -1358,9 +1354,9 @@ __global__ __launch_bounds__(2 * kThreads) void kda_inter_ws_kernel(PrefillArgs 
                 unsigned char *dst = wsbuf + ((c + s) & 1) * B::bytes;
                 const size_t sl = slot_of(c + s + 4);
                 __syncthreads();  // A
-                ws_step<DK, DV, C, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
                 __syncthreads();  // B
-                ws_step<DK, DV, C, HALF, B::UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, HALF, UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
             }
         }
 #pragma unroll
@@ -1369,9 +1365,9 @@ __global__ __launch_bounds__(2 * kThreads) void kda_inter_ws_kernel(PrefillArgs 
                 unsigned char *dst = wsbuf + ((c + s) & 1) * B::bytes;
                 const size_t sl = slot_of(c + s + 4);
                 __syncthreads();
-                ws_step<DK, DV, C, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
                 __syncthreads();
-                ws_step<DK, DV, C, HALF, B::UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, HALF, UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
             }
         }
         return;
@@ -1918,17 +1914,19 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
     const int nwg = a.N * a.H * (DV / BV);
     if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && C == 64 && BV == 16) {
         // loader-fed state chain (one chain per (sequence, head), no segments)
-        using WB = WsBuf<DK, DV, C>;
+        constexpr int NLW = kWsLoaderWaves;
+        using WB = WsBuf<DK, DV, C, NLW>;
         static bool ws_attr = false;
         if (!ws_attr) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C>),
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C, NLW>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(WB::lds_bytes));
             if (e != hipSuccess) return e;
             ws_attr = true;
         }
         if (nwg > 0) {
             prof_begin(s);
-            hipLaunchKernelGGL((kda_inter_ws_kernel<DK, DV, C>), dim3(nwg), dim3(2 * kThreads), WB::lds_bytes, s, a);
+            hipLaunchKernelGGL((kda_inter_ws_kernel<DK, DV, C, NLW>), dim3(nwg), dim3(kThreads + kWave * NLW),
+                               WB::lds_bytes, s, a);
             prof_end(s, "kda_inter");
         }
         return hipGetLastError();

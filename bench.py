@@ -7,9 +7,10 @@ beta and states, chunk 64, h0 ~ N(0, 0.02).  One step = one kda_chunk_prefill
 call over the whole batch (all of its kernels), inputs resident in HBM.
 value = tokens/s = B*T / (time per call).
 
-The K timed calls carry one event between consecutive calls and none
-inside a call: ms_per_step is their mean, "timing" their median and
-p10/p90.  Per-kernel durations come from a second timed pass of K calls
+Half a second of untimed calls precedes the W warmup calls (the GPU's
+clocks ramp up over the first tens of milliseconds of sustained work).  The
+K timed calls carry one event between consecutive calls and none inside a
+call: ms_per_step is their mean, "timing" their median and p10/p90.  Per-kernel durations come from a second timed pass of K calls
 with HIP events around every launch on its stream; "roofline" charges the
 longest kernel with the whole call's algorithmic bytes (1,540 B per
 token-head plus the states), "kernel_scoped" with its own, "path_roofline"
@@ -189,6 +190,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-passes", type=int, default=3)
+    ap.add_argument("--prewarm-seconds", type=float, default=0.5,
+                    help="untimed prefill calls for this long before the warmup steps (the GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="finish with a 1 GiB device-to-device copy (counter calibration)")
@@ -233,7 +236,19 @@ def main():
         kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], chunk_size=C, o=o, ht=ht,
                           workspace=ws)
 
-    log(f"prefill warmup x{args.warmup}")
+    # The GPU's clocks ramp up over the first tens of milliseconds of sustained
+    # work: right after a few warmup calls the headline call measured ~331 us,
+    # ~296 us once warm, with every timing method (events between calls, one
+    # pair around all calls, fence-free events).  Untimed calls for a fixed
+    # wall time first, then the warmup steps, so the timed calls see steady state.
+    log(f"prefill prewarm {args.prewarm_seconds:.2f} s, then warmup x{args.warmup}")
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while time.perf_counter() - t_pre < args.prewarm_seconds:
+        for _ in range(16):
+            step()
+        n_pre += 16
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -551,7 +566,8 @@ def main():
            "data": "synthetic (seeded generators: unit-norm q/k, N(0,1) v, sigmoid beta, g=-5*sigmoid(N(0,1)))",
            "config": {"workload": workload, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C,
                       "h0": "N(0,0.02)"},
-           "roofline": roofline, "path_roofline": path_roofline, "timing": headline_spread,
+           "roofline": roofline, "path_roofline": path_roofline,
+           "timing": dict(headline_spread, prewarm_calls=n_pre, prewarm_s=args.prewarm_seconds),
            "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
            "cpu_baseline": cpu, "parity": parity, "decode": decode, "varlen": varlen,
            "next": nxt if nxt is not None else {"speculative_verify": verify},

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <utility>
 #include <string>
 #include <vector>
 
@@ -86,6 +87,20 @@ struct Profiler {
     std::vector<std::string> names;
 } g_prof;
 }  // namespace
+
+hipError_t ensure_dynamic_lds(const void *kernel, int bytes) {
+    static std::mutex mu;
+    static std::vector<std::pair<const void *, int>> done;  // (kernel, device)
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &d : done)
+        if (d.first == kernel && d.second == dev) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.emplace_back(kernel, dev);
+    return e;
+}
 
 void prof_begin(hipStream_t s) {
     if (!g_prof.active || g_prof.used >= g_prof.cap) return;

@@ -67,6 +67,11 @@ inline int chunk_pad(int C, size_t elem_bytes) {
     return (C + k - 1) / k * k;
 }
 
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (kernel, device); thread-safe.  Kernels with more than 64 KiB of
+// dynamic LDS need it before their first launch on each device.
+hipError_t ensure_dynamic_lds(const void *kernel, int bytes);
+
 // Launch-time profiling hooks (no-ops unless a profiling session is open).
 void prof_begin(hipStream_t s);
 void prof_end(hipStream_t s, const char *name);

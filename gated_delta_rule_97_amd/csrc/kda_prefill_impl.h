@@ -1819,12 +1819,9 @@ template <class T, int DK, int DV, int C, int BV>
 hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
     using Ly = IntraLds<T, DK, DV, C>;
     static_assert(Ly::bytes <= 160 * 1024, "intra-chunk LDS exceeds 160 KiB");
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_intra_kernel<T, DK, DV, C>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(Ly::bytes));
+    {
+        hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&kda_intra_kernel<T, DK, DV, C>), int(Ly::bytes));
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     if (a.nc_max > 0) {
         // persistent: one workgroup per compute unit (LDS allows one), each
@@ -1916,12 +1913,10 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         // loader-fed state chain (one chain per (sequence, head), no segments)
         constexpr int NLW = kWsLoaderWaves;
         using WB = WsBuf<DK, DV, C, NLW>;
-        static bool ws_attr = false;
-        if (!ws_attr) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C, NLW>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(WB::lds_bytes));
+        {
+            hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C, NLW>),
+                                              int(WB::lds_bytes));
             if (e != hipSuccess) return e;
-            ws_attr = true;
         }
         if (nwg > 0) {
             prof_begin(s);

@@ -42,14 +42,14 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
     off = align_up(off + sizeof(int32_t) * size_t(N + 1), 256);
     L.W = off;
     off = align_up(off + slots * C * dk * elem_bytes, 256);
-    L.Qp = off;
+    L.Qg = off;
     off = align_up(off + slots * C * dk * elem_bytes, 256);
     L.KtT = off;
     off = align_up(off + slots * chunk_pad(C, elem_bytes) * dk * elem_bytes, 256);
     L.Ut = off;
     off = align_up(off + slots * C * dv * elem_bytes, 256);
-    L.Oi = off;
-    off = align_up(off + slots * C * dv * elem_bytes, 256);
+    L.Ps = off;
+    off = align_up(off + slots * score_elems(C, elem_bytes == 2 ? 32 : 4) * elem_bytes, 256);
     L.D = off;
     off = align_up(off + slots * dk * sizeof(float), 256);
     const size_t sch = nseg > 1 ? size_t(N) * nseg * H : 0;  // segment chains
@@ -325,7 +325,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     a.num_cu = device_cu_count();
     if (a.num_cu <= 0) return KDA_ERR_LAUNCH;
     a.o = o; a.ht = ht;
-    a.W = ws + L.W; a.Qp = ws + L.Qp; a.KtT = ws + L.KtT; a.Ut = ws + L.Ut; a.Oi = ws + L.Oi;
+    a.W = ws + L.W; a.Qg = ws + L.Qg; a.KtT = ws + L.KtT; a.Ut = ws + L.Ut; a.Ps = ws + L.Ps;
     a.D = reinterpret_cast<float *>(ws + L.D);
     a.dummy = ws + L.dummy;
     const bool want_ck = ck.ckpt && ck.num_ckpt > 0;

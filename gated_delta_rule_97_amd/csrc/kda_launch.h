@@ -25,10 +25,10 @@ struct PrefillArgs {
     // workspace, per (chunk slot, head); "operand" / "quad" order are the
     // wave-read orders defined in kda_prefill_impl.h:
     void *W;                   // [C][dk]  (I+A)^-1 (beta k e^Gam), operand order
-    void *Qp;                  // [C][dk]  q e^Gam - P W, operand order
+    void *Qg;                  // [C][dk]  q e^Gam, operand order
     void *KtT;                 // [dk][Cp] (k e^{Gam_last - Gam})^T, operand order
     void *Ut;                  // [C][dv]  (I+A)^-1 (beta v), quad order
-    void *Oi;                  // [C][dv]  P (I+A)^-1 (beta v), quad order
+    void *Ps;                  // [C][C]   scores P (lower by 16-token tiles), lower-block operand order
     float *D;                  // [dk]     e^{Gam_last}
     void *dummy;               // 1 KiB sink for the o rows past a sequence's end
     // strided state checkpoints (null ckpt: none): after every ck_every
@@ -57,7 +57,7 @@ SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq);
 
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {
-    size_t coff, ckoff, W, Qp, KtT, Ut, Oi, D, Mseg, Bseg, Sin, dummy, flag, total;
+    size_t coff, ckoff, W, Qg, KtT, Ut, Ps, D, Mseg, Bseg, Sin, dummy, flag, total;
 };
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
                              size_t elem_bytes, int nseg);
@@ -66,6 +66,17 @@ inline int chunk_pad(int C, size_t elem_bytes) {
     const int k = elem_bytes == 2 ? 32 : 4;
     return (C + k - 1) / k * k;
 }
+
+// Elements of a chunk's score matrix P in lower-block operand order: row
+// tile I (16 tokens) keeps only the k-blocks (16 x kstep values, kstep the
+// MFMA contraction: 32 for bf16, 4 for fp32) that reach its diagonal, i.e.
+// ceil(16 (I + 1) / kstep) of them; row tiles in order.
+constexpr int score_blocks(int C, int kstep) {
+    int n = 0;
+    for (int I = 0; I < C / 16; ++I) n += (16 * (I + 1) + kstep - 1) / kstep;
+    return n;
+}
+constexpr int score_elems(int C, int kstep) { return score_blocks(C, kstep) * 16 * kstep; }
 
 // Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
 // per (kernel, device); thread-safe.  Kernels with more than 64 KiB of

@@ -18,17 +18,18 @@
 //     e^{Gam_t - r_I} (<= 1, row operand) * e^{r_I - Gam_s} (<= e^80, column)
 //   L     = (I + A)^-1               blocked forward substitution, fp32
 //   W     = L (beta k e^Gam),  Ut = L (beta v)                   (WY / UT form)
-//   Q'    = q e^Gam - P W,     Oi = P Ut      (state-free part of the output)
 // and, sequentially over chunks, with the state kept on chip in fp32:
 //   U      = Ut - W S
-//   o      = Oi + Q' S
+//   o      = (q e^Gam) S + P U
 //   S_next = Diag(e^{Gam_last}) S + (k e^{Gam_last - Gam})^T U
 //
 // Kernel 1 (kda_intra_kernel): one workgroup per (chunk, head), fully
-//   parallel; everything that does not depend on the incoming state.
-// Kernel 2 (kda_inter_kernel): one workgroup per (sequence, head, dv block),
-//   sequential over the sequence's chunks; the fp32 state block lives in
-//   MFMA accumulator registers for the whole sequence.
+//   parallel; everything that does not depend on the incoming state: W, Ut,
+//   q e^Gam, P, K~^T = (k e^{Gam_last - Gam})^T and e^{Gam_last}.
+// Kernel 2 (kda_inter_kernel and its variants): one workgroup per
+//   (sequence, head, dv block), sequential over the sequence's chunks; the
+//   fp32 state block lives in MFMA accumulator registers for the whole
+//   sequence.
 #pragma once
 
 #include "kda_device.h"
@@ -137,6 +138,42 @@ __device__ __forceinline__ size_t quad_off(int tile_r, int tile_n, int lane) {
     return size_t(unsigned(tile_r) * (N / 16) + unsigned(tile_n)) * 256 + unsigned(lane) * 4;
 }
 
+// Lower-block operand order of a chunk's scores P [C][C] (zero above the
+// 16-token diagonal tiles): the operand order kept only for the k-blocks a
+// row tile's product reads, p_nk(I) blocks for row tile I, row tiles in
+// order (score_elems values in all).  Inside a kept block the values past
+// the row tile's diagonal tile are stored zeros.
+template <class T> __host__ __device__ constexpr int p_nk(int I) {
+    return (kTile * (I + 1) + Mma<T>::K - 1) / Mma<T>::K;
+}
+template <class T> __host__ __device__ constexpr int p_pre(int I) {
+    int n = 0;
+    for (int i = 0; i < I; ++i) n += p_nk<T>(i);
+    return n;
+}
+template <class T, int C> __host__ __device__ constexpr int p_elems() {
+    static_assert(score_elems(C, Mma<T>::K) == p_pre<T>(C / kTile) * 16 * Mma<T>::K, "score layout size");
+    return p_pre<T>(C / kTile) * 16 * Mma<T>::K;
+}
+// four consecutive k (s0 % 4 == 0) of row t into the lower-block order
+template <class T>
+__device__ __forceinline__ void store_p4(T *base, int t, int s0, float a, float b, float c, float d) {
+    using M = Mma<T>;
+    auto off = [&](int s) -> size_t {
+        const unsigned blk = unsigned(p_pre<T>(t >> 4)) + unsigned(s) / M::K;
+        const unsigned ln = unsigned(t & 15) + 16u * ((unsigned(s) % M::K) / M::KPL);
+        return size_t(blk) * (16 * M::K) + ln * M::KPL + (unsigned(s) % M::KPL);
+    };
+    if constexpr (M::KPL >= 4) {
+        store4(base + off(s0), a, b, c, d);
+    } else {
+        base[off(s0)] = from_f32<T>(a);
+        base[off(s0 + 1)] = from_f32<T>(b);
+        base[off(s0 + 2)] = from_f32<T>(c);
+        base[off(s0 + 3)] = from_f32<T>(d);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1: intra-chunk work, persistent.  Its LDS footprint allows one
 // workgroup per compute unit, so the workgroup is 16 wavefronts (four per
@@ -161,7 +198,6 @@ struct IntraLds {
     static constexpr int K_LD = DK + PT;        // K+, K-, Q+          [C][DK]
     static constexpr int KT_LD = C + PT;        // transposed operands [DK|DV][C]
     static constexpr int A_LD = C + 4;          // fp32 A, L           [C][C]
-    static constexpr int P_LD = C + PT;         // P                   [C][C]
     static constexpr int Y_LD = 20;             // fp32 16x16 tile of L^T, padded rows
     static constexpr int NLT = NT * (NT - 1) / 2;  // L^T tiles (K, J), J <= K <= NT - 2
     static constexpr size_t kKK = size_t(2) * C * K_LD * sizeof(T);  // K+ and K-
@@ -169,16 +205,14 @@ struct IntraLds {
     static constexpr size_t sQp = size_t(C) * K_LD * sizeof(T);
     static constexpr size_t sKT = size_t(DK) * KT_LD * sizeof(T);
     static constexpr size_t sVT = size_t(DV) * KT_LD * sizeof(T);
-    static constexpr size_t sP = size_t(C) * P_LD * sizeof(T);
     static constexpr size_t sTail = size_t(NLT > 0 ? NLT : 1) * 16 * Y_LD * 4 + size_t(NSEG + 1) * DK * 4 +
                                     size_t(NOFF > 0 ? NOFF : 1) * DK * 4 + size_t(NT) * DK * 4 + size_t(C) * 4;
     static constexpr size_t kKA = kKK > kAL ? kKK : kAL;
     // Compact placement, for the shapes whose plain layout exceeds the 160
     // KiB of a compute unit (fp32 with a 64-token chunk and dk or dv = 128):
     // (beta v)^T is staged after the A/P products, into the dead K+/K- space
-    // behind A and L, and P is stored into A's space once the inverse has
-    // read A.  Same products, same values; two phases hold them longer.
-    static constexpr bool COMPACT = kKA + sQp + sKT + sVT + sP + sTail > size_t(160) * 1024;
+    // behind A and L.  Same products, same values.
+    static constexpr bool COMPACT = kKA + sQp + sKT + sVT + sTail > size_t(160) * 1024;
     static constexpr size_t kReg = COMPACT ? (kKK > kAL + sVT ? kKK : kAL + sVT) : kKA;
     static constexpr size_t oKp = 0;
     static constexpr size_t oKm = oKp + size_t(C) * K_LD * sizeof(T);
@@ -187,9 +221,7 @@ struct IntraLds {
     static constexpr size_t oQp = kReg;
     static constexpr size_t oKT = oQp + sQp;
     static constexpr size_t oVT = COMPACT ? kAL : oKT + sKT;
-    static constexpr size_t oP = COMPACT ? oA : oVT + sVT;
-    static constexpr size_t oY = COMPACT ? oKT + sKT : oP + sP;
-    static_assert(!COMPACT || sP <= size_t(C) * A_LD * 4, "P fits in A's space");
+    static constexpr size_t oY = COMPACT ? oKT + sKT : oVT + sVT;
     static constexpr size_t oTot = oY + size_t(NLT > 0 ? NLT : 1) * 16 * Y_LD * 4;
     static constexpr size_t oF = oTot + size_t(NSEG + 1) * DK * 4;
     static constexpr size_t oR = oF + size_t(NOFF > 0 ? NOFF : 1) * DK * 4;
@@ -423,7 +455,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     typedef typename M::Frag Frag;
     constexpr int NT = C / kTile, NSEG = Ly::NSEG;
     constexpr int K_LD = Ly::K_LD, KT_LD = Ly::KT_LD;
-    constexpr int A_LD = Ly::A_LD, P_LD = Ly::P_LD, Y_LD = Ly::Y_LD;
+    constexpr int A_LD = Ly::A_LD, Y_LD = Ly::Y_LD;
 
     extern __shared__ __align__(16) unsigned char smem[];
     T *sKp = reinterpret_cast<T *>(smem + Ly::oKp);    // k e^{Gam - r_I}   (<= 1)
@@ -433,7 +465,6 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);    // (beta v)^T,       later Ut^T
     float *sA = reinterpret_cast<float *>(smem + Ly::oA);
     float *sL = reinterpret_cast<float *>(smem + Ly::oL);
-    T *sP = reinterpret_cast<T *>(smem + Ly::oP);
     float *sY = reinterpret_cast<float *>(smem + Ly::oY);
     float *sTot = reinterpret_cast<float *>(smem + Ly::oTot);  // segment decay totals, then their
                                                                // exclusive prefix     [NSEG + 1][DK]
@@ -547,6 +578,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
             // per channel: four tokens' beta k e^Gam and K~, for the column stores
             Col4<T> bke[4], ktv[4];
+            T *Qg = static_cast<T *>(a.Qg) + slot * C * DK;
             float run[4] = {base[0], base[1], base[2], base[3]};  // Gam - r_I, token by token
 #pragma unroll
             for (int r = 0; r < kSR; ++r) {
@@ -570,6 +602,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 store4(sKp + t * K_LD + c0, kp[0], kp[1], kp[2], kp[3]);
                 store4(sKm + t * K_LD + c0, km[0], km[1], km[2], km[3]);
                 store4(sQp + t * K_LD + c0, qp[0], qp[1], qp[2], qp[3]);
+                // q e^Gam = Q+ e^{r_I}, for the state pass's Q S
+                store_frag4<T, DK>(Qg, t, c0, qp[0] * er[0], qp[1] * er[1], qp[2] * er[2], qp[3] * er[3]);
             }
             // channels: (beta k e^Gam)^T to LDS and K~^T to HBM, 4 tokens per store
             T *KtT = static_cast<T *>(a.KtT) + slot * DK * kpad<T>(C);
@@ -598,7 +632,10 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         // ---- A (strictly lower, row-scaled by beta) and P (lower incl.) on
         //      MFMA, one 16x16 tile pair (I, J <= I) per wave.  Operands are
         //      K+ and Q+ of tile I and K- of tile J, times e^{r_I - r_J} when
-        //      J < I; on the diagonal the column operand is <= e^80. ----
+        //      J < I; on the diagonal the column operand is <= e^80.  P is
+        //      formed transposed (K- Q+^T), which leaves each lane four
+        //      consecutive k of one row: the operand fragment of the state
+        //      pass's P U, stored straight to HBM. ----
         constexpr int NPAIR = NT * (NT + 1) / 2;
         static_assert(NPAIR <= kIWaves, "A/P tile pairs");
         floatx4 accA = zero4(), accP = zero4();
@@ -625,39 +662,28 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     }
                 }
                 accA = M::mma(fk, fb, accA);
-                accP = M::mma(fq, fb, accP);
+                accP = M::mma(fb, fq, accP);
             }
+            // lane: P[16 I + l16][16 J + 4 grp + r], causal on the diagonal tile
+            float pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[r] = (J < I || 4 * grp + r <= l16) ? accP[r] : 0.f;
+            store_p4<T>(static_cast<T *>(a.Ps) + slot * p_elems<T, C>(), kTile * I + l16, kTile * J + 4 * grp, pv[0],
+                        pv[1], pv[2], pv[3]);
         }
         __syncthreads();  // K+ and K- are dead: their LDS becomes A and L
         static_assert(NT * NT <= kIWaves, "one tile of A/P or of the zero upper part per wave");
-        // P (lower, with the zero upper tiles) into its LDS space: here, or,
-        // in the compact layout where P takes A's space, after the inverse
-        auto store_p = [&]() {
-            if (wid >= NPAIR && wid < NT * NT) {
-                int I = 1, rem = wid - NPAIR;
-                while (rem >= I) { rem -= I; ++I; }
-                const int J = rem, col = kTile * I + l16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sP[(kTile * J + 4 * grp + r) * P_LD + col] = from_f32<T>(0.f);
-            }
-            if (wid < NPAIR) {
-                int I = 0, rem = wid;
-                while (rem > I) { rem -= I + 1; ++I; }
-                const int col = kTile * rem + l16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = kTile * I + 4 * grp + r;
-                    sP[t * P_LD + col] = from_f32<T>((col <= t) ? accP[r] : 0.f);
-                }
-            }
-        };
         if (wid >= NPAIR && wid < NT * NT) {
-            // tile (row J, column I), J < I, is zero in L (and P)
+            // tile (row J, column I), J < I, is zero in L and P; P's zeros are
+            // stored where the tile shares a kept k-block with row tile J
             int I = 1, rem = wid - NPAIR;
             while (rem >= I) { rem -= I; ++I; }
             const int J = rem, col = kTile * I + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) sL[(kTile * J + 4 * grp + r) * A_LD + col] = 0.f;
+            if ((kTile * I) / M::K < p_nk<T>(J))
+                store_p4<T>(static_cast<T *>(a.Ps) + slot * p_elems<T, C>(), kTile * J + l16, kTile * I + 4 * grp, 0.f,
+                            0.f, 0.f, 0.f);
         }
         if (wid < NPAIR) {
             int I = 0, rem = wid;
@@ -670,8 +696,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 sA[t * A_LD + col] = (col < t) ? sB[t] * accA[r] : 0.f;
             }
         }
-        if constexpr (!Ly::COMPACT) store_p();
-        else if (rt >= R::NG && rt < R::NG + R::NV) stage_bv(sVT, sB, in, tid);  // into the K+/K- space
+        if constexpr (Ly::COMPACT)
+            if (rt >= R::NG && rt < R::NG + R::NV) stage_bv(sVT, sB, in, tid);  // into the K+/K- space
         __syncthreads();
 
         // ---- L = (I + A)^-1 by blocked forward substitution (fp32) on the
@@ -751,8 +777,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         constexpr int KSTEPS = (C + M::K - 1) / M::K;
         static_assert(kIWaves % NT == 0, "a wave keeps one token tile");
         const int tt = wid % NT;
-        // the k-steps past the diagonal tile multiply the zero upper tiles of L
-        // and P: doing them keeps every operand read unconditional, so a wave
+        // the k-steps past the diagonal tile multiply the zero upper tiles of
+        // L: doing them keeps every operand read unconditional, so a wave
         // issues all its LDS reads before its first product
         // k-fragment kk of a row starting at p; zero past the chunk (when C < K)
         auto frag_at = [&](const T *p, int kk) -> Frag {
@@ -785,7 +811,9 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                 res[it] = acc;
             }
         }
-        __syncthreads();  // every read of the beta k e^Gam / beta v operands is done
+        // W and Ut to HBM, in their consumers' orders.  No LDS is written
+        // after the products: the next item's first writes (segment totals,
+        // beta) touch nothing they read, and its first barrier orders the rest.
         {
             T *Wg = static_cast<T *>(a.W) + slot * C * DK;
             T *Ug = static_cast<T *>(a.Ut) + slot * C * DV;
@@ -797,55 +825,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     // lane holds W[t][c0..c0+3]: t = 16 tt + l16, c0 = 16 m + 4 grp
                     const int t = kTile * tt + l16, c0 = kTile * (wi / NT) + 4 * grp;
                     store_frag4<T, DK>(Wg, t, c0, acc[0], acc[1], acc[2], acc[3]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sKT[(c0 + r) * KT_LD + t] = from_f32<T>(acc[r]);  // W^T
                 } else if (wi < NITEM) {
                     // lane holds Ut[t0..t0+3][j]: t0 = 16 tt + 4 grp, j = 16 n + l16
-                    const int n = (wi - NIW) / NT;
-                    store4(Ug + quad_off<DV>(tt, n, lane), acc[0], acc[1], acc[2], acc[3]);
-                    store4(sVT + (kTile * n + l16) * KT_LD + kTile * tt + 4 * grp, acc[0], acc[1], acc[2],
-                           acc[3]);  // Ut^T
+                    store4(Ug + quad_off<DV>(tt, (wi - NIW) / NT, lane), acc[0], acc[1], acc[2], acc[3]);
                 }
             }
         }
-        if constexpr (Ly::COMPACT) store_p();  // A's space: the inverse has read A
-        __syncthreads();
-
-        // ---- Q' = q e^Gam - P W (as (P W)^T = W^T P^T, four channels of one
-        //      token per lane) and Oi = P Ut ----
-        {
-            T *Qg = static_cast<T *>(a.Qp) + slot * C * DK;
-            T *Og = static_cast<T *>(a.Oi) + slot * C * DV;
-            Frag pf[KSTEPS];
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) pf[kk] = frag_at(sP + (kTile * tt + l16) * P_LD, kk);
-#pragma unroll
-            for (int it = 0; it < IPW; ++it) {
-                const int wi = wid + kIWaves * it;
-                floatx4 acc = zero4();
-                if (wi < NIW) {
-                    const int cc = wi / NT;
-                    const T *ob = sKT + (kTile * cc + l16) * KT_LD;
-#pragma unroll
-                    for (int kk = 0; kk < KSTEPS; ++kk)
-                        acc = M::mma(frag_at(ob, kk), pf[kk], acc);
-                    // q e^Gam = Q+ e^{r_I} (token tile tt)
-                    const int t = kTile * tt + l16, c0 = kTile * cc + 4 * grp;
-                    const T *qp = sQp + t * K_LD + c0;
-                    const float4 er = *reinterpret_cast<const float4 *>(sR + tt * DK + c0);
-                    store_frag4<T, DK>(Qg, t, c0, to_f32(qp[0]) * er.x - acc[0], to_f32(qp[1]) * er.y - acc[1],
-                                       to_f32(qp[2]) * er.z - acc[2], to_f32(qp[3]) * er.w - acc[3]);
-                } else if (wi < NITEM) {
-                    const int n = (wi - NIW) / NT;
-                    const T *ob = sVT + (kTile * n + l16) * KT_LD;
-#pragma unroll
-                    for (int kk = 0; kk < KSTEPS; ++kk)
-                        acc = M::mma(pf[kk], frag_at(ob, kk), acc);
-                    store4(Og + quad_off<DV>(tt, n, lane), acc[0], acc[1], acc[2], acc[3]);
-                }
-            }
-        }
-        __syncthreads();  // LDS is restaged for the next item
         item = nxt;
     }
 }
@@ -895,10 +880,11 @@ struct InterCfg {
 template <class T, int DK, int DV, int C, int BV>
 struct InterStage {
     using Cfg = InterCfg<T, DK, DV, C, BV>;
-    typename Cfg::Frag w[Cfg::KSD], q[Cfg::KSD];   // rows of W and Q' of this wave's row tile
+    typename Cfg::Frag w[Cfg::KSD], q[Cfg::KSD];   // rows of W and q e^Gam of this wave's row tile
     typename Cfg::Frag kt[Cfg::SPW][Cfg::KSC];     // rows of (k e^{Gam_last-Gam})^T per state tile
+    typename Cfg::Frag pf[Cfg::KSC];               // rows of P of this wave's row tile (zero past its blocks)
     floatx4 d[Cfg::SPW];                           // e^{Gam_last} per state-tile row
-    Quad<T> ut[Cfg::XPW], oi[Cfg::XPW];            // Ut, Oi at this lane's output positions
+    Quad<T> ut[Cfg::XPW];                          // Ut at this lane's output positions
 };
 
 template <class T, int DK, int DV, int C, int BV, int MODE>
@@ -908,10 +894,10 @@ __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, con
     using M = Mma<T>;
     const size_t slot = size_t(gc) * a.H + h;
     const T *W = static_cast<const T *>(a.W) + slot * C * DK;
-    const T *Qp = static_cast<const T *>(a.Qp) + slot * C * DK;
+    const T *Qg = static_cast<const T *>(a.Qg) + slot * C * DK;
     const T *KtT = static_cast<const T *>(a.KtT) + slot * DK * kpad<T>(C);
     const T *UtT = static_cast<const T *>(a.Ut) + slot * C * DV;  // quad order
-    const T *OiT = static_cast<const T *>(a.Oi) + slot * C * DV;  // quad order
+    const T *Ps = static_cast<const T *>(a.Ps) + slot * p_elems<T, C>();
     const float *D = a.D + slot * DK;
     const int I = wid % Cfg::NT;  // this wave's output row tile
     const int lane = l16 + 16 * grp;
@@ -919,7 +905,16 @@ __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, con
     for (int kk = 0; kk < Cfg::KSD; ++kk) {
         const size_t off = size_t(I * Cfg::KSD + kk) * (16 * M::K) + lane * M::KPL;
         st.w[kk] = M::load(W + off);
-        if (MODE == kFull) st.q[kk] = M::load(Qp + off);
+        if (MODE == kFull) st.q[kk] = M::load(Qg + off);
+    }
+    if (MODE == kFull) {
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSC; ++kk) {
+            const int kb = kk * M::K + grp * M::KPL;
+            st.pf[kk] = (kk < p_nk<T>(I) && kb < C)
+                            ? M::load(Ps + size_t(p_pre<T>(I) + kk) * (16 * M::K) + lane * M::KPL)
+                            : typename Cfg::Frag{};
+        }
     }
 #pragma unroll
     for (int i = 0; i < Cfg::SPW; ++i) {
@@ -941,7 +936,6 @@ __device__ __forceinline__ void inter_load(InterStage<T, DK, DV, C, BV> &st, con
         if (item < Cfg::NXI) {
             const int nn = item / Cfg::NT;
             if (MODE != kSumM) st.ut[i].load(UtT + quad_off<DV>(I, jb / kTile + nn, lane));
-            if (MODE == kFull) st.oi[i].load(OiT + quad_off<DV>(I, jb / kTile + nn, lane));
         }
     }
 }
@@ -973,10 +967,12 @@ __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &
     }
     __syncthreads();
 
-    // 2. X = W S and O = Q' S; U = Ut - X -> LDS; o = Oi + O
+    // 2. X = W S and O = (q e^Gam) S; U = Ut - X -> LDS
+    floatx4 oacc[XPW];
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
         const int item = wid + kWaves * i;
+        oacc[i] = zero4();
         if (item < NXI) {
             const int nn = item / NT;
             floatx4 ax = zero4(), ao = zero4();
@@ -987,7 +983,6 @@ __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &
                 ax = M::mma(cur.w[kk], sf, ax);
                 if (MODE == kFull) ao = M::mma(cur.q[kk], sf, ao);
             }
-            const int j = jb + kTile * nn + l16;
             const int t0 = kTile * I + 4 * grp;
             if (MODE == kSumM) {
                 store4(sUT + (kTile * nn + l16) * UT_LD + t0, -ax[0], -ax[1], -ax[2], -ax[3]);
@@ -995,16 +990,37 @@ __device__ __forceinline__ void inter_chunk(const InterStage<T, DK, DV, C, BV> &
                 store4(sUT + (kTile * nn + l16) * UT_LD + t0, cur.ut[i][0] - ax[0], cur.ut[i][1] - ax[1],
                        cur.ut[i][2] - ax[2], cur.ut[i][3] - ax[3]);
             }
-            if (MODE == kFull) {
+            oacc[i] = ao;
+        }
+    }
+    __syncthreads();
+
+    // o = (q e^Gam) S + P U, P's k-blocks up to this row tile's diagonal
+    if (MODE == kFull) {
+#pragma unroll
+        for (int i = 0; i < XPW; ++i) {
+            const int item = wid + kWaves * i;
+            if (item < NXI) {
+                const int nn = item / NT;
+                floatx4 acc = oacc[i];
+#pragma unroll
+                for (int kk = 0; kk < Cfg::KSC; ++kk) {
+                    if (kk < p_nk<T>(I)) {
+                        const int kb = kk * M::K + grp * M::KPL;
+                        const Frag bf = (kb < C) ? M::load(sUT + (kTile * nn + l16) * UT_LD + kb) : Frag{};
+                        acc = M::mma(cur.pf[kk], bf, acc);
+                    }
+                }
+                const int j = jb + kTile * nn + l16;
+                const int t0 = kTile * I + 4 * grp;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     T *dst = (t0 + r < len) ? og + (size_t(tok0 + t0 + r) * H + h) * DV + j : dummy;
-                    __builtin_nontemporal_store(from_f32<T>(cur.oi[i][r] + ao[r]), dst);
+                    __builtin_nontemporal_store(from_f32<T>(acc[r]), dst);
                 }
             }
         }
     }
-    __syncthreads();
 
     // 3. S = Diag(e^{Gam_last}) S + (k e^{Gam_last - Gam})^T U
 #pragma unroll
@@ -1185,8 +1201,8 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
 // issuing the next chunk's ~52 KiB of operand loads: every wave issues its
 // share at once and the compute unit's vector-memory pipeline takes them at
 // its own rate, while the products wait behind them in the same waves.  Here
-// loader waves copy each chunk's operands (W, Q', K~^T, e^{Gam_last} and this
-// block's Ut and Oi tiles, already in the order the products read them) into
+// loader waves copy each chunk's operands (W, q e^Gam, K~^T, P, e^{Gam_last}
+// and this block's Ut tiles, already in the order the products read them) into
 // one of two LDS buffers two chunks ahead, and the four compute waves read
 // them from LDS: their only global accesses are the o stores.  Both roles
 // pass the same barriers: one before the chain, then the two of each chunk.
@@ -1194,7 +1210,7 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
 // waves issue them (~41 B/clk from four waves, ~56 from sixteen), and with
 // twelve each loader thread holds five units a stage, so the kernel fits 128
 // VGPRs with no spill.  What bounds the chain is then the compute waves' own
-// latency per chunk (reads, S^T, X/O, state update, two barriers).
+// latency per chunk (S^T, X/O, state update and P U, two barriers).
 // ---------------------------------------------------------------------------
 constexpr int kWsLoaderWaves = 12;
 template <int DK, int DV, int C, int NLW>
@@ -1207,36 +1223,16 @@ struct WsBuf {
     static constexpr int oQ = oW + C * DK * 2;
     static constexpr int oK = oQ + C * DK * 2;
     static constexpr int oU = oK + DK * CP * 2;   // Ut tiles (I, this block), 256 values each
-    static constexpr int oO = oU + NT * 256 * 2;  // Oi tiles
-    static constexpr int oD = oO + NT * 256 * 2;  // e^{Gam_last}, fp32
+    static constexpr int oP = oU + NT * 256 * 2;  // P, lower-block operand order
+    static constexpr int oD = oP + p_elems<bf16, C>() * 2;  // e^{Gam_last}, fp32
     static constexpr int bytes = oD + DK * 4;
     static constexpr int units = bytes / 16;       // 16-byte copy units, laid end to end as above
-    static_assert(oQ % 16 == 0 && oK % 16 == 0 && oU % 16 == 0 && oO % 16 == 0 && oD % 16 == 0 && bytes % 16 == 0,
+    static_assert(oQ % 16 == 0 && oK % 16 == 0 && oU % 16 == 0 && oP % 16 == 0 && oD % 16 == 0 && bytes % 16 == 0,
                   "16-byte units");
     static constexpr int kLoaders = kWave * NLW;   // loader threads
     static constexpr int UPT = (units + kLoaders - 1) / kLoaders;  // units per loader thread
     static constexpr size_t lds_bytes = size_t(2) * bytes;
 };
-
-// Source of copy unit u (< units) of chunk slot (gc, h), for value block
-// nn0.  The units run over W, Q', K~^T (contiguous spans of the workspace),
-// then this block's Ut and Oi tiles (512-byte spans: 32 units a tile), then
-// e^{Gam_last}.  Selects, not branches, so every load is unconditional and
-// the compiler can count the loads in flight exactly.
-template <int DK, int DV, int C, int NLW>
-__device__ __forceinline__ const char *ws_src(const PrefillArgs &a, size_t slot, int nn0, int u) {
-    using B = WsBuf<DK, DV, C, NLW>;
-    constexpr int UW = C * DK * 2 / 16, UK = DK * B::CP * 2 / 16, UT = B::NT * 32;
-    const char *wq = static_cast<const char *>(u < UW ? a.W : a.Qp) + slot * (C * DK * 2) +
-                     size_t(u < UW ? u : u - UW) * 16;
-    const char *kt = static_cast<const char *>(a.KtT) + slot * (DK * B::CP * 2) + size_t(u - 2 * UW) * 16;
-    const int j = u - 2 * UW - UK;               // unit within this block's Ut, Oi tiles
-    const int jt = j < UT ? j : j - UT;
-    const char *uo = static_cast<const char *>(j < UT ? a.Ut : a.Oi) + slot * (C * DV * 2) +
-                     (size_t((jt / 32) * (DV / 16) + nn0) * 256 + (jt % 32) * 8) * 2;
-    const char *d = reinterpret_cast<const char *>(a.D + slot * DK) + size_t(min(j - 2 * UT, DK / 4 - 1)) * 16;
-    return u < 2 * UW ? wq : (u < 2 * UW + UK ? kt : (j < 2 * UT ? uo : d));
-}
 
 // Copy unit lt + kLoaders * i of a chunk; units past the end repeat the last.
 template <int DK, int DV, int C, int NLW, int i>
@@ -1245,11 +1241,61 @@ __device__ __forceinline__ int ws_unit(int lt) {
     return min(lt + B::kLoaders * i, B::units - 1);
 }
 
+// Where a loader thread's units come from.  The units run over W, q e^Gam,
+// K~^T (contiguous spans of a chunk slot), this block's Ut tiles (512-byte
+// spans: 32 units a tile), P and e^{Gam_last} (contiguous).  Every region
+// starts at a multiple of 64 units and a loader wave's step i covers 64
+// consecutive units, so the region of step i is uniform over the wave: its
+// base and per-slot stride sit in scalar registers, and a lane keeps only
+// its byte offset inside the slot's span, which is the same for every chunk.
+template <int DK, int DV, int C, int NLW>
+struct WsPlan {
+    using B = WsBuf<DK, DV, C, NLW>;
+    static constexpr int UW = C * DK * 2 / 16, UK = DK * B::CP * 2 / 16, UT = B::NT * 32;
+    static constexpr int UP = p_elems<bf16, C>() * 2 / 16, UD = DK * 4 / 16;
+    static constexpr int R1 = UW, R2 = 2 * UW, R3 = R2 + UK, R4 = R3 + UT, R5 = R4 + UP;
+    static_assert(R1 % kWave == 0 && R2 % kWave == 0 && R3 % kWave == 0 && R4 % kWave == 0 && R5 % kWave == 0 &&
+                      B::kLoaders % kWave == 0 && R5 + UD == B::units,
+                  "regions of whole loader waves");
+    typedef const __attribute__((address_space(1))) char gchar;  // global memory: vector-memory loads only
+    const gchar *base[B::UPT];  // region base (uniform)
+    unsigned stride[B::UPT];    // region bytes per chunk slot (uniform)
+    unsigned voff[B::UPT];      // this lane's byte offset inside a slot's span
+
+    template <int i>
+    __device__ __forceinline__ void init_unit(const PrefillArgs &a, int lt, int nn0) {
+        if constexpr (i < B::UPT) {
+            const int u = ws_unit<DK, DV, C, NLW, i>(lt);
+            const int u0 = __builtin_amdgcn_readfirstlane(u);
+            const int r = (u0 >= R1) + (u0 >= R2) + (u0 >= R3) + (u0 >= R4) + (u0 >= R5);
+            const void *bases[6] = {a.W, a.Qg, a.KtT, a.Ut, a.Ps, a.D};  // all in global memory
+            constexpr unsigned strides[6] = {C * DK * 2, C * DK * 2, DK * B::CP * 2, C * DV * 2,
+                                             p_elems<bf16, C>() * 2, DK * 4};
+            constexpr int starts[6] = {0, R1, R2, R3, R4, R5};
+            // (read back through readfirstlane: the values are uniform, and the
+            // compiler then keeps them, and each slot's span base, in scalar
+            // registers; the loads take the lane offset as a 32-bit VGPR)
+            const unsigned long long b = reinterpret_cast<unsigned long long>(bases[r]);
+            const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(b)),
+                           hi = __builtin_amdgcn_readfirstlane(unsigned(b >> 32));
+            base[i] = reinterpret_cast<const gchar *>((static_cast<unsigned long long>(hi) << 32) | lo);
+            stride[i] = __builtin_amdgcn_readfirstlane(strides[r]);
+            const int j = u - starts[r];
+            voff[i] = r == 3 ? unsigned(((j / 32) * (DV / 16) + nn0) * 512 + (j % 32) * 16) : unsigned(j * 16);
+            init_unit<i + 1>(a, lt, nn0);
+        }
+    }
+    __device__ __forceinline__ u32x4 fetch(int i, size_t slot) const {
+        const gchar *span = base[i] + slot * stride[i];
+        return *reinterpret_cast<const __attribute__((address_space(1))) u32x4 *>(span + voff[i]);
+    }
+};
+
 template <int DK, int DV, int C, int NLW, int i>
-__device__ __forceinline__ void ws_fetch_unit(u32x4 *r, const PrefillArgs &a, size_t slot, int nn0, int lt) {
+__device__ __forceinline__ void ws_fetch_unit(u32x4 *r, const WsPlan<DK, DV, C, NLW> &pl, size_t slot) {
     if constexpr (i < WsBuf<DK, DV, C, NLW>::UPT) {
-        r[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, NLW>(a, slot, nn0, ws_unit<DK, DV, C, NLW, i>(lt)));
-        ws_fetch_unit<DK, DV, C, NLW, i + 1>(r, a, slot, nn0, lt);
+        r[i] = pl.fetch(i, slot);
+        ws_fetch_unit<DK, DV, C, NLW, i + 1>(r, pl, slot);
     }
 }
 
@@ -1266,13 +1312,12 @@ __device__ __forceinline__ void ws_put_unit(const u32x4 *r, unsigned char *dst, 
 // requested into rf.  Alternating the two keeps the LDS and the
 // vector-memory pipelines busy together.
 template <int DK, int DV, int C, int NLW, int i, int iend>
-__device__ __forceinline__ void ws_step(const u32x4 *rp, unsigned char *dst, u32x4 *rf, const PrefillArgs &a,
-                                        size_t slot, int nn0, int lt) {
+__device__ __forceinline__ void ws_step(const u32x4 *rp, unsigned char *dst, u32x4 *rf,
+                                        const WsPlan<DK, DV, C, NLW> &pl, size_t slot, int lt) {
     if constexpr (i < iend) {
-        const int u = ws_unit<DK, DV, C, NLW, i>(lt);
-        *reinterpret_cast<u32x4 *>(dst + u * 16) = rp[i];
-        rf[i] = *reinterpret_cast<const u32x4 *>(ws_src<DK, DV, C, NLW>(a, slot, nn0, u));
-        ws_step<DK, DV, C, NLW, i + 1, iend>(rp, dst, rf, a, slot, nn0, lt);
+        *reinterpret_cast<u32x4 *>(dst + ws_unit<DK, DV, C, NLW, i>(lt) * 16) = rp[i];
+        rf[i] = pl.fetch(i, slot);
+        ws_step<DK, DV, C, NLW, i + 1, iend>(rp, dst, rf, pl, slot, lt);
     }
 }
 
@@ -1285,7 +1330,8 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
     constexpr int NRT = Cfg::NRT, NSI = Cfg::NSI, SPW = Cfg::SPW, XPW = Cfg::XPW;
     constexpr int NB = DV / BV;
     constexpr int PT = 8;
-    static_assert(Cfg::NCT == 1 && XPW == 1, "one 16-column tile per block, one output tile per wave");
+    static_assert(Cfg::NCT == 1 && XPW == 1 && C % M::K == 0,
+                  "one 16-column tile per block, one output tile per wave, whole k-steps over the chunk");
     __shared__ __align__(16) bf16 sST[BV * (DK + PT)];
     __shared__ __align__(16) bf16 sUT[BV * (C + PT)];
     extern __shared__ __align__(16) unsigned char wsbuf[];
@@ -1326,9 +1372,11 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         const int lt = tid - kThreads;
         constexpr int UPT = B::UPT;
         u32x4 st[3][UPT];
+        WsPlan<DK, DV, C, NLW> pl;
+        pl.template init_unit<0>(a, lt, nn0);
         auto fetch = [&](u32x4 (&r)[UPT], int c) {
             const size_t slot = size_t(c_begin + min(c, nc - 1)) * H + h;
-            ws_fetch_unit<DK, DV, C, NLW, 0>(r, a, slot, nn0, lt);
+            ws_fetch_unit<DK, DV, C, NLW, 0>(r, pl, slot);
         };
         auto put = [&](const u32x4 (&r)[UPT], int buf) { ws_put_unit<DK, DV, C, NLW, 0>(r, wsbuf + buf * B::bytes, lt); };
         // chunk x lives in register stage x % 3 and LDS buffer x & 1.  During
@@ -1354,9 +1402,9 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
                 unsigned char *dst = wsbuf + ((c + s) & 1) * B::bytes;
                 const size_t sl = slot_of(c + s + 4);
                 __syncthreads();  // A
-                ws_step<DK, DV, C, NLW, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], pl, sl, lt);
                 __syncthreads();  // B
-                ws_step<DK, DV, C, NLW, HALF, UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, HALF, UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], pl, sl, lt);
             }
         }
 #pragma unroll
@@ -1365,9 +1413,9 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
                 unsigned char *dst = wsbuf + ((c + s) & 1) * B::bytes;
                 const size_t sl = slot_of(c + s + 4);
                 __syncthreads();
-                ws_step<DK, DV, C, NLW, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, 0, HALF>(st[(s + 2) % 3], dst, st[(s + 1) % 3], pl, sl, lt);
                 __syncthreads();
-                ws_step<DK, DV, C, NLW, HALF, UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], a, sl, nn0, lt);
+                ws_step<DK, DV, C, NLW, HALF, UPT>(st[(s + 2) % 3], dst, st[(s + 1) % 3], pl, sl, lt);
             }
         }
         return;
@@ -1389,39 +1437,125 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
                 S[i][r] = a.h0[sbase + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16];
         }
     }
-    bf16 *og = static_cast<bf16 *>(a.o);
-    bf16 *dummy = static_cast<bf16 *>(a.dummy) + tid;
-    __syncthreads();  // chunk 0 staged
-    for (int c = 0; c < nc; ++c) {
-        const unsigned char *buf = wsbuf + (c & 1) * B::bytes;
-        InterStage<bf16, DK, DV, C, BV> cur;
-        const int I = wid % Cfg::NT;
+    // Reads of a chunk's operands are split around the two barriers so that
+    // none of them sits on the path S^T -> X/O -> S: W and q e^Gam of chunk
+    // c + 1 (staged in buffer (c + 1) & 1 before barrier A of chunk c) are
+    // read during chunk c's state update, and the rest of chunk c (Ut, K~^T,
+    // P, e^{Gam_last}; rewritten by the loader only after barrier B) during
+    // its X/O products.
+    static_assert(B::UPT / 2 * B::kLoaders <= B::oK / 16,
+                  "the loader's first half-step (after barrier A) rewrites only W and q e^Gam units");
+    typedef M::Frag Frag;
+    constexpr int ST_LD = DK + PT, UT_LD = C + PT;
+    const int I = wid % Cfg::NT;
+    const int t0 = kTile * I + 4 * grp;
+    Frag w[Cfg::KSD], q[Cfg::KSD];
+    auto read_wq = [&](const unsigned char *buf) {
 #pragma unroll
         for (int kk = 0; kk < Cfg::KSD; ++kk) {
             const int off = ((I * Cfg::KSD + kk) * (16 * M::K) + lane * M::KPL) * 2;
-            cur.w[kk] = *reinterpret_cast<const bf16x8 *>(buf + B::oW + off);
-            cur.q[kk] = *reinterpret_cast<const bf16x8 *>(buf + B::oQ + off);
+            w[kk] = *reinterpret_cast<const bf16x8 *>(buf + B::oW + off);
+            q[kk] = *reinterpret_cast<const bf16x8 *>(buf + B::oQ + off);
         }
+    };
+    // byte offset of this lane's first o value from its chunk's first row
+    // (the next three are a row apart)
+    const int ooff = (t0 * H * DV + jb + l16) * 2, orow = H * DV * 2;
+    // S^T -> LDS in bf16, for the next chunk's products
+    auto put_st = [&]() {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int item = wid + kWaves * i;
+            if (item < NSI) {
+                const int m = item % NRT;
+                store4(sST + l16 * ST_LD + kTile * m + 4 * grp, S[i][0], S[i][1], S[i][2], S[i][3]);
+            }
+        }
+    };
+    __syncthreads();  // chunks 0 and 1 staged
+    if (nc > 0) read_wq(wsbuf);
+    put_st();
+    for (int c = 0; c < nc; ++c) {
+        const unsigned char *buf = wsbuf + (c & 1) * B::bytes;
+        const int tok0 = tok_start + c * C;
+        const int len = max(0, min(C, tok_end - tok0));
+        __syncthreads();  // A: S^T of this chunk's entering state is in LDS
+
+        // 2. X = W S, O = (q e^Gam) S; U = Ut - X -> LDS.  The rest of this
+        // chunk's operands are read alongside.
+        floatx4 ax = zero4(), ao = zero4();
+        Frag sf[Cfg::KSD];
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSD; ++kk) sf[kk] = M::load(sST + l16 * ST_LD + kk * M::K + grp * M::KPL);
+        Quad<bf16> ut;
+        ut.load(reinterpret_cast<const bf16 *>(buf + B::oU) + I * 256 + lane * 4);
+        Frag pf[Cfg::KSC];  // rows of P of tile I; its k-blocks past the diagonal are zero
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSC; ++kk)
+            pf[kk] = kk < p_nk<bf16>(I) ? *reinterpret_cast<const bf16x8 *>(
+                                              buf + B::oP + ((p_pre<bf16>(I) + kk) * (16 * M::K) + lane * M::KPL) * 2)
+                                        : bf16x8{};
+        Frag kt[SPW][Cfg::KSC];
+        floatx4 d[SPW];
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int item = wid + kWaves * i;
             if (item < NSI) {
                 const int m = item % NRT;
 #pragma unroll
-                for (int kk = 0; kk < Cfg::KSC; ++kk) {
-                    const int kb = kk * M::K + grp * M::KPL;
-                    cur.kt[i][kk] = (kb < C) ? *reinterpret_cast<const bf16x8 *>(
-                                                   buf + B::oK + ((m * Cfg::KSC + kk) * (16 * M::K) + lane * M::KPL) * 2)
-                                             : bf16x8{};
-                }
-                cur.d[i] = *reinterpret_cast<const floatx4 *>(buf + B::oD + (kTile * m + 4 * grp) * 4);
+                for (int kk = 0; kk < Cfg::KSC; ++kk)
+                    kt[i][kk] = *reinterpret_cast<const bf16x8 *>(
+                        buf + B::oK + ((m * Cfg::KSC + kk) * (16 * M::K) + lane * M::KPL) * 2);
+                d[i] = *reinterpret_cast<const floatx4 *>(buf + B::oD + (kTile * m + 4 * grp) * 4);
             }
         }
-        cur.ut[0].load(reinterpret_cast<const bf16 *>(buf + B::oU) + I * 256 + lane * 4);
-        cur.oi[0].load(reinterpret_cast<const bf16 *>(buf + B::oO) + I * 256 + lane * 4);
-        const int tok0 = tok_start + c * C;
-        inter_chunk<bf16, DK, DV, C, BV, kFull>(cur, S, sST, sUT, og, dummy, tok0, min(C, tok_end - tok0), H, h, wid,
-                                                grp, l16, jb);
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSD; ++kk) {
+            ax = M::mma(w[kk], sf[kk], ax);
+            ao = M::mma(q[kk], sf[kk], ao);
+        }
+        store4(sUT + l16 * UT_LD + t0, ut[0] - ax[0], ut[1] - ax[1], ut[2] - ax[2], ut[3] - ax[3]);
+        __syncthreads();  // B
+
+        // 3. S = Diag(e^{Gam_last}) S + (k e^{Gam_last - Gam})^T U, then its
+        // S^T for the next chunk (this chunk's reads of S^T ended before
+        // barrier B), then o = (q e^Gam) S + P U on the same U fragments,
+        // off the path to the next chunk.  The next chunk's W, q e^Gam are
+        // requested behind the U fragments (no branch: after the last chunk
+        // the read is of a stale buffer, unused).
+        Frag uf[Cfg::KSC];
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSC; ++kk) uf[kk] = M::load(sUT + l16 * UT_LD + kk * M::K + grp * M::KPL);
+        read_wq(wsbuf + ((c + 1) & 1) * B::bytes);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int item = wid + kWaves * i;
+            if (item < NSI) {
+                floatx4 acc = S[i] * d[i];
+#pragma unroll
+                for (int kk = 0; kk < Cfg::KSC; ++kk) acc = M::mma(kt[i][kk], uf[kk], acc);
+                S[i] = acc;
+            }
+        }
+        put_st();
+        __builtin_amdgcn_sched_barrier(0);  // keep P U behind the state's path
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSC; ++kk) ao = M::mma(pf[kk], uf[kk], ao);
+        {
+            // o rows of this chunk through a buffer resource whose range ends
+            // at row len: stores of rows past the sequence's end are dropped.
+            // The whole byte offset is the per-lane one, which the range check
+            // covers (the range is uniform; readfirstlane keeps the resource
+            // in scalar registers)
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<bf16 *>(a.o) + (size_t(tok0) * H + h) * DV, (short)0,
+                __builtin_amdgcn_readfirstlane(len * H * DV * 2), 0x00020000);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bf16 v = static_cast<bf16>(ao[r]);
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), orsrc, ooff + r * orow, 0, 0);
+            }
+        }
         inter_ckpt<bf16, DK, DV, C, BV>(a, S, n, h, c, tok0 + C <= tok_end, wid, grp, l16, jb);
     }
     if (a.ht) {
@@ -1526,14 +1660,16 @@ __device__ __forceinline__ void chain_ckpt(const PrefillArgs &a, const floatx4 (
 // the 16x16x32 bf16 MFMA with a permuted contraction order: slot j < 4 of a
 // lane's 8 operand values is row 4 grp + j of tile 2p, slot j >= 4 row
 // 4 grp + j - 4 of tile 2p + 1.  With that order the B operand of X = W S and
-// O = Q' S is just the lane's own accumulators of tiles 2p, 2p + 1, and
-// U = Ut - X (token tiles 2q, 2q + 1) is the B operand of S += K~^T U: the
-// state and U never leave the wave.  The A operands every wave needs — W,
-// Q', K~^T — are staged per chunk in LDS in the same permuted order (one
-// 16-byte read per operand), with e^{Gam_last}, double-buffered, from a
-// ring of NS register stages loaded NS - 1 chunks ahead; one barrier per
-// chunk (the d = 128 output chains: one buffer, two barriers, see ONE).  The loop runs whole NS-chunk groups; chunks past the chain's end
-// are inactive (state kept, nothing stored): branch-free, static ring indices.
+// O = (q e^Gam) S is just the lane's own accumulators of tiles 2p, 2p + 1,
+// and U = Ut - X (token tiles 2q, 2q + 1) is the B operand of both
+// S += K~^T U and o = O + P U: the state and U never leave the wave.  The A
+// operands every wave needs — W, q e^Gam, K~^T, P — are staged per chunk in
+// LDS in the same permuted order (one 16-byte read per operand), with
+// e^{Gam_last}, double-buffered, from a ring of NS register stages loaded
+// NS - 1 chunks ahead; one barrier per chunk (the d = 128 output chains: one
+// buffer, two barriers, see ONE).  The loop runs whole NS-chunk groups;
+// chunks past the chain's end are inactive (state kept, nothing stored):
+// branch-free, static ring indices.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int C, int NWV, int MODE>
 struct ChainCfg {
@@ -1542,11 +1678,15 @@ struct ChainCfg {
     static constexpr int NT = C / kTile, MT = DK / kTile;
     static constexpr int NQ = (NT + 1) / 2, MP = MT / 2;    // 32-wide token / dk slices
     static constexpr int CP = kpad<bf16>(C);                // K~^T row length (operand order)
-    static constexpr bool HAS_Q = MODE == kFull;
+    static constexpr bool HAS_Q = MODE == kFull;           // q e^Gam and P: outputs
     static constexpr int W_EL = C * DK, K_EL = DK * CP;     // bf16 elements per chunk
     static constexpr int PW = W_EL * 2 / 16, PK = K_EL * 2 / 16, PD = DK * 4 / 16;  // 16-byte pieces
+    static constexpr int PP = HAS_Q ? p_elems<bf16, C>() * 2 / 16 : 0;
     static constexpr int KB = PW * (HAS_Q ? 2 : 1);        // first K~^T piece
-    static constexpr int P = KB + PK + PD;
+    static constexpr int PB = KB + PK;                      // first P piece
+    static constexpr int DB = PB + PP;                      // first e^{Gam_last} piece
+    static constexpr int P = DB + PD;
+    static_assert(PW % 64 == 0 && PK % 64 == 0 && PP % 64 == 0, "whole 1 KiB operand blocks");
     static constexpr int PPT = (P + NTHR - 1) / NTHR;       // pieces per thread
     static constexpr int BUF = PPT * NTHR * 16;             // bytes per LDS buffer (padded)
     // d = 128 output chains: one LDS buffer and two register stages, so that
@@ -1563,20 +1703,22 @@ template <int DK, int DV, int C, int NWV, int MODE>
 struct ChainStage {
     using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
     u32x4 stg[Cfg::PPT];                  // this thread's pieces of the staged operands
-    bf16x4 ut[Cfg::NT], oi[Cfg::NT];      // Ut, Oi at this lane's positions of its column block
+    bf16x4 ut[Cfg::NT];                   // Ut at this lane's positions of its column block
 };
 
 // Loads one chunk's stage: 16-byte pieces p = tid + NTHR i of the operand-
-// order W, Q', K~^T and of e^{Gam_last}, laid end to end; Ut and Oi (quad
-// order) at this lane's positions.  Bases are uniform (scalar registers).
+// order W, q e^Gam, K~^T, of P (lower-block order) and of e^{Gam_last}, laid
+// end to end; Ut (quad order) at this lane's positions.  Bases are uniform
+// (scalar registers).
 template <int DK, int DV, int C, int NWV, int MODE>
 __device__ __forceinline__ void chain_load(ChainStage<DK, DV, C, NWV, MODE> &st, const PrefillArgs &a, int gc, int h,
                                            int tid, int loff, int nblk, bool isM) {
     using Cfg = ChainCfg<DK, DV, C, NWV, MODE>;
     const size_t slot = size_t(gc) * a.H + h;
     const char *W = static_cast<const char *>(a.W) + slot * Cfg::W_EL * 2;
-    const char *Q = static_cast<const char *>(a.Qp) + slot * Cfg::W_EL * 2;
+    const char *Q = static_cast<const char *>(a.Qg) + slot * Cfg::W_EL * 2;
     const char *K = static_cast<const char *>(a.KtT) + slot * Cfg::K_EL * 2;
+    const char *Ps = static_cast<const char *>(a.Ps) + slot * p_elems<bf16, C>() * 2;
     const char *D = reinterpret_cast<const char *>(a.D + slot * DK);
 #pragma unroll
     for (int i = 0; i < Cfg::PPT; ++i) {
@@ -1584,19 +1726,16 @@ __device__ __forceinline__ void chain_load(ChainStage<DK, DV, C, NWV, MODE> &st,
         const char *src;
         if (p < Cfg::PW) src = W + p * 16;
         else if (Cfg::HAS_Q && p < Cfg::KB) src = Q + (p - Cfg::PW) * 16;
-        else if (p < Cfg::KB + Cfg::PK) src = K + (p - Cfg::KB) * 16;
-        else src = D + (p - Cfg::KB - Cfg::PK) * 16;
+        else if (p < Cfg::PB) src = K + (p - Cfg::KB) * 16;
+        else if (Cfg::HAS_Q && p < Cfg::DB) src = Ps + (p - Cfg::PB) * 16;
+        else src = D + (p - Cfg::DB) * 16;
         st.stg[i] = *reinterpret_cast<const u32x4 *>(src);
     }
     if (MODE != kSumM && !(MODE == kSumBM && isM)) {
         // quad order: tile (I, nblk) is 256 values, lane l holds 4 of them
         const char *U = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.Ut) + slot * C * DV + nblk * 256);
-        const char *O = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.Oi) + slot * C * DV + nblk * 256);
 #pragma unroll
-        for (int I = 0; I < Cfg::NT; ++I) {
-            st.ut[I] = *reinterpret_cast<const bf16x4 *>(U + I * (DV / kTile) * 512 + loff);
-            if (MODE == kFull) st.oi[I] = *reinterpret_cast<const bf16x4 *>(O + I * (DV / kTile) * 512 + loff);
-        }
+        for (int I = 0; I < Cfg::NT; ++I) st.ut[I] = *reinterpret_cast<const bf16x4 *>(U + I * (DV / kTile) * 512 + loff);
     }
 }
 
@@ -1604,7 +1743,8 @@ __device__ __forceinline__ void chain_load(ChainStage<DK, DV, C, NWV, MODE> &st,
 // ln = l16 + 16 q of its block: 8 consecutive k from 8 q) goes, as two
 // 8-byte halves, to the permuted order: the half with k offset c = 8 q + 4 h
 // lands in lane l16 + 16 g of the same block, slot c / 16, with g = (c % 16)
-// / 4.  K~^T columns past the chunk (the pad of a 16-token chunk) become 0.
+// / 4.  K~^T and P columns past the chunk (the pad of a 16-token chunk)
+// become 0.
 template <int DK, int DV, int C, int NWV, int MODE>
 __device__ __forceinline__ void chain_stage_write(unsigned char *buf, const ChainStage<DK, DV, C, NWV, MODE> &st,
                                                   int tid) {
@@ -1613,7 +1753,7 @@ __device__ __forceinline__ void chain_stage_write(unsigned char *buf, const Chai
     for (int i = 0; i < Cfg::PPT; ++i) {
         const int p = tid + Cfg::NTHR * i;
         const u32x4 v = st.stg[i];
-        if (p >= Cfg::KB + Cfg::PK) {  // e^{Gam_last} and the padding: as is
+        if (p >= Cfg::DB) {  // e^{Gam_last} and the padding: as is
             *reinterpret_cast<u32x4 *>(buf + p * 16) = v;
             continue;
         }
@@ -1621,7 +1761,7 @@ __device__ __forceinline__ void chain_stage_write(unsigned char *buf, const Chai
         const int s0 = q >> 1;                                      // slot of both halves
         const int g0 = 2 * (q & 1);                                 // lane group of half 0; half 1: g0 + 1
         u32x2 lo{v[0], v[1]}, hi{v[2], v[3]};
-        if (C < 32 && p >= Cfg::KB && s0 == 1) lo = hi = u32x2{0u, 0u};  // K~^T pad columns
+        if (C < 32 && p >= Cfg::KB && s0 == 1) lo = hi = u32x2{0u, 0u};  // K~^T, P pad columns
         unsigned char *base = buf + blk * 1024 + l16 * 16 + 8 * s0;
         *reinterpret_cast<u32x2 *>(base + (16 * g0) * 16) = lo;
         *reinterpret_cast<u32x2 *>(base + (16 * (g0 + 1)) * 16) = hi;
@@ -1729,7 +1869,7 @@ void kda_chain_kernel(PrefillArgs a) {
                                                         tid);
             const int bsel = ONE ? 0 : (s & 1);
             const unsigned char *ra = sbuf[0] + opaque(bsel * Cfg::BUF + 16 * lane);
-            const unsigned char *rd = sbuf[0] + opaque(bsel * Cfg::BUF + (Cfg::KB + Cfg::PK) * 16 + 16 * grp);
+            const unsigned char *rd = sbuf[0] + opaque(bsel * Cfg::BUF + Cfg::DB * 16 + 16 * grp);
             const Stage &cur = st[s];
 
             // B operands from the state: tiles 2p, 2p + 1
@@ -1755,6 +1895,7 @@ void kda_chain_kernel(PrefillArgs a) {
             M::Frag ub[NQ];
 #pragma unroll
             for (int qq = 0; qq < NQ; ++qq) ub[qq] = M::Frag{};
+            floatx4 oacc[NT];
 #pragma unroll
             for (int I = 0; I < NT; ++I) {
                 floatx4 xa = zero4(), oa = zero4();
@@ -1768,10 +1909,21 @@ void kda_chain_kernel(PrefillArgs a) {
                 for (int r = 0; r < 4; ++r)
                     ub[I >> 1][4 * (I & 1) + r] =
                         static_cast<bf16>((isM ? 0.f : static_cast<float>(cur.ut[I][r])) - xa[r]);
-                if (MODE == kFull) {
+                oacc[I] = oa;
+            }
+            if (MODE == kFull) {
+                // o = (q e^Gam) S + P U: P's kept k-blocks of row tile I, in
+                // the same permuted order as U
+#pragma unroll
+                for (int I = 0; I < NT; ++I) {
+                    floatx4 acc = oacc[I];
+#pragma unroll
+                    for (int qq = 0; qq < p_nk<bf16>(I); ++qq)
+                        acc = M::mma(*reinterpret_cast<const M::Frag *>(ra + Cfg::PB * 16 + (p_pre<bf16>(I) + qq) * 1024),
+                                     ub[qq], acc);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const bf16 v = static_cast<bf16>(static_cast<float>(cur.oi[I][r]) + oa[r]);
+                        const bf16 v = static_cast<bf16>(acc[r]);
                         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), orsrc,
                                                               ((kTile * I + 4 * grp + r) * H * DV + l16) * 2, 0, 0);
                     }

@@ -38,9 +38,12 @@ def test_status_strings():
 
 def test_workspace_size():
     w1 = kda.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 1, 64, BF16)
-    # W, Q', K~^T, Ut, Oi (bf16) + decay (fp32) per (chunk, head), plus the chunk map
+    # W, q e^Gam, K~^T, Ut (bf16), the scores P in 16 x 32 blocks up to each
+    # 16-row tile's diagonal (1 + 1 + 2 + 2 blocks, bf16) and the decay (fp32)
+    # per (chunk, head), plus the chunk map
     slots = (8192 // 64 + 1) * 32
-    assert w1 >= slots * (5 * 64 * 128 * 2 + 128 * 4)
+    per_slot = 4 * 64 * 128 * 2 + 6 * 16 * 32 * 2 + 128 * 4
+    assert slots * per_slot <= w1 < slots * per_slot + (1 << 20)
     assert w1 % 256 == 0
     w2 = kda.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64, 64, BF16)
     assert w2 > w1
@@ -64,7 +67,7 @@ def test_workspace_segment_states_follow_the_plan():
     (segment, head), the two summaries and the scanned incoming state.  The
     H = 32, T = 8192 call (128 chains) and a sequence under 64 chunks run one
     chain per head and add none."""
-    per_slot = 5 * 64 * 128 * 2 + 128 * 4
+    per_slot = 4 * 64 * 128 * 2 + 6 * 16 * 32 * 2 + 128 * 4
     st = 128 * 128 * 4
 
     def extra(T, H):

@@ -83,7 +83,9 @@ __device__ __forceinline__ floatx4 mma_f32(float a, float b, floatx4 c) {
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 // Natural exponential through the hardware base-2 exponential.
-__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float exp_e(float x) { return exp2_hw(x * kLog2e); }
 
 // Store four consecutive values of type T (8 bytes for bf16, 16 for fp32).
 __device__ __forceinline__ void store4(bf16 *p, float a, float b, float c, float d) {

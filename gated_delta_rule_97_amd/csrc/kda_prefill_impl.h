@@ -461,12 +461,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     T *sKp = reinterpret_cast<T *>(smem + Ly::oKp);    // k e^{Gam - r_I}   (<= 1)
     T *sKm = reinterpret_cast<T *>(smem + Ly::oKm);    // k e^{r_I - Gam}   (<= e^80)
     T *sQp = reinterpret_cast<T *>(smem + Ly::oQp);    // q e^{Gam - r_I}   (<= 1)
-    T *sKT = reinterpret_cast<T *>(smem + Ly::oKT);    // (beta k e^Gam)^T, later W^T
-    T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);    // (beta v)^T,       later Ut^T
+    T *sKT = reinterpret_cast<T *>(smem + Ly::oKT);    // (beta k e^Gam)^T
+    T *sVT = reinterpret_cast<T *>(smem + Ly::oVT);    // (beta v)^T
     float *sA = reinterpret_cast<float *>(smem + Ly::oA);
     float *sL = reinterpret_cast<float *>(smem + Ly::oL);
     float *sY = reinterpret_cast<float *>(smem + Ly::oY);
-    float *sTot = reinterpret_cast<float *>(smem + Ly::oTot);  // segment decay totals, then their
+    float *sTot = reinterpret_cast<float *>(smem + Ly::oTot);  // segment decay totals (base 2), then their
                                                                // exclusive prefix     [NSEG + 1][DK]
     float *sF = reinterpret_cast<float *>(smem + Ly::oF);      // e^{r_I - r_J}, J < I    [NOFF][DK]
     float *sR = reinterpret_cast<float *>(smem + Ly::oR);      // e^{r_I}                 [NT][DK]
@@ -515,7 +515,9 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
             if (lane < C) sB[lane] = lane < blen ? bnx : 0.f;
         }
 
-        // ---- cumulative log-decay: per-thread partial sums over kSR tokens ----
+        // ---- cumulative log-decay: per-thread partial sums over kSR tokens.
+        //      The decays are taken to base 2 once, in place (g log2(e)), so
+        //      every factor below is one hardware exp2 of a difference ----
         const int rt = role_tid<T, DK, DV, C>(tid);
         if (rt < R::NG) {
             const int cg = tid % (DK / 4), sg = tid / (DK / 4);
@@ -523,7 +525,11 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < kSR; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) run[c] += __uint_as_float(in.raw[r][c]);
+                for (int c = 0; c < 4; ++c) {
+                    const float g2 = __uint_as_float(in.raw[r][c]) * kLog2e;
+                    in.raw[r][c] = __float_as_uint(g2);
+                    run[c] += g2;
+                }
             *reinterpret_cast<float4 *>(sTot + sg * DK + 4 * cg) = make_float4(run[0], run[1], run[2], run[3]);
         }
         __syncthreads();
@@ -545,12 +551,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     run += x[s2];
                 }
                 sTot[NSEG * DK + c] = run;
-                a.D[slot * DK + c] = exp_e(run);
+                a.D[slot * DK + c] = exp2_hw(run);
 #pragma unroll
                 for (int I2 = 0; I2 < NT; ++I2) {
-                    sR[I2 * DK + c] = exp_e(rr[I2]);
+                    sR[I2 * DK + c] = exp2_hw(rr[I2]);
 #pragma unroll
-                    for (int J2 = 0; J2 < I2; ++J2) sF[(I2 * (I2 - 1) / 2 + J2) * DK + c] = exp_e(rr[I2] - rr[J2]);
+                    for (int J2 = 0; J2 < I2; ++J2) sF[(I2 * (I2 - 1) / 2 + J2) * DK + c] = exp2_hw(rr[I2] - rr[J2]);
                 }
             }
         } else if (!Ly::COMPACT && rt >= R::NG) {
@@ -591,13 +597,13 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                     const float kv = raw_get<T>(in.raw + kSR, (sizeof(T) == 2 ? 8 * r : 4 * r) + c);
                     const float qv = sizeof(T) == 2 ? raw_get<T>(in.raw + kSR, 8 * r + 4 + c)
                                                     : raw_get<T>(in.raw + 2 * kSR, 4 * r + c);
-                    const float e = exp_e(x);    // <= 1
-                    const float ei = exp_e(-x);  // <= e^80
+                    const float e = exp2_hw(x);    // <= 1
+                    const float ei = exp2_hw(-x);  // <= e^80
                     kp[c] = kv * e;
                     qp[c] = qv * e;
                     km[c] = kv * ei;
                     bke[c].set(r, bt[r] * er[c] * kp[c]);
-                    ktv[c].set(r, kv * exp_e(glr[c] - x));  // <= 1
+                    ktv[c].set(r, kv * exp2_hw(glr[c] - x));  // <= 1
                 }
                 store4(sKp + t * K_LD + c0, kp[0], kp[1], kp[2], kp[3]);
                 store4(sKm + t * K_LD + c0, km[0], km[1], km[2], km[3]);

@@ -136,7 +136,7 @@ int kda_chunk_prefill(const void *q, const void *k, const void *v,
  * that every GPU it runs on holds until the process ends; the call itself
  * allocates nothing.  Sizes whose workspace (kda_chunk_prefill_workspace_size)
  * exceeds it return KDA_ERR_TOO_LARGE before anything is enqueued; at d = 128
- * and chunk 64 that is about 1,600 (chunk, head) slots, e.g. 2048 tokens x 32
+ * and chunk 64 that is about 1,800 (chunk, head) slots, e.g. 2048 tokens x 32
  * heads.  Every call on one GPU shares that GPU's array: calls that overlap in
  * time on one GPU (different streams or host threads) race and give
  * undefined results.  Nothing in the array needs to start at zero.  Every

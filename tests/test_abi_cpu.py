@@ -241,7 +241,7 @@ def _noalloc(**kw):
     (dict(chunk_size=32), kda.KDA_ERR_UNSUPPORTED),
     (dict(H=0), kda.KDA_ERR_SHAPE),
     (dict(num_seqs=2), kda.KDA_ERR_SHAPE),
-    # the headline prefill (H=32, T=8192, d=128) needs ~340 MB of workspace
+    # the headline prefill (H=32, T=8192, d=128) needs ~300 MB of workspace
     (dict(T=8192, H=32, dk=128, dv=128, chunk_size=64, dtype=BF16), kda.KDA_ERR_TOO_LARGE),
     (dict(B=4, num_seqs=4, T=4096, H=16, dk=128, dv=128, chunk_size=64, dtype=BF16), kda.KDA_ERR_TOO_LARGE),
 ])

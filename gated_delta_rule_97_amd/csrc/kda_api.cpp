@@ -206,8 +206,11 @@ static int prefill_shape(int B, int T, int H, int dk, int dv, int num_seqs, int 
         if (slots > INT32_MAX / 2) return KDA_ERR_SHAPE;
         *nc_max = int(slots);
     }
-    // element offsets are computed in 64 bits; per-dimension products in 32
+    // element offsets are computed in 64 bits; per-dimension products in 32,
+    // and so are the byte offsets of one chunk's output rows (up to C rows of
+    // H x dv values), which the range-checked o stores take as 32-bit offsets
     if (int64_t(B) * T * H > INT32_MAX || int64_t(*N) * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (int64_t(chunk_size) * H * dv * 4 > INT32_MAX) return KDA_ERR_SHAPE;
     return KDA_OK;
 }
 

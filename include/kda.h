@@ -119,7 +119,10 @@ int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv,
  *              bytes, 256-byte aligned; its contents on entry do not matter.
  *              Two calls in flight on different streams need two workspaces.
  *   stream     HIP stream the kernels are enqueued on.
- * A sequence of length 0 gives ht = h0 (or zeros).
+ * A sequence of length 0 gives ht = h0 (or zeros).  Sizes: B*T*H and N*H
+ * below 2^31, and chunk_size*H*dv*4 below 2^31 (the byte span of one
+ * chunk's output rows at fp32 width: H < 65536 at dv = 128, chunk 64);
+ * KDA_ERR_SHAPE otherwise.
  */
 int kda_chunk_prefill(const void *q, const void *k, const void *v,
                       const float *g, const float *beta, const float *h0,

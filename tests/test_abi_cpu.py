@@ -58,6 +58,11 @@ def test_workspace_size():
     with pytest.raises(kda.KdaError) as e:
         kda.kda_chunk_prefill_workspace_size(2, 100, 2, 64, 64, 3, 64, BF16)
     assert e.value.status == kda.KDA_ERR_SHAPE
+    # one chunk's output rows must span less than 2 GiB at fp32 width
+    assert kda.kda_chunk_prefill_workspace_size(1, 64, 65535, 128, 128, 1, 64, BF16) > 0
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_workspace_size(1, 64, 65536, 128, 128, 1, 64, BF16)
+    assert e.value.status == kda.KDA_ERR_SHAPE
 
 
 

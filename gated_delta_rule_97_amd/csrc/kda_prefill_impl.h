@@ -1240,11 +1240,22 @@ struct WsBuf {
     static constexpr size_t lds_bytes = size_t(2) * bytes;
 };
 
-// Copy unit lt + kLoaders * i of a chunk; units past the end repeat the last.
+// Copy unit lt + kLoaders * i of a chunk (clamped to the last unit, so the
+// plan's addresses stay inside the chunk's regions).  Only the last step can
+// run past the end; there the lanes whose unit does not exist neither load
+// nor write (a clamped copy would have every such lane write the same 16
+// bytes of LDS, and the youngest loader waves, which own those units, are
+// the last to issue).
 template <int DK, int DV, int C, int NLW, int i>
 __device__ __forceinline__ int ws_unit(int lt) {
     using B = WsBuf<DK, DV, C, NLW>;
     return min(lt + B::kLoaders * i, B::units - 1);
+}
+template <int DK, int DV, int C, int NLW, int i>
+__device__ __forceinline__ bool ws_live(int lt) {
+    using B = WsBuf<DK, DV, C, NLW>;
+    if constexpr (B::kLoaders * (i + 1) <= B::units) return true;
+    else return lt + B::kLoaders * i < B::units;
 }
 
 // Where a loader thread's units come from.  The units run over W, q e^Gam,
@@ -1298,17 +1309,17 @@ struct WsPlan {
 };
 
 template <int DK, int DV, int C, int NLW, int i>
-__device__ __forceinline__ void ws_fetch_unit(u32x4 *r, const WsPlan<DK, DV, C, NLW> &pl, size_t slot) {
+__device__ __forceinline__ void ws_fetch_unit(u32x4 *r, const WsPlan<DK, DV, C, NLW> &pl, size_t slot, int lt) {
     if constexpr (i < WsBuf<DK, DV, C, NLW>::UPT) {
-        r[i] = pl.fetch(i, slot);
-        ws_fetch_unit<DK, DV, C, NLW, i + 1>(r, pl, slot);
+        if (ws_live<DK, DV, C, NLW, i>(lt)) r[i] = pl.fetch(i, slot);
+        ws_fetch_unit<DK, DV, C, NLW, i + 1>(r, pl, slot, lt);
     }
 }
 
 template <int DK, int DV, int C, int NLW, int i>
 __device__ __forceinline__ void ws_put_unit(const u32x4 *r, unsigned char *dst, int lt) {
     if constexpr (i < WsBuf<DK, DV, C, NLW>::UPT) {
-        *reinterpret_cast<u32x4 *>(dst + ws_unit<DK, DV, C, NLW, i>(lt) * 16) = r[i];
+        if (ws_live<DK, DV, C, NLW, i>(lt)) *reinterpret_cast<u32x4 *>(dst + ws_unit<DK, DV, C, NLW, i>(lt) * 16) = r[i];
         ws_put_unit<DK, DV, C, NLW, i + 1>(r, dst, lt);
     }
 }
@@ -1321,8 +1332,10 @@ template <int DK, int DV, int C, int NLW, int i, int iend>
 __device__ __forceinline__ void ws_step(const u32x4 *rp, unsigned char *dst, u32x4 *rf,
                                         const WsPlan<DK, DV, C, NLW> &pl, size_t slot, int lt) {
     if constexpr (i < iend) {
-        *reinterpret_cast<u32x4 *>(dst + ws_unit<DK, DV, C, NLW, i>(lt) * 16) = rp[i];
-        rf[i] = pl.fetch(i, slot);
+        if (ws_live<DK, DV, C, NLW, i>(lt)) {
+            *reinterpret_cast<u32x4 *>(dst + ws_unit<DK, DV, C, NLW, i>(lt) * 16) = rp[i];
+            rf[i] = pl.fetch(i, slot);
+        }
         ws_step<DK, DV, C, NLW, i + 1, iend>(rp, dst, rf, pl, slot, lt);
     }
 }
@@ -1382,7 +1395,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         pl.template init_unit<0>(a, lt, nn0);
         auto fetch = [&](u32x4 (&r)[UPT], int c) {
             const size_t slot = size_t(c_begin + min(c, nc - 1)) * H + h;
-            ws_fetch_unit<DK, DV, C, NLW, 0>(r, pl, slot);
+            ws_fetch_unit<DK, DV, C, NLW, 0>(r, pl, slot, lt);
         };
         auto put = [&](const u32x4 (&r)[UPT], int buf) { ws_put_unit<DK, DV, C, NLW, 0>(r, wsbuf + buf * B::bytes, lt); };
         // chunk x lives in register stage x % 3 and LDS buffer x & 1.  During

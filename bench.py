@@ -11,10 +11,12 @@ Half a second of untimed calls precedes the W warmup calls (the GPU's
 clocks ramp up over the first tens of milliseconds of sustained work).  The
 K timed calls carry one event between consecutive calls and none inside a
 call: ms_per_step is their mean, "timing" their median and p10/p90.  Per-kernel durations come from a second timed pass of K calls
-with HIP events around every launch on its stream; "roofline" charges the
-longest kernel with the whole call's algorithmic bytes (1,540 B per
-token-head plus the states), "kernel_scoped" with its own, "path_roofline"
-gives the whole call's fraction.
+with HIP events around every launch on its stream; "roofline" takes the
+kernel with the longest time per call and charges each of its launches its
+share of the whole call's algorithmic bytes (1,540 B per token-head plus the
+states; the headline call runs as two chunk windows, so each of its kernels
+launches twice and a launch covers half the tokens), "kernel_scoped" with
+its own bytes, "path_roofline" gives the whole call's fraction.
 
 Also measured and reported in the same JSON line: decode (256 sequences x 32
 heads, d = 128, 128 consecutive in-place steps); packed variable-length
@@ -293,23 +295,27 @@ def main():
     kt = kda.kda_profile_stop()
 
     per_kernel_us = {name: 1e3 * tot / n for name, (n, tot) in kt.items()}
+    # launches of each kernel per call (2 when the call runs as two chunk
+    # windows): a launch covers that share of the call's tokens
+    per_call = {name: n / args.steps for name, (n, tot) in kt.items()}
     th = B * T * H
     state_bytes = 2 * B * H * dk * dv * 4
     path_bytes = BYTES_PER_TOKEN_HEAD * th + state_bytes
     kernel_bytes = {"kda_intra": INTRA_BYTES_PER_TOKEN_HEAD * th,
                     "kda_inter": INTER_BYTES_PER_TOKEN_HEAD * th + state_bytes}
-    dom = max(per_kernel_us, key=per_kernel_us.get)
+    dom = max(per_kernel_us, key=lambda k: per_kernel_us[k] * per_call[k])
     dom_us = per_kernel_us[dom]
-    achieved = path_bytes / (dom_us * 1e-6) / 1e9
-    own = kernel_bytes.get(dom, 0) / (dom_us * 1e-6) / 1e9
+    dom_launches = per_call[dom]
+    achieved = path_bytes / dom_launches / (dom_us * 1e-6) / 1e9
+    own = kernel_bytes.get(dom, 0) / dom_launches / (dom_us * 1e-6) / 1e9
     workload = PREFILL_WORKLOAD
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(dom, workload),
-                "avg_launch_us": round(dom_us, 2),
-                "algorithmic_bytes_per_launch": path_bytes,
-                "kernel_scoped": {"bytes_per_launch": kernel_bytes.get(dom, 0), "achieved": round(own, 1),
-                                  "frac": round(own / HBM_PEAK_GBS, 4)}}
+                "avg_launch_us": round(dom_us, 2), "launches_per_call": round(dom_launches, 2),
+                "algorithmic_bytes_per_launch": int(path_bytes / dom_launches),
+                "kernel_scoped": {"bytes_per_launch": int(kernel_bytes.get(dom, 0) / dom_launches),
+                                  "achieved": round(own, 1), "frac": round(own / HBM_PEAK_GBS, 4)}}
     path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
     path_tflops = FLOPS_PER_TOKEN_HEAD * th / (ms_step * 1e-3) / 1e12
     floor_us = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -569,6 +575,7 @@ def main():
            "roofline": roofline, "path_roofline": path_roofline,
            "timing": dict(headline_spread, prewarm_calls=n_pre, prewarm_s=args.prewarm_seconds),
            "kernels_us": {k: round(v, 2) for k, v in per_kernel_us.items()},
+           "kernel_launches_per_call": {k: round(v, 2) for k, v in per_call.items()},
            "cpu_baseline": cpu, "parity": parity, "decode": decode, "varlen": varlen,
            "next": nxt if nxt is not None else {"speculative_verify": verify},
            "source_digest": source_digest()}

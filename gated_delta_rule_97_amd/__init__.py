@@ -49,6 +49,7 @@ KDA_ERR_TOO_LARGE = -9
 NOALLOC_SCRATCH_BYTES = 128 << 20
 KDA_FLAG_CHECK_DECAY = 1
 KDA_FLAG_NO_SEGMENTS = 2
+KDA_FLAG_NO_WINDOWS = 4
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 

@@ -45,6 +45,13 @@ struct PrefillArgs {
     // Sin [chains][dk][dv]: the true state entering each segment.
     int seg_len, nseg;
     float *Mseg, *Bseg, *Sin;
+    // chunk windows (fixed-length batches on the loader-fed chain only):
+    // the call runs as nwin (intra-chunk pass, state pass) pairs over chunks
+    // [w win_len, min((w + 1) win_len, nc_seq)) of every sequence, the state
+    // handed from one window to the next through carry [N][H][dk][dv].  A
+    // launch covers chunks [win_c0, win_c0 + win_nc) (0 and nc_seq: all).
+    int nwin, win_len, win_c0, win_nc;
+    float *carry;
 };
 
 // Segment plan of a prefill: segments when long fixed-length sequences have
@@ -55,12 +62,19 @@ struct SegPlan {
 };
 SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq);
 
+// Chunk windows of a prefill (1: none).  A pure function of the sizes, like
+// the segment plan, so the workspace size query and the call agree.
+int win_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq, int nseg);
+
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {
-    size_t coff, ckoff, W, Qg, KtT, Ut, Ps, D, Mseg, Bseg, Sin, dummy, flag, total;
+    size_t coff, ckoff, W, Qg, KtT, Ut, Ps, D, Mseg, Bseg, Sin, carry, dummy, flag, total;
 };
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C,
-                             size_t elem_bytes, int nseg);
+                             size_t elem_bytes, int nseg, int nwin);
+// bytes of one (chunk, head) slot of the hand-off from the intra-chunk pass
+// to the state pass (W, q e^Gam, K~^T, Ut, P, e^{Gam_last})
+size_t handoff_slot_bytes(int dk, int dv, int C, size_t elem_bytes);
 // chunk length rounded up to the MFMA contraction of the dtype (K~^T pad)
 inline int chunk_pad(int C, size_t elem_bytes) {
     const int k = elem_bytes == 2 ? 32 : 4;

@@ -86,11 +86,27 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C
 // every sequence's first chunks are written last: the state pass, which
 // starts there, then finds them still in the last-level cache.
 __device__ __forceinline__ int intra_slot(const PrefillArgs &a, int wc) {
-    if (!a.cu) {
+    if (!a.cu) {  // chunks win_c0 .. win_c0 + win_nc - 1 of every sequence
         const int j = wc / a.N;
-        return (wc - j * a.N) * a.nc_seq + (a.nc_seq - 1 - j);
+        return (wc - j * a.N) * a.nc_seq + (a.win_c0 + a.win_nc - 1 - j);
     }
     return a.nc_max - 1 - wc;
+}
+
+// Hand-off slot (chunk index) of global chunk gc.  The chunk windows of a
+// fixed-length batch all use the slots of the first one, so that a window's
+// hand-off overwrites the previous window's while the last-level cache still
+// holds it (those lines are then never written back to HBM); with one window
+// this is gc itself.
+__device__ __forceinline__ int handoff_chunk(const PrefillArgs &a, int gc) {
+    if (a.cu || a.nc_seq <= 0) return gc;
+    const int n = gc / a.nc_seq;
+    return n * a.win_len + (gc - n * a.nc_seq - a.win_c0);
+}
+
+// (chunk, all heads) groups the intra-chunk pass walks in one launch
+__host__ __device__ __forceinline__ int intra_groups(const PrefillArgs &a) {
+    return a.cu ? a.nc_max : a.N * a.win_nc;
 }
 
 // ---------------------------------------------------------------------------
@@ -473,7 +489,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     float *sB = reinterpret_cast<float *>(smem + Ly::oB);
 
     const int H = a.H;
-    const int nitems = a.nc_max * H;
+    const int nitems = intra_groups(a) * H;
 
     // first item of this workgroup with a valid chunk
     int item = blockIdx.x;
@@ -504,7 +520,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile math stays scalar
         const int grp = lane >> 4, l16 = lane & 15;
         const int gc = intra_slot(a, item / H), h = item % H;
-        const size_t slot = size_t(gc) * H + h;
+        const size_t slot = size_t(handoff_chunk(a, gc)) * H + h;
         // The prefetched registers are consumed from here on, and only from
         // here: without this fence the compiler moves unpacking work up to
         // the loads at the end of the previous item, which then must wait
@@ -1373,11 +1389,11 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
     const int jb = blk * BV, nn0 = jb / kTile;
 
     int c_begin, c_end, tok_start, tok_end;
-    if (!a.cu) {
-        c_begin = n * a.nc_seq;
-        c_end = c_begin + a.nc_seq;
-        tok_start = n * a.T;
-        tok_end = tok_start + a.T;
+    if (!a.cu) {  // this launch's chunk window of the sequence
+        c_begin = n * a.nc_seq + a.win_c0;
+        c_end = c_begin + a.win_nc;
+        tok_start = n * a.T + a.win_c0 * C;
+        tok_end = n * a.T + a.T;
     } else {
         c_begin = min(a.coff[n], a.nc_max);
         c_end = min(max(a.coff[n + 1], c_begin), a.nc_max);
@@ -1385,6 +1401,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         tok_end = clampi(a.cu[n + 1], tok_start, a.T);
     }
     const int nc = c_end - c_begin;  // chunks of this chain (may be 0)
+    const int hc_begin = a.cu ? c_begin : n * a.win_len;  // its first hand-off slot (handoff_chunk)
 
     if (wid_all >= kWaves) {
         // ---------------- loader waves ----------------
@@ -1394,7 +1411,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         WsPlan<DK, DV, C, NLW> pl;
         pl.template init_unit<0>(a, lt, nn0);
         auto fetch = [&](u32x4 (&r)[UPT], int c) {
-            const size_t slot = size_t(c_begin + min(c, nc - 1)) * H + h;
+            const size_t slot = size_t(hc_begin + min(c, nc - 1)) * H + h;
             ws_fetch_unit<DK, DV, C, NLW, 0>(r, pl, slot, lt);
         };
         auto put = [&](const u32x4 (&r)[UPT], int buf) { ws_put_unit<DK, DV, C, NLW, 0>(r, wsbuf + buf * B::bytes, lt); };
@@ -1404,7 +1421,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         // requests chunk c + 4, half after each of the chunk's two barriers,
         // so neither half holds a barrier back.
         constexpr int HALF = UPT / 2;
-        auto slot_of = [&](int x) { return size_t(c_begin + min(x, nc - 1)) * H + h; };
+        auto slot_of = [&](int x) { return size_t(hc_begin + min(x, nc - 1)) * H + h; };
         if (nc > 0) {
             fetch(st[0], 0);
             fetch(st[1], 1);
@@ -1575,7 +1592,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
                 __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), orsrc, ooff + r * orow, 0, 0);
             }
         }
-        inter_ckpt<bf16, DK, DV, C, BV>(a, S, n, h, c, tok0 + C <= tok_end, wid, grp, l16, jb);
+        inter_ckpt<bf16, DK, DV, C, BV>(a, S, n, h, a.win_c0 + c, tok0 + C <= tok_end, wid, grp, l16, jb);
     }
     if (a.ht) {
         float *dst = a.ht + size_t(n * H + h) * DK * DV;
@@ -1983,6 +2000,24 @@ void kda_chain_kernel(PrefillArgs a) {
     }
 }
 
+// Loader-fed state chain over this launch's chunks (bf16, 16-column blocks).
+template <int DK, int DV, int C>
+hipError_t launch_ws_chain(const PrefillArgs &a, hipStream_t s) {
+    constexpr int NLW = kWsLoaderWaves;
+    using WB = WsBuf<DK, DV, C, NLW>;
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C, NLW>),
+                                      int(WB::lds_bytes));
+    if (e != hipSuccess) return e;
+    const int nwg = a.N * a.H * (DV / 16);
+    if (nwg > 0) {
+        prof_begin(s);
+        hipLaunchKernelGGL((kda_inter_ws_kernel<DK, DV, C, NLW>), dim3(nwg), dim3(kThreads + kWave * NLW),
+                           WB::lds_bytes, s, a);
+        prof_end(s, "kda_inter");
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch of one (dtype, dk, dv, chunk, bv) instance.
 // ---------------------------------------------------------------------------
@@ -1994,15 +2029,42 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&kda_intra_kernel<T, DK, DV, C>), int(Ly::bytes));
         if (e != hipSuccess) return e;
     }
-    if (a.nc_max > 0) {
-        // persistent: one workgroup per compute unit (LDS allows one), each
-        // walking (chunk, head) items with its next item's inputs in flight
-        const int items = a.nc_max * a.H;
-        const int grid = items < a.num_cu ? items : a.num_cu;
+    // persistent: one workgroup per compute unit (LDS allows one), each
+    // walking (chunk, head) items with its next item's inputs in flight
+    auto launch_intra = [&](const PrefillArgs &b) -> hipError_t {
+        const int items = intra_groups(b) * b.H;
+        if (b.nc_max <= 0 || items <= 0) return hipSuccess;
+        const int grid = items < b.num_cu ? items : b.num_cu;
         prof_begin(s);
-        hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV, C>), dim3(grid), dim3(kIThreads), Ly::bytes, s, a);
+        hipLaunchKernelGGL((kda_intra_kernel<T, DK, DV, C>), dim3(grid), dim3(kIThreads), Ly::bytes, s, b);
         prof_end(s, "kda_intra");
-        hipError_t e = hipGetLastError();
+        return hipGetLastError();
+    };
+    if (a.nwin > 1) {
+        // chunk windows: each window's intra-chunk pass, then its state pass
+        // from the carried state (loader-fed chain, fixed-length batches)
+        if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && C == 64 && BV == 16) {
+            if (a.cu || a.seg_len > 0 || a.win_len <= 0) return hipErrorInvalidValue;
+            for (int w = 0; w < a.nwin; ++w) {
+                PrefillArgs b = a;
+                b.win_c0 = w * a.win_len;
+                b.win_nc = min(a.win_len, a.nc_seq - b.win_c0);
+                if (b.win_nc <= 0) break;
+                const bool last = b.win_c0 + b.win_nc >= a.nc_seq;
+                if (w > 0) b.h0 = a.carry;
+                if (!last) b.ht = a.carry;
+                hipError_t e = launch_intra(b);
+                if (e == hipSuccess) e = launch_ws_chain<DK, DV, C>(b, s);
+                if (e != hipSuccess) return e;
+                if (last) break;
+            }
+            return hipSuccess;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    {
+        hipError_t e = launch_intra(a);
         if (e != hipSuccess) return e;
     }
     if constexpr (sizeof(T) == 2) {
@@ -2082,20 +2144,7 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
     const int nwg = a.N * a.H * (DV / BV);
     if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && C == 64 && BV == 16) {
         // loader-fed state chain (one chain per (sequence, head), no segments)
-        constexpr int NLW = kWsLoaderWaves;
-        using WB = WsBuf<DK, DV, C, NLW>;
-        {
-            hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C, NLW>),
-                                              int(WB::lds_bytes));
-            if (e != hipSuccess) return e;
-        }
-        if (nwg > 0) {
-            prof_begin(s);
-            hipLaunchKernelGGL((kda_inter_ws_kernel<DK, DV, C, NLW>), dim3(nwg), dim3(kThreads + kWave * NLW),
-                               WB::lds_bytes, s, a);
-            prof_end(s, "kda_inter");
-        }
-        return hipGetLastError();
+        return launch_ws_chain<DK, DV, C>(a, s);
     }
     if (nwg > 0) {
         prof_begin(s);

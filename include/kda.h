@@ -82,6 +82,16 @@ enum {
  * part summarised by its state transition; here across compute units).
  * Results agree up to rounding either way; for comparisons and timing. */
 #define KDA_FLAG_NO_SEGMENTS 2u
+/* Prefill: run the whole call as one intra-chunk pass and one state pass
+ * even when the sizes would split it into chunk windows.  A fixed-length
+ * bf16 batch at dk = dv = 128, chunk 64 whose hand-off between the two
+ * passes (72,192 bytes per (chunk, head)) comes to more than 192 MiB and at
+ * most 384 MiB otherwise runs as two windows over the chunks of every
+ * sequence, each an intra-chunk pass followed by a state pass, so that the
+ * state pass reads a hand-off the 256 MiB last-level cache still holds; the
+ * state crosses from one window to the next in the workspace.  Results are
+ * bit-identical either way; for comparisons and timing. */
+#define KDA_FLAG_NO_WINDOWS 4u
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes
  * (written to *bytes).  Same arguments as kda_chunk_prefill.  The figure

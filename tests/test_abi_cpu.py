@@ -43,7 +43,9 @@ def test_workspace_size():
     # per (chunk, head), plus the chunk map
     slots = (8192 // 64 + 1) * 32
     per_slot = 4 * 64 * 128 * 2 + 6 * 16 * 32 * 2 + 128 * 4
-    assert slots * per_slot <= w1 < slots * per_slot + (1 << 20)
+    # this call runs as two chunk windows: plus the carried fp32 state
+    carry = 32 * 128 * 128 * 4
+    assert slots * per_slot + carry <= w1 < slots * per_slot + carry + (1 << 20)
     assert w1 % 256 == 0
     w2 = kda.kda_chunk_prefill_workspace_size(1, 8192, 32, 128, 128, 64, 64, BF16)
     assert w2 > w1
@@ -80,8 +82,32 @@ def test_workspace_segment_states_follow_the_plan():
         return w - (T // 64 + 1) * H * per_slot
 
     assert 3 * 32 * 8 * st <= extra(1 << 20, 8) < 3 * 32 * 8 * st + (1 << 20)
-    assert 0 <= extra(8192, 32) < st
+    assert 32 * st <= extra(8192, 32) < 33 * st  # no segments; the chunk-window carry
     assert 0 <= extra(63 * 64, 1) < st
+
+
+def test_workspace_window_carry_follows_the_plan():
+    """Fixed-length bf16 batches at d = 128, chunk 64 run as two chunk windows
+    (with an fp32 carry state per (sequence, head) in the workspace) exactly
+    when their hand-off between the passes, 72,192 bytes per (chunk, head),
+    comes to more than 192 MiB and at most 384 MiB: one split then brings
+    each window under the 256 MiB last-level cache."""
+    per_slot = 4 * 64 * 128 * 2 + 6 * 16 * 32 * 2 + 128 * 4
+    st = 128 * 128 * 4
+
+    def extra(B, T, H, N=None):
+        N = B if N is None else N
+        w = kda.kda_chunk_prefill_workspace_size(B, T, H, 128, 128, N, 64, BF16)
+        slots = B * T // 64 + (1 if B == 1 else 0)  # B = 1 may also be read as packed: one slot more
+        return w - slots * H * per_slot
+
+    assert extra(2, 4096, 16) < st              # 141 MiB: one window
+    assert 32 * st <= extra(1, 8192, 32) < 33 * st   # 282 MiB: two
+    assert 64 * st <= extra(2, 4096, 32) < 65 * st   # 282 MiB over two sequences: two
+    assert 48 * st <= extra(2, 4096, 24) < 49 * st   # 211 MiB: two
+    assert extra(1, 8192, 48) < st              # 423 MiB: one (two windows would not fit the cache)
+    assert extra(1, 63 * 64, 32) < st           # 139 MiB over 63 chunks: one
+
 
 
 # fake, never-dereferenced device addresses (validation fails before use)

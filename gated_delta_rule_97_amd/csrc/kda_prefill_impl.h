@@ -93,15 +93,17 @@ __device__ __forceinline__ int intra_slot(const PrefillArgs &a, int wc) {
     return a.nc_max - 1 - wc;
 }
 
-// Hand-off slot (chunk index) of global chunk gc.  The chunk windows of a
+// Hand-off slot (chunk index) of the same group.  The chunk windows of a
 // fixed-length batch all use the slots of the first one, so that a window's
 // hand-off overwrites the previous window's while the last-level cache still
 // holds it (those lines are then never written back to HBM); with one window
-// this is gc itself.
-__device__ __forceinline__ int handoff_chunk(const PrefillArgs &a, int gc) {
-    if (a.cu || a.nc_seq <= 0) return gc;
-    const int n = gc / a.nc_seq;
-    return n * a.win_len + (gc - n * a.nc_seq - a.win_c0);
+// this is intra_slot itself.
+__device__ __forceinline__ int intra_handoff(const PrefillArgs &a, int wc) {
+    if (!a.cu) {
+        const int j = wc / a.N;
+        return (wc - j * a.N) * a.win_len + (a.win_nc - 1 - j);
+    }
+    return a.nc_max - 1 - wc;
 }
 
 // (chunk, all heads) groups the intra-chunk pass walks in one launch
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile math stays scalar
         const int grp = lane >> 4, l16 = lane & 15;
         const int gc = intra_slot(a, item / H), h = item % H;
-        const size_t slot = size_t(handoff_chunk(a, gc)) * H + h;
+        const size_t slot = size_t(intra_handoff(a, item / H)) * H + h;
         // The prefetched registers are consumed from here on, and only from
         // here: without this fence the compiler moves unpacking work up to
         // the loads at the end of the previous item, which then must wait
@@ -1401,7 +1403,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         tok_end = clampi(a.cu[n + 1], tok_start, a.T);
     }
     const int nc = c_end - c_begin;  // chunks of this chain (may be 0)
-    const int hc_begin = a.cu ? c_begin : n * a.win_len;  // its first hand-off slot (handoff_chunk)
+    const int hc_begin = a.cu ? c_begin : n * a.win_len;  // its first hand-off slot (intra_handoff)
 
     if (wid_all >= kWaves) {
         // ---------------- loader waves ----------------

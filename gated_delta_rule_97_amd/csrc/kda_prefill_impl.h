@@ -521,7 +521,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const int tid = opaque(int(threadIdx.x)), lane = tid & 63;
         const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile math stays scalar
         const int grp = lane >> 4, l16 = lane & 15;
-        const int gc = intra_slot(a, item / H), h = item % H;
+        const int h = item % H;
         const size_t slot = size_t(intra_handoff(a, item / H)) * H + h;
         // The prefetched registers are consumed from here on, and only from
         // here: without this fence the compiler moves unpacking work up to

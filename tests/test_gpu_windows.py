@@ -33,7 +33,7 @@ def _intra_launches(kda, f):
     return kt["kda_intra"][0], out
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 8192, 32), (2, 4096, 32), (1, 8152, 32)])
+@pytest.mark.parametrize("B,T,H", [(1, 8192, 32), (2, 4096, 32), (1, 8152, 32), (2, 4100, 32), (3, 2752, 32)])
 def test_windows_equal_the_one_pass_chain(B, T, H):
     import gated_delta_rule_97_amd as kda
     spec = workloads.PREFILL_H32_T8K.replace(B=B, T=T, H=H, g_mode="slow", h0_std=1.0, seed=201)

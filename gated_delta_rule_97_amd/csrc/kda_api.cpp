@@ -37,21 +37,30 @@ size_t handoff_slot_bytes(int dk, int dv, int C, size_t elem_bytes) {
             size_t(score_elems(C, elem_bytes == 2 ? 32 : 4))) * elem_bytes + size_t(dk) * sizeof(float);
 }
 
-int win_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq, int nseg) {
+WinPlan win_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq, int nseg) {
     // The state pass reads the hand-off the intra-chunk pass wrote; it runs
-    // ~15% faster when that hand-off is still in the 256 MiB last-level
-    // cache (headline batch of 282 MiB: state pass 140 -> 120 us as two
-    // windows of 141 MiB).  Each extra window costs a launch pair and their
-    // pipeline fills (~7 us measured at four windows), so the call splits in
-    // two when that brings each window under 192 MiB, and not otherwise.
+    // 15-18% faster when that hand-off is still in the 256 MiB last-level
+    // cache.  Once the hand-off passes 192 MiB the call runs as windows of
+    // about 160 MiB: groups of whole sequences, or, for a sequence larger
+    // than that, windows over its chunks (with the state carried between
+    // them), provided each keeps at least 32 of its chunks: a state chain of
+    // fewer does not repay its pipeline fill (measured: 16 chunks even, 8
+    // slower).  Each window costs a launch pair.
+    const WinPlan none{N, 1};
     const bool loader_fed = dtype == KDA_DTYPE_BF16 && dk == 128 && dv == 128 && C == 64;
-    if (packed || !loader_fed || nseg > 1 || nc_seq < 2) return 1;
-    const double mib = double(N) * nc_seq * H * double(handoff_slot_bytes(dk, dv, C, 2)) / double(1 << 20);
-    return (mib > 192.0 && mib <= 384.0) ? 2 : 1;
+    if (packed || !loader_fed || nseg > 1 || nc_seq < 1 || N < 1) return none;
+    const double mib_seq = double(nc_seq) * H * double(handoff_slot_bytes(dk, dv, C, 2)) / double(1 << 20);
+    if (mib_seq * N <= 192.0) return none;
+    if (mib_seq <= 160.0) {
+        const int grp = int(160.0 / mib_seq);
+        return grp >= N ? none : WinPlan{grp, 1};
+    }
+    const int nchunk = int(mib_seq / 160.0 + 0.999);
+    return nc_seq / nchunk >= 32 ? WinPlan{1, nchunk} : none;
 }
 
 PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, size_t elem_bytes, int nseg,
-                             int nwin) {
+                             bool carry) {
     PrefillLayout L;
     const size_t slots = size_t(nc_max) * size_t(H);
     size_t off = 0;
@@ -79,7 +88,7 @@ PrefillLayout prefill_layout(int nc_max, int H, int N, int dk, int dv, int C, si
     L.Sin = off;
     off = align_up(off + sch * dk * dv * sizeof(float), 256);
     L.carry = off;  // the state between chunk windows
-    off = align_up(off + (nwin > 1 ? size_t(N) * H * dk * dv * sizeof(float) : 0), 256);
+    off = align_up(off + (carry ? size_t(N) * H * dk * dv * sizeof(float) : 0), 256);
     L.dummy = off;
     off += 1024;
     L.flag = off;  // result word of the checked mode
@@ -256,8 +265,8 @@ int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int nu
     // the window carry when it runs in windows
     const int ncs = (T + chunk_size - 1) / chunk_size;
     const int nseg = (num_seqs == B) ? seg_plan(false, B, H, dv, ncs).nseg : 1;
-    const int nwin = (num_seqs == B) ? win_plan(false, dtype, dk, dv, chunk_size, B, H, ncs, nseg) : 1;
-    *bytes = prefill_layout(nc, H, num_seqs, dk, dv, chunk_size, dtype_bytes(dtype), nseg, nwin).total;
+    const bool carry = num_seqs == B && win_plan(false, dtype, dk, dv, chunk_size, B, H, ncs, nseg).nchunk > 1;
+    *bytes = prefill_layout(nc, H, num_seqs, dk, dv, chunk_size, dtype_bytes(dtype), nseg, carry).total;
     return KDA_OK;
 }
 
@@ -331,8 +340,8 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     // the layout is the one the size query computed (segment buffers present
     // whenever the sizes call for them, also when a flag turns them off)
     const SegPlan sp_ws = seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
-    const int nwin_ws = win_plan(packed, dtype, dk, dv, chunk_size, N, H, (T + chunk_size - 1) / chunk_size, sp_ws.nseg);
-    const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb, sp_ws.nseg, nwin_ws);
+    const WinPlan wp = win_plan(packed, dtype, dk, dv, chunk_size, N, H, (T + chunk_size - 1) / chunk_size, sp_ws.nseg);
+    const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb, sp_ws.nseg, wp.nchunk > 1);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     if (flags & KDA_FLAG_CHECK_DECAY) {
         // the result word is this call's own (in its workspace)
@@ -367,10 +376,14 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     a.Mseg = reinterpret_cast<float *>(ws + L.Mseg);
     a.Bseg = reinterpret_cast<float *>(ws + L.Bseg);
     a.Sin = reinterpret_cast<float *>(ws + L.Sin);
-    // chunk windows: the size plan's, unless a flag turned them or the
-    // segments off (the carry is in the workspace whenever the plan has them)
-    a.nwin = (nwin_ws > 1 && sp.nseg == 1 && !(flags & KDA_FLAG_NO_WINDOWS)) ? nwin_ws : 1;
-    a.win_len = (a.nc_seq + a.nwin - 1) / a.nwin;
+    // windows: the size plan's, unless a flag turned them or the segments off
+    // (the carry is in the workspace whenever the plan has chunk windows)
+    const bool win = (wp.grp < N || wp.nchunk > 1) && sp.nseg == 1 && !(flags & KDA_FLAG_NO_WINDOWS);
+    a.win_grp = win ? wp.grp : N;
+    a.win_len = win ? (a.nc_seq + wp.nchunk - 1) / wp.nchunk : a.nc_seq;
+    a.nwin = win ? ((N + a.win_grp - 1) / a.win_grp) * wp.nchunk : 1;
+    a.win_n0 = 0;
+    a.win_nn = N;
     a.win_c0 = 0;
     a.win_nc = a.nc_seq;
     a.carry = reinterpret_cast<float *>(ws + L.carry);
@@ -389,6 +402,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
         a.win_nc = 0;
         a.win_len = 0;
         a.nwin = 1;
+        a.win_grp = N;
         a.T = 0;
         a.ckpt = nullptr;
         a.ck_per_seq = 0;

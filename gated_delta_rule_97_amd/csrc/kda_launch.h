@@ -45,12 +45,15 @@ struct PrefillArgs {
     // Sin [chains][dk][dv]: the true state entering each segment.
     int seg_len, nseg;
     float *Mseg, *Bseg, *Sin;
-    // chunk windows (fixed-length batches on the loader-fed chain only):
-    // the call runs as nwin (intra-chunk pass, state pass) pairs over chunks
-    // [w win_len, min((w + 1) win_len, nc_seq)) of every sequence, the state
-    // handed from one window to the next through carry [N][H][dk][dv].  A
-    // launch covers chunks [win_c0, win_c0 + win_nc) (0 and nc_seq: all).
-    int nwin, win_len, win_c0, win_nc;
+    // windows (fixed-length batches on the loader-fed chain only): the call
+    // runs as (intra-chunk pass, state pass) pairs, one per window: groups of
+    // win_grp sequences, and inside each group chunk windows
+    // [w win_len, min((w + 1) win_len, nc_seq)) (several only when
+    // win_grp = 1), the state handed from one chunk window to the next
+    // through carry [N][H][dk][dv].  A launch covers sequences
+    // [win_n0, win_n0 + win_nn) and their chunks [win_c0, win_c0 + win_nc)
+    // (0, N, 0, nc_seq: all).  nwin: the number of windows (1: none).
+    int nwin, win_grp, win_len, win_n0, win_nn, win_c0, win_nc;
     float *carry;
 };
 
@@ -62,9 +65,14 @@ struct SegPlan {
 };
 SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq);
 
-// Chunk windows of a prefill (1: none).  A pure function of the sizes, like
-// the segment plan, so the workspace size query and the call agree.
-int win_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq, int nseg);
+// Windows of a prefill: win_grp sequences per window and chunk windows per
+// sequence (nchunk > 1 only with win_grp = 1); {N, 1}: none.  A pure
+// function of the sizes, like the segment plan, so the workspace size query
+// and the call agree.
+struct WinPlan {
+    int grp, nchunk;
+};
+WinPlan win_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq, int nseg);
 
 // Workspace carve-up shared by the size query and the prefill call.
 struct PrefillLayout {

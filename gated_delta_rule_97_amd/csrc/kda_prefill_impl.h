@@ -86,29 +86,30 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C
 // every sequence's first chunks are written last: the state pass, which
 // starts there, then finds them still in the last-level cache.
 __device__ __forceinline__ int intra_slot(const PrefillArgs &a, int wc) {
-    if (!a.cu) {  // chunks win_c0 .. win_c0 + win_nc - 1 of every sequence
-        const int j = wc / a.N;
-        return (wc - j * a.N) * a.nc_seq + (a.win_c0 + a.win_nc - 1 - j);
+    if (!a.cu) {  // chunks win_c0 .. win_c0 + win_nc - 1 of this launch's sequences
+        const int j = wc / a.win_nn;
+        return (a.win_n0 + wc - j * a.win_nn) * a.nc_seq + (a.win_c0 + a.win_nc - 1 - j);
     }
     return a.nc_max - 1 - wc;
 }
 
-// Hand-off slot (chunk index) of the same group.  The chunk windows of a
-// fixed-length batch all use the slots of the first one, so that a window's
-// hand-off overwrites the previous window's while the last-level cache still
-// holds it (those lines are then never written back to HBM); with one window
-// this is intra_slot itself.
+// Hand-off slot (chunk index) of the same group.  The windows of a
+// fixed-length batch all use the slots of the first one (slot = sequence in
+// the window x win_len + chunk in the window), so that a window's hand-off
+// overwrites the previous window's while the last-level cache still holds
+// it (those lines are then never written back to HBM); with one window this
+// is intra_slot itself.
 __device__ __forceinline__ int intra_handoff(const PrefillArgs &a, int wc) {
     if (!a.cu) {
-        const int j = wc / a.N;
-        return (wc - j * a.N) * a.win_len + (a.win_nc - 1 - j);
+        const int j = wc / a.win_nn;
+        return (wc - j * a.win_nn) * a.win_len + (a.win_nc - 1 - j);
     }
     return a.nc_max - 1 - wc;
 }
 
 // (chunk, all heads) groups the intra-chunk pass walks in one launch
 __host__ __device__ __forceinline__ int intra_groups(const PrefillArgs &a) {
-    return a.cu ? a.nc_max : a.N * a.win_nc;
+    return a.cu ? a.nc_max : a.win_nn * a.win_nc;
 }
 
 // ---------------------------------------------------------------------------
@@ -1374,7 +1375,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
     extern __shared__ __align__(16) unsigned char wsbuf[];
 
     const int H = a.H;
-    const int nchains = a.N * H;
+    const int nchains = (a.cu ? a.N : a.win_nn) * H;  // this launch's (sequence, head) chains
     const int wg = blockIdx.x;
     int chain, blk;
     if ((nchains & 7) == 0) {  // the NB blocks of a chain share an XCD
@@ -1385,7 +1386,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         chain = wg / NB;
         blk = wg - chain * NB;
     }
-    const int h = chain % H, n = chain / H;
+    const int h = chain % H, nw = chain / H, n = (a.cu ? 0 : a.win_n0) + nw;
     const int tid = threadIdx.x;
     const int wid_all = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int jb = blk * BV, nn0 = jb / kTile;
@@ -1403,7 +1404,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
         tok_end = clampi(a.cu[n + 1], tok_start, a.T);
     }
     const int nc = c_end - c_begin;  // chunks of this chain (may be 0)
-    const int hc_begin = a.cu ? c_begin : n * a.win_len;  // its first hand-off slot (intra_handoff)
+    const int hc_begin = a.cu ? c_begin : nw * a.win_len;  // its first hand-off slot (intra_handoff)
 
     if (wid_all >= kWaves) {
         // ---------------- loader waves ----------------
@@ -1463,7 +1464,7 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
     const int wid = wid_all, lane = tid & 63;
     const int grp = lane >> 4, l16 = lane & 15;
     floatx4 S[SPW];
-    const size_t sbase = size_t(chain) * DK * DV;
+    const size_t sbase = (size_t(n) * H + h) * DK * DV;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int item = wid + kWaves * i;
@@ -2010,7 +2011,7 @@ hipError_t launch_ws_chain(const PrefillArgs &a, hipStream_t s) {
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(&kda_inter_ws_kernel<DK, DV, C, NLW>),
                                       int(WB::lds_bytes));
     if (e != hipSuccess) return e;
-    const int nwg = a.N * a.H * (DV / 16);
+    const int nwg = (a.cu ? a.N : a.win_nn) * a.H * (DV / 16);
     if (nwg > 0) {
         prof_begin(s);
         hipLaunchKernelGGL((kda_inter_ws_kernel<DK, DV, C, NLW>), dim3(nwg), dim3(kThreads + kWave * NLW),
@@ -2043,22 +2044,25 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
         return hipGetLastError();
     };
     if (a.nwin > 1) {
-        // chunk windows: each window's intra-chunk pass, then its state pass
-        // from the carried state (loader-fed chain, fixed-length batches)
+        // windows: each window's intra-chunk pass, then its state pass
+        // (loader-fed chain, fixed-length batches): groups of win_grp
+        // sequences, and for each group its chunk windows, the state carried
+        // from one to the next
         if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && C == 64 && BV == 16) {
-            if (a.cu || a.seg_len > 0 || a.win_len <= 0) return hipErrorInvalidValue;
-            for (int w = 0; w < a.nwin; ++w) {
-                PrefillArgs b = a;
-                b.win_c0 = w * a.win_len;
-                b.win_nc = min(a.win_len, a.nc_seq - b.win_c0);
-                if (b.win_nc <= 0) break;
-                const bool last = b.win_c0 + b.win_nc >= a.nc_seq;
-                if (w > 0) b.h0 = a.carry;
-                if (!last) b.ht = a.carry;
-                hipError_t e = launch_intra(b);
-                if (e == hipSuccess) e = launch_ws_chain<DK, DV, C>(b, s);
-                if (e != hipSuccess) return e;
-                if (last) break;
+            if (a.cu || a.seg_len > 0 || a.win_len <= 0 || a.win_grp <= 0) return hipErrorInvalidValue;
+            for (int n0 = 0; n0 < a.N; n0 += a.win_grp) {
+                for (int c0 = 0; c0 < a.nc_seq; c0 += a.win_len) {
+                    PrefillArgs b = a;
+                    b.win_n0 = n0;
+                    b.win_nn = min(a.win_grp, a.N - n0);
+                    b.win_c0 = c0;
+                    b.win_nc = min(a.win_len, a.nc_seq - c0);
+                    if (c0 > 0) b.h0 = a.carry;
+                    if (c0 + b.win_nc < a.nc_seq) b.ht = a.carry;
+                    hipError_t e = launch_intra(b);
+                    if (e == hipSuccess) e = launch_ws_chain<DK, DV, C>(b, s);
+                    if (e != hipSuccess) return e;
+                }
             }
             return hipSuccess;
         } else {

@@ -83,14 +83,16 @@ enum {
  * Results agree up to rounding either way; for comparisons and timing. */
 #define KDA_FLAG_NO_SEGMENTS 2u
 /* Prefill: run the whole call as one intra-chunk pass and one state pass
- * even when the sizes would split it into chunk windows.  A fixed-length
- * bf16 batch at dk = dv = 128, chunk 64 whose hand-off between the two
- * passes (72,192 bytes per (chunk, head)) comes to more than 192 MiB and at
- * most 384 MiB otherwise runs as two windows over the chunks of every
- * sequence, each an intra-chunk pass followed by a state pass, so that the
- * state pass reads a hand-off the 256 MiB last-level cache still holds; the
- * state crosses from one window to the next in the workspace.  Results are
- * bit-identical either way; for comparisons and timing. */
+ * even when the sizes would split it into windows.  A fixed-length bf16
+ * batch at dk = dv = 128, chunk 64 whose hand-off between the two passes
+ * (72,192 bytes per (chunk, head)) comes to more than 192 MiB otherwise runs
+ * as windows of at most about 160 MiB, each an intra-chunk pass followed by
+ * a state pass, so that the state pass reads a hand-off the 256 MiB
+ * last-level cache still holds: groups of whole sequences when one
+ * sequence's hand-off fits 160 MiB, else windows over the chunks of every
+ * sequence (at least 32 chunks each) with the state crossing from one to
+ * the next in the workspace.  Results are bit-identical either way; for
+ * comparisons and timing. */
 #define KDA_FLAG_NO_WINDOWS 4u
 
 /* Bytes of device workspace kda_chunk_prefill needs for these sizes

@@ -87,11 +87,12 @@ def test_workspace_segment_states_follow_the_plan():
 
 
 def test_workspace_window_carry_follows_the_plan():
-    """Fixed-length bf16 batches at d = 128, chunk 64 run as two chunk windows
-    (with an fp32 carry state per (sequence, head) in the workspace) exactly
-    when their hand-off between the passes, 72,192 bytes per (chunk, head),
-    comes to more than 192 MiB and at most 384 MiB: one split then brings
-    each window under the 256 MiB last-level cache."""
+    """Fixed-length bf16 batches at d = 128, chunk 64 whose hand-off between the
+    passes (72,192 bytes per (chunk, head)) passes 192 MiB run as windows of
+    about 160 MiB: groups of whole sequences when a sequence's hand-off fits,
+    else windows over each sequence's chunks (at least 32 chunks each) with
+    an fp32 carry state per (sequence, head) in the workspace.  Only chunk
+    windows add the carry."""
     per_slot = 4 * 64 * 128 * 2 + 6 * 16 * 32 * 2 + 128 * 4
     st = 128 * 128 * 4
 
@@ -101,12 +102,16 @@ def test_workspace_window_carry_follows_the_plan():
         slots = B * T // 64 + (1 if B == 1 else 0)  # B = 1 may also be read as packed: one slot more
         return w - slots * H * per_slot
 
-    assert extra(2, 4096, 16) < st              # 141 MiB: one window
-    assert 32 * st <= extra(1, 8192, 32) < 33 * st   # 282 MiB: two
-    assert 64 * st <= extra(2, 4096, 32) < 65 * st   # 282 MiB over two sequences: two
-    assert 48 * st <= extra(2, 4096, 24) < 49 * st   # 211 MiB: two
-    assert extra(1, 8192, 48) < st              # 423 MiB: one (two windows would not fit the cache)
-    assert extra(1, 63 * 64, 32) < st           # 139 MiB over 63 chunks: one
+    assert 32 * st <= extra(1, 8192, 32) < 33 * st   # 282 MiB, one sequence: two chunk windows
+    assert 48 * st <= extra(1, 8192, 48) < 49 * st   # 423 MiB: three chunk windows
+    assert 64 * st <= extra(1, 8192, 64) < 65 * st   # 564 MiB: four, 32 chunks each
+    assert 128 * st <= extra(4, 8192, 32) < 129 * st  # 1.1 GiB: two chunk windows per sequence
+    assert extra(2, 4096, 32) < st              # 282 MiB over two sequences: one per window, no carry
+    assert extra(2, 4096, 24) < st              # 211 MiB: the same
+    assert extra(2, 4096, 16) < st              # 141 MiB: no windows
+    assert extra(1, 63 * 64, 32) < st           # 139 MiB over 63 chunks: no windows
+    assert extra(1, 3072, 128) < st             # 423 MiB, but 48 chunks: windows of 16 would not pay
+
 
 
 

@@ -1,10 +1,10 @@
 """Chunk windows of the prefill (needs a GPU).
 
 A fixed-length bf16 batch at d = 128, chunk 64 whose hand-off between the
-two passes comes to 192-384 MiB runs as two (intra-chunk pass, state pass)
-windows over the chunks of every sequence, the state carried from one to
-the next in the workspace, so that the state pass reads a hand-off the
-last-level cache still holds.  Windows change no arithmetic: the chain
+two passes passes 192 MiB runs as (intra-chunk pass, state pass) windows of
+about 160 MiB, so that the state pass reads a hand-off the last-level cache
+still holds: groups of whole sequences, or windows over the chunks of each
+sequence with the state carried from one to the next in the workspace.  Windows change no arithmetic: the chain
 takes the same products in the same order and the carried state is the
 fp32 state itself, so o, the final state and the checkpoints must be
 bit-identical to the one-pass chain (KDA_FLAG_NO_WINDOWS).  The windowed
@@ -33,14 +33,18 @@ def _intra_launches(kda, f):
     return kt["kda_intra"][0], out
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 8192, 32), (2, 4096, 32), (1, 8152, 32), (2, 4100, 32), (3, 2752, 32)])
-def test_windows_equal_the_one_pass_chain(B, T, H):
+# (B, T, H, windows): chunk windows of one sequence (2, ragged 2, 3), one
+# sequence per window (2, ragged 2, 3), groups of four and two sequences,
+# and two chunk windows in each of four sequences
+@pytest.mark.parametrize("B,T,H,nwin", [(1, 8192, 32, 2), (1, 8152, 32, 2), (1, 12288, 32, 3), (2, 4096, 32, 2),
+                                        (2, 4100, 32, 2), (3, 2752, 32, 3), (6, 1024, 32, 2), (4, 8192, 32, 8)])
+def test_windows_equal_the_one_pass_chain(B, T, H, nwin):
     import gated_delta_rule_97_amd as kda
     spec = workloads.PREFILL_H32_T8K.replace(B=B, T=T, H=H, g_mode="slow", h0_std=1.0, seed=201)
     x = workloads.make_prefill(spec, device="cuda")
     print(f"[windows] B={B} T={T} H={H}", flush=True)
     n, (o, ht) = _intra_launches(kda, lambda: _run(kda, x, T))
-    assert n == 2, f"expected two chunk windows, got {n} intra-chunk launches"
+    assert n == nwin, f"expected {nwin} windows, got {n} intra-chunk launches"
     n1, (o1, ht1) = _intra_launches(kda, lambda: _run(kda, x, T, flags=kda.KDA_FLAG_NO_WINDOWS))
     assert n1 == 1
     assert torch.equal(o, o1)
@@ -50,7 +54,7 @@ def test_windows_equal_the_one_pass_chain(B, T, H):
     # sequence positions
     n2, (o2, ht2, ck2) = _intra_launches(kda, lambda: _run(kda, x, T, ckpt_stride=512))
     n3, (o3, ht3, ck3) = _intra_launches(kda, lambda: _run(kda, x, T, ckpt_stride=512, flags=kda.KDA_FLAG_NO_WINDOWS))
-    assert (n2, n3) == (2, 1)
+    assert (n2, n3) == (nwin, 1)
     assert torch.equal(o2, o) and torch.equal(ht2, ht)
     assert torch.equal(ck2, ck3) and torch.equal(o3, o) and torch.equal(ht3, ht)
 

@@ -127,31 +127,12 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
 // are shared.  So one wavefront holds CW value columns x all DK rows of one
 // (sequence, head) and needs no other wave: each lane owns RPT consecutive
 // rows of one float4 of columns, and the reductions over dk sum a lane's
-// rows and then its row groups by xor shuffles.  No LDS, no barrier.
+// rows and then its row groups by cross-lane moves.  No barrier.
 // ---------------------------------------------------------------------------
 enum DecodeMode { kVerify = 0, kCommit = 1, kStep = 2 };
 
 template <int DV>
 constexpr int wave_columns() { return DV < 32 ? DV : 32; }
-
-// R consecutive values of T (R a multiple of 4, p aligned to 4 values)
-template <int R>
-__device__ __forceinline__ void load_vec(const bf16 *p, float (&x)[R]) {
-#pragma unroll
-    for (int i = 0; i < R; i += 4) {
-        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p + i);
-        x[i] = static_cast<float>(v[0]); x[i + 1] = static_cast<float>(v[1]);
-        x[i + 2] = static_cast<float>(v[2]); x[i + 3] = static_cast<float>(v[3]);
-    }
-}
-template <int R>
-__device__ __forceinline__ void load_vec(const float *p, float (&x)[R]) {
-#pragma unroll
-    for (int i = 0; i < R; i += 4) {
-        const floatx4 v = *reinterpret_cast<const floatx4 *>(p + i);
-        x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
-    }
-}
 
 // Per-token vectors of a group of KG tokens are staged once per wave in the
 // wave's own LDS region (one 16-byte unit per lane and load, e^g taken once
@@ -165,6 +146,55 @@ constexpr int kWavePB = 4;   // waves per workgroup
 template <int DK>
 __device__ __forceinline__ int wave_vec_idx(int c) { return c + (c >> 4) * 4; }  // 4-float pad per 16: row groups hit distinct banks
 
+// Cross-lane moves over the row-group bits of a wave whose lanes are
+// 8 * row group + column group, all on the VALU: xor 8 stays inside a
+// 16-lane row (DPP row_ror:8); v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second, so (x, y)
+// becomes (x_r0 | y_r0 | x_r2 | y_r2, x_r1 | y_r1 | x_r3 | y_r3); and
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 lanes of its second: (x, y) becomes (x_lo | y_lo, x_hi | y_hi).
+__device__ __forceinline__ float lane_xor8(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void lane_swap16(float x, float y, float &xs, float &ys) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    xs = __uint_as_float(r[0]);
+    ys = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void lane_swap32(float x, float y, float &xs, float &ys) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    xs = __uint_as_float(r[0]);
+    ys = __uint_as_float(r[1]);
+}
+
+// Sum of a float4 over the eight row groups, reduce-scattered: the lanes
+// whose row-group bits 4 and 5 are b4 and b5 get the sum of component
+// 2 b5 + b4 (both lanes of a bit-3 pair the same value).  Each halving
+// moves only the components the partner keeps.
+__device__ __forceinline__ float rg_sum_scatter(floatx4 x, int b4, int b5) {
+    float p0, p1, q0, q1;
+    lane_swap32(x[0], x[2], p0, p1);  // p0 + p1: component 0 in the lower half, 2 in the upper
+    lane_swap32(x[1], x[3], q0, q1);
+    const float a = p0 + p1, b = q0 + q1;  // components 2 b5 and 2 b5 + 1
+    float a2, b2;
+    lane_swap16(a, b, a2, b2);
+    const float r = a2 + b2;  // component 2 b5 in even rows, 2 b5 + 1 in odd rows
+    return r + lane_xor8(r);
+}
+
+// The inverse gather: lane (b4, b5) holds component 2 b5 + b4; every lane
+// gets all four.
+__device__ __forceinline__ floatx4 rg_gather(float x, int b4, int b5) {
+    float xe, xo;
+    lane_swap16(x, x, xe, xo);  // xe: even rows' values in each row pair, xo: odd rows'
+    const float o = b4 ? xe : xo;  // component 2 b5 + 1 - b4
+    const float lo = b4 ? o : x, hi = b4 ? x : o;  // components 2 b5, 2 b5 + 1
+    float p0, p1, q0, q1;
+    lane_swap32(lo, hi, p0, p1);  // lower half: p1 = component 2; upper half: p0 = component 1
+    lane_swap32(hi, lo, q0, q1);  // lower half: q1 = component 3; upper half: q0 = component 0
+    return b5 ? floatx4{q0, p0, lo, hi} : floatx4{lo, hi, p1, q1};
+}
+
 template <class T, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
@@ -177,6 +207,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     constexpr int NB = DV / CW;             // waves per (sequence, head)
     constexpr bool OUT = MODE != kCommit, WRITE = MODE != kVerify;
     static_assert(CG * RG == kWave && RPT * RG == DK && RPT % 4 == 0 && DV % CW == 0, "decode wave split");
+    static_assert(CG == 8, "row groups are lane bits 3..5");
     constexpr int NVEC = OUT ? 3 : 2;                   // staged per token: k, e^g (, q), as fp32
     constexpr int DKP = DK + DK / 4;                    // padded row of one vector
     constexpr int EPU = 16 / int(sizeof(T));            // values of T per 16-byte unit
@@ -191,6 +222,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     const int n = ch / H, h = ch - n * H;
     const int lane = threadIdx.x & (kWave - 1), cg = lane % CG, rg = lane / CG;
     const int r0 = rg * RPT, col = cb * CW + 4 * cg;
+    const int b4 = (lane >> 4) & 1, b5 = lane >> 5, cj = 2 * b5 + b4;  // row-group bits 4, 5
     float(*my)[NVEC][DKP] = sv[threadIdx.x / kWave];
     int ntok = K;
     if (MODE == kCommit) {
@@ -254,8 +286,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
             const float *kv = &my[tt][0][wave_vec_idx<DK>(r0)];
             const float *ev = &my[tt][1][wave_vec_idx<DK>(r0)];
             float kf[RPT];
-            floatx4 w = zero4(), y = zero4();
-            float kq = 0.f;
+            floatx4 w = zero4();
 #pragma unroll
             for (int i = 0; i < RPT; i += 4) {
                 const floatx4 k4 = *reinterpret_cast<const floatx4 *>(kv + i);
@@ -267,40 +298,23 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
                     w += k4[j] * s[i + j];
                 }
             }
-            if constexpr (OUT) {  // y = S'^T q and k . q
+            // lane (b4, b5) finishes column cj of its group: w, then u = beta (v - w)
+            const float wj = rg_sum_scatter(w, b4, b5);
+            const float uj = beta[row] * (to_f32(v[row * DV + col + cj]) - wj);
+            const floatx4 u = rg_gather(uj, b4, b5);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) s[i] += kf[i] * u;
+            if constexpr (OUT) {  // o = S^T q of the updated state
                 const float *qv = &my[tt][2][wave_vec_idx<DK>(r0)];
+                floatx4 y = zero4();
 #pragma unroll
                 for (int i = 0; i < RPT; i += 4) {
                     const floatx4 q4 = *reinterpret_cast<const floatx4 *>(qv + i);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        y += q4[j] * s[i + j];
-                        kq += kf[i + j] * q4[j];
-                    }
+                    for (int j = 0; j < 4; ++j) y += q4[j] * s[i + j];
                 }
-            }
-#pragma unroll
-            for (int off = CG; off < kWave; off <<= 1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w[j] += __shfl_xor(w[j], off);
-                if constexpr (OUT) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) y[j] += __shfl_xor(y[j], off);
-                    kq += __shfl_xor(kq, off);
-                }
-            }
-            const float bt = beta[row];
-            float vf[4];
-            load_vec<4>(v + row * DV + col, vf);
-            const floatx4 u = floatx4{bt * (vf[0] - w[0]), bt * (vf[1] - w[1]), bt * (vf[2] - w[2]),
-                                      bt * (vf[3] - w[3])};
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) s[i] += kf[i] * u;
-            if constexpr (OUT) {
-                // o = S^T q after the update = y + (k . q) u
-                if (rg == 0)
-                    store4(o + row * DV + col, y[0] + kq * u[0], y[1] + kq * u[1], y[2] + kq * u[2],
-                           y[3] + kq * u[3]);
+                const float yj = rg_sum_scatter(y, b4, b5);
+                if (!(lane & CG)) o[row * DV + col + cj] = from_f32<T>(yj);
             }
         }
     }

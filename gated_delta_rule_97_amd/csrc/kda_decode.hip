@@ -14,6 +14,70 @@
 
 namespace kda {
 
+// Cross-lane moves on the VALU (no LDS traffic): xor 8 stays inside a
+// 16-lane row (DPP row_ror:8); v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second, so (x, y)
+// becomes (x_r0 | y_r0 | x_r2 | y_r2, x_r1 | y_r1 | x_r3 | y_r3); and
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 lanes of its second: (x, y) becomes (x_lo | y_lo, x_hi | y_hi).
+__device__ __forceinline__ float lane_xor8(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void lane_swap16(float x, float y, float &xs, float &ys) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    xs = __uint_as_float(r[0]);
+    ys = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void lane_swap32(float x, float y, float &xs, float &ys) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    xs = __uint_as_float(r[0]);
+    ys = __uint_as_float(r[1]);
+}
+
+// Sum over all 64 lanes, in every lane: the halves and the row pairs by
+// swaps, then rotations inside each 16-lane row.
+__device__ __forceinline__ float wave_sum(float x) {
+    float a, b;
+    lane_swap32(x, x, a, b);
+    x = a + b;
+    lane_swap16(x, x, a, b);
+    x = a + b;
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xF, 0xF, false));  // row_ror:2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xF, 0xF, false));  // row_ror:1
+    return x;
+}
+
+// For a wave whose lanes are 8 * row group + column group: the sum of a
+// float4 over the eight row groups, reduce-scattered: the lanes
+// whose row-group bits 4 and 5 are b4 and b5 get the sum of component
+// 2 b5 + b4 (both lanes of a bit-3 pair the same value).  Each halving
+// moves only the components the partner keeps.
+__device__ __forceinline__ float rg_sum_scatter(floatx4 x, int b4, int b5) {
+    float p0, p1, q0, q1;
+    lane_swap32(x[0], x[2], p0, p1);  // p0 + p1: component 0 in the lower half, 2 in the upper
+    lane_swap32(x[1], x[3], q0, q1);
+    const float a = p0 + p1, b = q0 + q1;  // components 2 b5 and 2 b5 + 1
+    float a2, b2;
+    lane_swap16(a, b, a2, b2);
+    const float r = a2 + b2;  // component 2 b5 in even rows, 2 b5 + 1 in odd rows
+    return r + lane_xor8(r);
+}
+
+// The inverse gather: lane (b4, b5) holds component 2 b5 + b4; every lane
+// gets all four.
+__device__ __forceinline__ floatx4 rg_gather(float x, int b4, int b5) {
+    float xe, xo;
+    lane_swap16(x, x, xe, xo);  // xe: even rows' values in each row pair, xo: odd rows'
+    const float o = b4 ? xe : xo;  // component 2 b5 + 1 - b4
+    const float lo = b4 ? o : x, hi = b4 ? x : o;  // components 2 b5, 2 b5 + 1
+    float p0, p1, q0, q1;
+    lane_swap32(lo, hi, p0, p1);  // lower half: p1 = component 2; upper half: p0 = component 1
+    lane_swap32(hi, lo, q0, q1);  // lower half: q1 = component 3; upper half: q0 = component 0
+    return b5 ? floatx4{q0, p0, lo, hi} : floatx4{lo, hi, p1, q1};
+}
+
 // Threads per workgroup of the single-token step: each thread holds a 4 x 4
 // block of the state (4 rows, one float4 of columns).  Small per-thread
 // slices keep the register count low enough for eight waves per SIMD, so
@@ -35,9 +99,9 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
     constexpr int NW = NTH / kWave; // wavefronts
     static_assert(RG * CG == NTH && RPT * RG == DK && RPT >= 1, "decode thread split");
     static_assert(CG <= kWave && kWave % CG == 0, "a wave spans whole row groups");
+    static_assert(CG <= kWave / 2, "row group 0 lies in wave 0");
     __shared__ float sk[DK], sq[DK], sd[DK];
     __shared__ float4 sw[NW][CG], sy[NW][CG];
-    __shared__ float skq;
 
     const size_t ch = blockIdx.x;  // sequence * H + head
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
@@ -54,13 +118,6 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
         sd[c] = exp_e(g[ch * DK + c]);
     }
     __syncthreads();
-    if (tid < kWave) {
-        float p = 0.f;
-        for (int c = tid; c < DK; c += kWave) p += sk[c] * sq[c];
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) p += __shfl_xor(p, off);
-        if (tid == 0) skq = p;
-    }
     // partial w = S'^T k and y = S'^T q over this thread's rows, then over
     // the row groups of the wave (lanes CG apart), then over the waves
     float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
@@ -72,16 +129,29 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
         w.x += kc * s[i][0]; w.y += kc * s[i][1]; w.z += kc * s[i][2]; w.w += kc * s[i][3];
         y.x += qc * s[i][0]; y.y += qc * s[i][1]; y.z += qc * s[i][2]; y.w += qc * s[i][3];
     }
+    if constexpr (2 * CG == kWave) {
+        // the wave's two row groups are its 32-lane halves: one swap per
+        // component leaves w's sums in the lower half and y's in the upper
+        float4 r;
+        float p, q;
+        lane_swap32(w.x, y.x, p, q); r.x = p + q;
+        lane_swap32(w.y, y.y, p, q); r.y = p + q;
+        lane_swap32(w.z, y.z, p, q); r.z = p + q;
+        lane_swap32(w.w, y.w, p, q); r.w = p + q;
+        if (lane < CG) sw[wid][cg] = r;
+        else sy[wid][cg] = r;
+    } else {
 #pragma unroll
-    for (int off = CG; off < kWave; off <<= 1) {
-        w.x += __shfl_xor(w.x, off); w.y += __shfl_xor(w.y, off);
-        w.z += __shfl_xor(w.z, off); w.w += __shfl_xor(w.w, off);
-        y.x += __shfl_xor(y.x, off); y.y += __shfl_xor(y.y, off);
-        y.z += __shfl_xor(y.z, off); y.w += __shfl_xor(y.w, off);
-    }
-    if (lane < CG) {
-        sw[wid][cg] = w;
-        sy[wid][cg] = y;
+        for (int off = CG; off < kWave; off <<= 1) {
+            w.x += __shfl_xor(w.x, off); w.y += __shfl_xor(w.y, off);
+            w.z += __shfl_xor(w.z, off); w.w += __shfl_xor(w.w, off);
+            y.x += __shfl_xor(y.x, off); y.y += __shfl_xor(y.y, off);
+            y.z += __shfl_xor(y.z, off); y.w += __shfl_xor(y.w, off);
+        }
+        if (lane < CG) {
+            sw[wid][cg] = w;
+            sy[wid][cg] = y;
+        }
     }
     __syncthreads();
     float4 W = make_float4(0.f, 0.f, 0.f, 0.f), Y = W;
@@ -106,9 +176,11 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
         r[0] += kc * u.x; r[1] += kc * u.y; r[2] += kc * u.z; r[3] += kc * u.w;
         __builtin_nontemporal_store(r, reinterpret_cast<floatx4 *>(S + size_t(c) * DV) + cg);
     }
-    if (rg == 0) {
-        const float kq = skq;
-        store4(o + ch * DV + 4 * cg, Y.x + kq * u.x, Y.y + kq * u.y, Y.z + kq * u.z, Y.w + kq * u.w);
+    if (wid == 0) {  // the o row: row group 0 lies in wave 0, which also sums k . q
+        float kq = 0.f;
+        for (int c = lane; c < DK; c += kWave) kq += sk[c] * sq[c];
+        kq = wave_sum(kq);
+        if (rg == 0) store4(o + ch * DV + 4 * cg, Y.x + kq * u.x, Y.y + kq * u.y, Y.z + kq * u.z, Y.w + kq * u.w);
     }
 }
 
@@ -145,55 +217,6 @@ constexpr int kWavePB = 4;   // waves per workgroup
 
 template <int DK>
 __device__ __forceinline__ int wave_vec_idx(int c) { return c + (c >> 4) * 4; }  // 4-float pad per 16: row groups hit distinct banks
-
-// Cross-lane moves over the row-group bits of a wave whose lanes are
-// 8 * row group + column group, all on the VALU: xor 8 stays inside a
-// 16-lane row (DPP row_ror:8); v_permlane16_swap exchanges the odd 16-lane
-// rows of its first operand with the even rows of its second, so (x, y)
-// becomes (x_r0 | y_r0 | x_r2 | y_r2, x_r1 | y_r1 | x_r3 | y_r3); and
-// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
-// the lower 32 lanes of its second: (x, y) becomes (x_lo | y_lo, x_hi | y_hi).
-__device__ __forceinline__ float lane_xor8(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
-}
-__device__ __forceinline__ void lane_swap16(float x, float y, float &xs, float &ys) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    xs = __uint_as_float(r[0]);
-    ys = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void lane_swap32(float x, float y, float &xs, float &ys) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    xs = __uint_as_float(r[0]);
-    ys = __uint_as_float(r[1]);
-}
-
-// Sum of a float4 over the eight row groups, reduce-scattered: the lanes
-// whose row-group bits 4 and 5 are b4 and b5 get the sum of component
-// 2 b5 + b4 (both lanes of a bit-3 pair the same value).  Each halving
-// moves only the components the partner keeps.
-__device__ __forceinline__ float rg_sum_scatter(floatx4 x, int b4, int b5) {
-    float p0, p1, q0, q1;
-    lane_swap32(x[0], x[2], p0, p1);  // p0 + p1: component 0 in the lower half, 2 in the upper
-    lane_swap32(x[1], x[3], q0, q1);
-    const float a = p0 + p1, b = q0 + q1;  // components 2 b5 and 2 b5 + 1
-    float a2, b2;
-    lane_swap16(a, b, a2, b2);
-    const float r = a2 + b2;  // component 2 b5 in even rows, 2 b5 + 1 in odd rows
-    return r + lane_xor8(r);
-}
-
-// The inverse gather: lane (b4, b5) holds component 2 b5 + b4; every lane
-// gets all four.
-__device__ __forceinline__ floatx4 rg_gather(float x, int b4, int b5) {
-    float xe, xo;
-    lane_swap16(x, x, xe, xo);  // xe: even rows' values in each row pair, xo: odd rows'
-    const float o = b4 ? xe : xo;  // component 2 b5 + 1 - b4
-    const float lo = b4 ? o : x, hi = b4 ? x : o;  // components 2 b5, 2 b5 + 1
-    float p0, p1, q0, q1;
-    lane_swap32(lo, hi, p0, p1);  // lower half: p1 = component 2; upper half: p0 = component 1
-    lane_swap32(hi, lo, q0, q1);  // lower half: q1 = component 3; upper half: q0 = component 0
-    return b5 ? floatx4{q0, p0, lo, hi} : floatx4{lo, hi, p1, q1};
-}
 
 template <class T, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(

@@ -1,4 +1,4 @@
-"""Chunk windows of the prefill (needs a GPU).
+"""Windows of the prefill: groups of whole sequences and chunk windows (needs a GPU).
 
 A fixed-length bf16 batch at d = 128, chunk 64 whose hand-off between the
 two passes passes 192 MiB runs as (intra-chunk pass, state pass) windows of

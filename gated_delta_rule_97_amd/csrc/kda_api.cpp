@@ -381,7 +381,7 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     const bool win = (wp.grp < N || wp.nchunk > 1) && sp.nseg == 1 && !(flags & KDA_FLAG_NO_WINDOWS);
     a.win_grp = win ? wp.grp : N;
     a.win_len = win ? (a.nc_seq + wp.nchunk - 1) / wp.nchunk : a.nc_seq;
-    a.nwin = win ? ((N + a.win_grp - 1) / a.win_grp) * wp.nchunk : 1;
+    a.nwin = win ? ((N + a.win_grp - 1) / a.win_grp) * ((a.nc_seq + a.win_len - 1) / a.win_len) : 1;
     a.win_n0 = 0;
     a.win_nn = N;
     a.win_c0 = 0;

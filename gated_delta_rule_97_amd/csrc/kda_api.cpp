@@ -421,6 +421,9 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     // sequences of 256 to 4096 tokens, 16 heads)
     const bool loader_fed = dtype == KDA_DTYPE_BF16 && dk == 128 && dv == 128 && chunk_size == 64;
     const int bv = (loader_fed || int64_t(N) * H * (dv / 32) < 512) ? 16 : 32;
+    a.fd_H = make_fastdiv(uint32_t(a.H));
+    a.fd_nc_seq = make_fastdiv(uint32_t(a.nc_seq));
+    a.fd_win_nn = make_fastdiv(uint32_t(a.win_nn));
     hipError_t e = (dtype == KDA_DTYPE_BF16) ? launch_prefill_bf16(a, dk, dv, chunk_size, bv, stream)
                                              : launch_prefill_f32(a, dk, dv, chunk_size, bv, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;

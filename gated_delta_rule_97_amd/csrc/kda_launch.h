@@ -8,6 +8,33 @@
 
 namespace kda {
 
+// Division by a divisor fixed for a launch, as a multiply-high and two
+// shifts (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, the round-up method for unsigned operands):
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the quotient
+// of any 32-bit n is (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0), where
+// t = mulhi(m, n).  Built on the host; a zero divisor is taken as 1.
+struct FastDiv {
+    uint32_t m;
+    uint32_t s1, s2;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    if (d == 0) d = 1;
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    FastDiv f;
+    f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    f.s1 = l < 1 ? l : 1;
+    f.s2 = l > 1 ? l - 1 : 0;
+    return f;
+}
+// n / d for a non-negative n (on the device, uniform operands stay scalar:
+// the high half of the 64-bit product is one s_mul_hi_u32)
+__host__ __device__ inline int fdiv(int n, const FastDiv &f) {
+    const uint32_t un = uint32_t(n), t = uint32_t((uint64_t(f.m) * un) >> 32);
+    return int((t + ((un - t) >> f.s1)) >> f.s2);
+}
+
 // Everything the prefill kernels need, by value.
 struct PrefillArgs {
     const void *q, *k, *v;     // [rows][H][dk|dv] in the compute dtype
@@ -55,6 +82,9 @@ struct PrefillArgs {
     // (0, N, 0, nc_seq: all).  nwin: the number of windows (1: none).
     int nwin, win_grp, win_len, win_n0, win_nn, win_c0, win_nc;
     float *carry;
+    // the divisions of the intra-chunk pass's item walk: by H, by nc_seq and
+    // by win_nn (set right before each launch)
+    FastDiv fd_H, fd_nc_seq, fd_win_nn;
 };
 
 // Segment plan of a prefill: segments when long fixed-length sequences have

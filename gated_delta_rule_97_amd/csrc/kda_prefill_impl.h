@@ -59,7 +59,7 @@ __device__ __forceinline__ int ld_const(const int32_t *p, int i) {
 
 __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C, ChunkLoc &out) {
     if (!a.cu) {
-        const int n = gc / a.nc_seq, ci = gc - n * a.nc_seq;
+        const int n = fdiv(gc, a.fd_nc_seq), ci = gc - n * a.nc_seq;
         if (n >= a.N) return false;
         out.seq = n;
         out.tok0 = n * a.T + ci * C;
@@ -87,7 +87,7 @@ __device__ __forceinline__ bool locate_chunk(const PrefillArgs &a, int gc, int C
 // starts there, then finds them still in the last-level cache.
 __device__ __forceinline__ int intra_slot(const PrefillArgs &a, int wc) {
     if (!a.cu) {  // chunks win_c0 .. win_c0 + win_nc - 1 of this launch's sequences
-        const int j = wc / a.win_nn;
+        const int j = fdiv(wc, a.fd_win_nn);
         return (a.win_n0 + wc - j * a.win_nn) * a.nc_seq + (a.win_c0 + a.win_nc - 1 - j);
     }
     return a.nc_max - 1 - wc;
@@ -101,7 +101,7 @@ __device__ __forceinline__ int intra_slot(const PrefillArgs &a, int wc) {
 // is intra_slot itself.
 __device__ __forceinline__ int intra_handoff(const PrefillArgs &a, int wc) {
     if (!a.cu) {
-        const int j = wc / a.win_nn;
+        const int j = fdiv(wc, a.fd_win_nn);
         return (wc - j * a.win_nn) * a.win_len + (a.win_nc - 1 - j);
     }
     return a.nc_max - 1 - wc;
@@ -497,10 +497,10 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     // first item of this workgroup with a valid chunk
     int item = blockIdx.x;
     ChunkLoc loc;
-    while (item < nitems && !locate_chunk(a, intra_slot(a, item / H), C, loc)) item += gridDim.x;
+    while (item < nitems && !locate_chunk(a, intra_slot(a, fdiv(item, a.fd_H)), C, loc)) item += gridDim.x;
     if (item >= nitems) return;
     In in;
-    intra_fetch(in, a, loc, item % H, int(threadIdx.x));
+    intra_fetch(in, a, loc, item - H * fdiv(item, a.fd_H), int(threadIdx.x));
     // beta of the chunk: one value per lane of the last wave (which loads no
     // other input), staged in LDS at the top of each item
     constexpr int kBetaWave = kIWaves - 1;
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
     int blen = 0;
     if (beta_wave) {
         const int t = min(int(threadIdx.x & 63), loc.len - 1);
-        bnx = a.beta[size_t(loc.tok0 + t) * H + item % H];
+        bnx = a.beta[size_t(loc.tok0 + t) * H + (item - H * fdiv(item, a.fd_H))];
         blen = loc.len;
     }
 
@@ -522,8 +522,8 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         const int tid = opaque(int(threadIdx.x)), lane = tid & 63;
         const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile math stays scalar
         const int grp = lane >> 4, l16 = lane & 15;
-        const int h = item % H;
-        const size_t slot = size_t(intra_handoff(a, item / H)) * H + h;
+        const int wc = fdiv(item, a.fd_H), h = item - H * wc;
+        const size_t slot = size_t(intra_handoff(a, wc)) * H + h;
         // The prefetched registers are consumed from here on, and only from
         // here: without this fence the compiler moves unpacking work up to
         // the loads at the end of the previous item, which then must wait
@@ -646,12 +646,12 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
         // the next item (its inputs are requested during the inversion below)
         const ChunkLoc cur = loc;
         int nxt = item + gridDim.x;
-        while (nxt < nitems && !locate_chunk(a, intra_slot(a, nxt / H), C, loc)) nxt += gridDim.x;
+        while (nxt < nitems && !locate_chunk(a, intra_slot(a, fdiv(nxt, a.fd_H)), C, loc)) nxt += gridDim.x;
         if (nxt >= nitems) {  // no next item: the prefetch below (never used) reads one row
             loc = cur;
             loc.len = 1;
         }
-        const int nxt_h = (nxt < nitems ? nxt : item) % H;
+        const int nxt_i = nxt < nitems ? nxt : item, nxt_h = nxt_i - H * fdiv(nxt_i, a.fd_H);
         __syncthreads();
 
         // ---- A (strictly lower, row-scaled by beta) and P (lower incl.) on
@@ -2055,6 +2055,7 @@ hipError_t launch_prefill_instance(const PrefillArgs &a, hipStream_t s) {
                     PrefillArgs b = a;
                     b.win_n0 = n0;
                     b.win_nn = min(a.win_grp, a.N - n0);
+                    b.fd_win_nn = make_fastdiv(uint32_t(b.win_nn));
                     b.win_c0 = c0;
                     b.win_nc = min(a.win_len, a.nc_seq - c0);
                     if (c0 > 0) b.h0 = a.carry;

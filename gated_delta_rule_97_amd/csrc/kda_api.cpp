@@ -19,12 +19,19 @@ namespace kda {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq) {
+SegPlan seg_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq) {
     // worth it when the chains (32-column blocks) number under half a device
     // of compute units and the sequences are long; each segment keeps at
-    // least 8 chunks, and the segments aim at ~1024 chains in all
+    // least 8 chunks, and the segments aim at ~1024 chains in all.  "Long"
+    // depends on the single chain it replaces: the loader-fed chain (bf16,
+    // dk = dv = 128, chunk 64) keeps up until at least 128 chunks and three
+    // chunks per 32-column chain (measured: 64 chunks 0.84-0.93x, H = 16 at
+    // 128 chunks 0.84x, 128 chunks at up to 32 chains 1.05-1.15x), the other
+    // chains until 64 chunks
     const int64_t chains = int64_t(N) * H * (dv >= 32 ? dv / 32 : 1);
-    if (packed || chains <= 0 || chains >= 128 || nc_seq < 64) return SegPlan{1, 0};
+    const bool loader_fed = dtype == KDA_DTYPE_BF16 && dk == 128 && dv == 128 && C == 64;
+    const int64_t min_nc = loader_fed ? std::max<int64_t>(128, 3 * chains) : 64;
+    if (packed || chains <= 0 || chains >= 128 || nc_seq < min_nc) return SegPlan{1, 0};
     int64_t nseg = (1024 + chains - 1) / chains;
     if (nseg > nc_seq / 8) nseg = nc_seq / 8;
     if (nseg < 2) return SegPlan{1, 0};
@@ -264,7 +271,7 @@ int kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int nu
     // segment buffers when the fixed-length reading of these sizes segments,
     // the window carry when it runs in windows
     const int ncs = (T + chunk_size - 1) / chunk_size;
-    const int nseg = (num_seqs == B) ? seg_plan(false, B, H, dv, ncs).nseg : 1;
+    const int nseg = (num_seqs == B) ? seg_plan(false, dtype, dk, dv, chunk_size, B, H, ncs).nseg : 1;
     const bool carry = num_seqs == B && win_plan(false, dtype, dk, dv, chunk_size, B, H, ncs, nseg).nchunk > 1;
     *bytes = prefill_layout(nc, H, num_seqs, dk, dv, chunk_size, dtype_bytes(dtype), nseg, carry).total;
     return KDA_OK;
@@ -336,10 +343,11 @@ int prefill_impl(const void *q, const void *k, const void *v, const float *g, co
     }
 
     const SegPlan sp = (flags & KDA_FLAG_NO_SEGMENTS) ? SegPlan{1, 0}
-                                                     : seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
+                                                     : seg_plan(packed, dtype, dk, dv, chunk_size, N, H,
+                                                                (T + chunk_size - 1) / chunk_size);
     // the layout is the one the size query computed (segment buffers present
     // whenever the sizes call for them, also when a flag turns them off)
-    const SegPlan sp_ws = seg_plan(packed, N, H, dv, (T + chunk_size - 1) / chunk_size);
+    const SegPlan sp_ws = seg_plan(packed, dtype, dk, dv, chunk_size, N, H, (T + chunk_size - 1) / chunk_size);
     const WinPlan wp = win_plan(packed, dtype, dk, dv, chunk_size, N, H, (T + chunk_size - 1) / chunk_size, sp_ws.nseg);
     const PrefillLayout L = prefill_layout(nc_max, H, N, dk, dv, chunk_size, eb, sp_ws.nseg, wp.nchunk > 1);
     unsigned char *ws = static_cast<unsigned char *>(workspace);

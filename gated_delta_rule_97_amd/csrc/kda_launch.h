@@ -93,7 +93,7 @@ struct PrefillArgs {
 struct SegPlan {
     int nseg, seg_len;  // nseg 1, seg_len 0: no segmentation
 };
-SegPlan seg_plan(bool packed, int N, int H, int dv, int nc_seq);
+SegPlan seg_plan(bool packed, int dtype, int dk, int dv, int C, int N, int H, int nc_seq);
 
 // Windows of a prefill: win_grp sequences per window and chunk windows per
 // sequence (nchunk > 1 only with win_grp = 1); {N, 1}: none.  A pure

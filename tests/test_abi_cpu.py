@@ -73,7 +73,9 @@ def test_workspace_segment_states_follow_the_plan():
     with 32 segments per head: the workspace adds three fp32 dk x dv states per
     (segment, head), the two summaries and the scanned incoming state.  The
     H = 32, T = 8192 call (128 chains) and a sequence under 64 chunks run one
-    chain per head and add none."""
+    chain per head and add none; so does a 64-chunk sequence at d = 128, bf16,
+    chunk 64, where the loader-fed single chain is faster, while 128 chunks
+    of one head take 16 segments of 8."""
     per_slot = 4 * 64 * 128 * 2 + 6 * 16 * 32 * 2 + 128 * 4
     st = 128 * 128 * 4
 
@@ -84,6 +86,8 @@ def test_workspace_segment_states_follow_the_plan():
     assert 3 * 32 * 8 * st <= extra(1 << 20, 8) < 3 * 32 * 8 * st + (1 << 20)
     assert 32 * st <= extra(8192, 32) < 33 * st  # no segments; the chunk-window carry
     assert 0 <= extra(63 * 64, 1) < st
+    assert 0 <= extra(64 * 64, 1) < st
+    assert 3 * 16 * st <= extra(128 * 64, 1) < 3 * 16 * st + (1 << 20)
 
 
 def test_workspace_window_carry_follows_the_plan():

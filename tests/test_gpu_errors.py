@@ -79,7 +79,7 @@ def _nan_case(segmented, which):
     channel j); returns (inputs, GPU o, GPU ht, oracle o, oracle ht, n, t, h,
     j) with o as [B, T, H, dv]."""
     import gated_delta_rule_97_amd as kda
-    T = 64 * 64 + 37 if segmented else 300
+    T = 128 * 64 + 37 if segmented else 300
     H = 1 if segmented else 3
     spec = Spec(H=H, dk=128, dv=128, T=T, B=2, dtype="bf16", chunk=64, h0_std=1.0, g_mode="slow", seed=112)
     x = workloads.make_prefill(spec)

@@ -21,7 +21,8 @@ its own bytes, "path_roofline" gives the whole call's fraction.
 Also measured and reported in the same JSON line: decode (256 sequences x 32
 heads, d = 128, 128 consecutive in-place steps); packed variable-length
 prefill (64 sequences of U[256, 4096] tokens, H = 16); under "next":
-speculative verify/commit of 4 draft tokens on the decode batch, the
+speculative verify/commit of 4 draft tokens on the decode batch (token by
+token, and from the update vectors a verify kept), the
 headline prefill with a state checkpoint every 512 tokens, and the 1M-token
 x 8-head prefill (segment-parallel chain, and the single chain for
 comparison); roofline fractions against MI355X peaks (HBM 8 TB/s; bf16 MFMA
@@ -397,12 +398,25 @@ def main():
         st_c = state0.clone()
         t_commit = (timed(lambda: kda.decode_commit(drafts["k"], drafts["v"], drafts["g"], drafts["beta"], nacc,
                                                     st_c), 20) if with_commit else float("nan"))
+        if with_commit:  # verify that keeps the update vectors, and the commit from them
+            uk = torch.empty((dspec.N, K, dspec.H, dspec.dv), dtype=torch.float32, device=dev)
+            t_vkeep = timed(lambda: kda.decode_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"],
+                                                      drafts["beta"], st_v, o=ov, u=uk), 20)
+            st_k = state0.clone()
+            t_ckept = timed(lambda: kda.decode_commit(drafts["k"], None, drafts["g"], None, nacc, st_k, u=uk), 20)
+            del uk, st_k
+        else:
+            t_vkeep = t_ckept = float("nan")
         nh = dspec.N * dspec.H
         vbytes = nh * (dspec.dk * dspec.dv * 4 + K * 1540)            # state read once + K tokens' vectors
         cbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * 1284)        # state read + written, no q or o
+        # state read + written; k (bf16), g (fp32) and the kept u (fp32) of K tokens
+        kbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * (dspec.dk * 2 + dspec.dk * 4 + dspec.dv * 4))
         vgbs = vbytes / (t_verify * 1e-3) / 1e9
         cgbs = cbytes / (t_commit * 1e-3) / 1e9
-        log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s)")
+        kgbs = kbytes / (t_ckept * 1e-3) / 1e9
+        log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s); "
+            f"keeping u: verify {t_vkeep * 1e3:.1f} us, commit from u {t_ckept * 1e3:.1f} us ({kgbs:.0f} GB/s)")
         r = lambda x, nd: None if x != x else round(x, nd)  # NaN (not measured) -> null
         verify = {"workload": f"decode batch N={dspec.N} H={dspec.H} d=128 bf16, {K} draft tokens",
                   "verify_us": round(t_verify * 1e3, 2), "commit_us": r(t_commit * 1e3, 2),
@@ -415,7 +429,14 @@ def main():
                                "algorithmic_bytes_per_launch": vbytes},
                   "commit_roofline": {"kernel": "kda_decode_commit", "bound": "hbm", "achieved": r(cgbs, 1),
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": r(cgbs / HBM_PEAK_GBS, 4),
-                                      "avg_launch_us": r(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes}}
+                                      "avg_launch_us": r(t_commit * 1e3, 2), "algorithmic_bytes_per_launch": cbytes},
+                  # verify keeping each draft's update vector, then the commit from them
+                  "verify_keep_us": r(t_vkeep * 1e3, 2), "commit_kept_us": r(t_ckept * 1e3, 2),
+                  "vs_k_decode_steps_kept": r(K * dec_launch_us / (t_vkeep * 1e3 + t_ckept * 1e3), 3),
+                  "commit_kept_roofline": {"kernel": "kda_decode_commit_kept", "bound": "hbm", "achieved": r(kgbs, 1),
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": r(kgbs / HBM_PEAK_GBS, 4), "avg_launch_us": r(t_ckept * 1e3, 2),
+                                           "algorithmic_bytes_per_launch": kbytes}}
         del drafts, ov, st_v, st_c
         return verify
 

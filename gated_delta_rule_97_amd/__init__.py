@@ -77,6 +77,10 @@ _lib.kda_decode_verify.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i
 _lib.kda_decode_verify.restype = _i
 _lib.kda_decode_commit.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _u, _vp]
 _lib.kda_decode_commit.restype = _i
+_lib.kda_decode_verify_keep.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _u, _vp]
+_lib.kda_decode_verify_keep.restype = _i
+_lib.kda_decode_commit_kept.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _u, _vp]
+_lib.kda_decode_commit_kept.restype = _i
 _lib.kda_status_string.argtypes = [_i]
 _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_profile_start.argtypes = [_i]
@@ -148,6 +152,18 @@ def kda_decode_commit(k, v, g, beta, n_accept, state, N, K, H, dk, dv, dtype, fl
     """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
     return _lib.kda_decode_commit(k or None, v or None, g or None, beta or None, n_accept or None,
                                   state or None, N, K, H, dk, dv, dtype, flags, stream or None)
+
+
+def kda_decode_verify_keep(q, k, v, g, beta, state, o, u, N, K, H, dk, dv, dtype, flags, stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_decode_verify_keep(q or None, k or None, v or None, g or None, beta or None, state or None,
+                                       o or None, u or None, N, K, H, dk, dv, dtype, flags, stream or None)
+
+
+def kda_decode_commit_kept(k, g, u, n_accept, state, N, K, H, dk, dv, dtype, flags, stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_decode_commit_kept(k or None, g or None, u or None, n_accept or None, state or None, N, K, H,
+                                       dk, dv, dtype, flags, stream or None)
 
 
 def kda_profile_start(max_launches: int) -> None:
@@ -281,32 +297,49 @@ def decode_step(q, k, v, g, beta, state, o=None, *, flags=0, stream=None):
     return o
 
 
-def decode_verify(q, k, v, g, beta, state, o=None, *, flags=0, stream=None):
+def decode_verify(q, k, v, g, beta, state, o=None, *, keep_u=False, u=None, flags=0, stream=None):
     """K draft tokens per sequence from the committed state (left unchanged):
     q, k [N, K, H, dk]; v [N, K, H, dv]; g [N, K, H, dk] fp32; beta [N, K, H]
-    fp32; state [N, H, dk, dv] fp32.  Returns o [N, K, H, dv]."""
+    fp32; state [N, H, dk, dv] fp32.  Returns o [N, K, H, dv]; with keep_u
+    (or a u buffer given) also each draft's update vector u [N, K, H, dv]
+    fp32, for decode_commit(..., u=u), and returns (o, u)."""
     torch = _torch()
     N, K, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
     if o is None:
         o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
-    st = kda_decode_verify(_ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
-                           _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
-                           _ptr(state, torch.float32, "state"), _ptr(o, q.dtype, "o"),
-                           N, K, H, dk, dv, dt, flags, _stream(stream))
+    keep = keep_u or u is not None
+    if keep and u is None:
+        u = torch.empty((N, K, H, dv), dtype=torch.float32, device=q.device)
+    args = (_ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"), _ptr(g, torch.float32, "g"),
+            _ptr(beta, torch.float32, "beta"), _ptr(state, torch.float32, "state"), _ptr(o, q.dtype, "o"))
+    if keep:
+        st = kda_decode_verify_keep(*args, _ptr(u, torch.float32, "u"), N, K, H, dk, dv, dt, flags, _stream(stream))
+    else:
+        st = kda_decode_verify(*args, N, K, H, dk, dv, dt, flags, _stream(stream))
     if st != KDA_OK:
-        raise KdaError(st, "kda_decode_verify")
-    return o
+        raise KdaError(st, "kda_decode_verify_keep" if keep else "kda_decode_verify")
+    return (o, u) if keep else o
 
 
-def decode_commit(k, v, g, beta, n_accept, state, *, flags=0, stream=None):
+def decode_commit(k, v, g, beta, n_accept, state, *, u=None, flags=0, stream=None):
     """Folds the first n_accept[n] (int32 [N] on the device) of the K draft
-    tokens into each sequence's state, in place.  Returns state."""
+    tokens into each sequence's state, in place.  With u, the update vectors
+    decode_verify kept on this same state and these drafts, the accepted
+    drafts are applied in closed form from them (v and beta are then not
+    read).  Returns state."""
     torch = _torch()
     N, K, H, dk = k.shape
-    dv = v.shape[-1]
+    dv = state.shape[-1]
     dt = _dtype_code(k)
+    if u is not None:
+        st = kda_decode_commit_kept(_ptr(k, k.dtype, "k"), _ptr(g, torch.float32, "g"), _ptr(u, torch.float32, "u"),
+                                    _ptr(n_accept, torch.int32, "n_accept"), _ptr(state, torch.float32, "state"),
+                                    N, K, H, dk, dv, dt, flags, _stream(stream))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_decode_commit_kept")
+        return state
     st = kda_decode_commit(_ptr(k, k.dtype, "k"), _ptr(v, k.dtype, "v"), _ptr(g, torch.float32, "g"),
                            _ptr(beta, torch.float32, "beta"), _ptr(n_accept, torch.int32, "n_accept"),
                            _ptr(state, torch.float32, "state"), N, K, H, dk, dv, dt, flags, _stream(stream))

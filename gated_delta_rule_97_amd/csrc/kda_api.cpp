@@ -544,7 +544,35 @@ int kda_decode_verify(const void *q, const void *k, const void *v, const float *
         if (run_checks(g, rows * dk, nullptr, 0, 0, nullptr, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
         if (flag & 1u) return KDA_ERR_DECAY_BOUND;
     }
-    hipError_t e = launch_decode_verify(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, N, K, H, dk,
+    hipError_t e = launch_decode_verify(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, nullptr, N, K,
+                                        H, dk, dv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_decode_verify_keep(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                           const float *state, void *o, float *u, int N, int K, int H, int dk, int dv,
+                           kda_dtype dtype, unsigned flags, hipStream_t stream) {
+    int st = decode_multi_shape(N, K, H, dk, dv, dtype);
+    if (st != KDA_OK) return st;
+    if (N == 0 || K == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o || !u) return KDA_ERR_NULL;
+    for (const void *p : {q, k, v, (const void *)g, (const void *)beta, (const void *)state, (const void *)o,
+                          (const void *)u})
+        if (misaligned(p, 16)) return KDA_ERR_ALIGN;
+    const size_t rows = size_t(N) * K * H, eb = dtype_bytes(dtype);
+    const size_t nstate = size_t(N) * H * dk * dv * 4, no = rows * dv * eb, nu = rows * dv * 4;
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{q, rows * dk * eb}, {k, rows * dk * eb}, {v, rows * dv * eb}, {g, rows * dk * 4},
+                       {beta, rows * 4}, {state, nstate}};
+    for (const Buf &b : ins)
+        if (overlap(o, no, b.p, b.n) || overlap(u, nu, b.p, b.n)) return KDA_ERR_ALIAS;
+    if (overlap(o, no, u, nu)) return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        unsigned flag = 0;
+        if (run_checks(g, rows * dk, nullptr, 0, 0, nullptr, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    hipError_t e = launch_decode_verify(dtype == KDA_DTYPE_BF16 ? 1 : 0, q, k, v, g, beta, state, o, u, N, K, H, dk,
                                         dv, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -573,6 +601,31 @@ int kda_decode_commit(const void *k, const void *v, const float *g, const float 
     }
     hipError_t e = launch_decode_commit(dtype == KDA_DTYPE_BF16 ? 1 : 0, k, v, g, beta, n_accept, state, N, K, H,
                                         dk, dv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_decode_commit_kept(const void *k, const float *g, const float *u, const int32_t *n_accept, float *state,
+                           int N, int K, int H, int dk, int dv, kda_dtype dtype, unsigned flags, hipStream_t stream) {
+    int st = decode_multi_shape(N, K, H, dk, dv, dtype);
+    if (st != KDA_OK) return st;
+    if (N == 0 || K == 0) return KDA_OK;
+    if (!k || !g || !u || !n_accept || !state) return KDA_ERR_NULL;
+    for (const void *p : {k, (const void *)g, (const void *)u, (const void *)state})
+        if (misaligned(p, 16)) return KDA_ERR_ALIGN;
+    if (misaligned(n_accept, 4)) return KDA_ERR_ALIGN;
+    const size_t rows = size_t(N) * K * H, eb = dtype_bytes(dtype);
+    const size_t nstate = size_t(N) * H * dk * dv * 4;
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{k, rows * dk * eb}, {g, rows * dk * 4}, {u, rows * dv * 4}, {n_accept, size_t(N) * 4}};
+    for (const Buf &b : ins)
+        if (overlap(state, nstate, b.p, b.n)) return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_CHECK_DECAY) {
+        unsigned flag = 0;
+        if (run_checks(g, rows * dk, nullptr, 0, 0, nullptr, stream, &flag) != hipSuccess) return KDA_ERR_LAUNCH;
+        if (flag & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    hipError_t e = launch_decode_commit_kept(dtype == KDA_DTYPE_BF16 ? 1 : 0, k, g, u, n_accept, state, N, K, H, dk,
+                                             dv, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

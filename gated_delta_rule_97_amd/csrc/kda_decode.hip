@@ -222,7 +222,7 @@ template <class T, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ n_accept, float *__restrict__ state,
-    T *__restrict__ o, int K, int H, int nwaves) {
+    T *__restrict__ o, float *__restrict__ u_out, int K, int H, int nwaves) {
     constexpr int CW = wave_columns<DV>();  // value columns of one wave
     constexpr int CG = CW / 4;              // float4 column groups: lanes cg = lane % CG
     constexpr int RG = kWave / CG;          // row groups: lanes rg = lane / CG
@@ -327,6 +327,8 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
             const floatx4 u = rg_gather(uj, b4, b5);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) s[i] += kf[i] * u;
+            if constexpr (MODE == kVerify)  // the update vector, kept for a commit from it
+                if (u_out && !(lane & CG)) u_out[row * DV + col + cj] = uj;
             if constexpr (OUT) {  // o = S^T q of the updated state
                 const float *qv = &my[tt][2][wave_vec_idx<DK>(r0)];
                 floatx4 y = zero4();
@@ -350,8 +352,8 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
 
 template <class T, int DK, int DV, int MODE>
 static hipError_t launch_wave_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
-                                const int32_t *n_accept, float *state, void *o, int N, int K, int H, hipStream_t s,
-                                const char *name) {
+                                const int32_t *n_accept, float *state, void *o, float *u_out, int N, int K, int H,
+                                hipStream_t s, const char *name) {
     if (N == 0 || K == 0) return hipSuccess;
     constexpr int NB = DV / wave_columns<DV>();
     const int nwaves = N * H * NB;
@@ -359,21 +361,21 @@ static hipError_t launch_wave_t(const void *q, const void *k, const void *v, con
     prof_begin(s);
     hipLaunchKernelGGL((kda_decode_wave_kernel<T, DK, DV, MODE>), dim3((nwaves + WPB - 1) / WPB), dim3(WPB * kWave),
                        0, s, static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
-                       n_accept, state, static_cast<T *>(o), K, H, nwaves);
+                       n_accept, state, static_cast<T *>(o), u_out, K, H, nwaves);
     prof_end(s, name);
     return hipGetLastError();
 }
 
 template <class T, bool VERIFY>
 static hipError_t multi_dispatch(int dk, int dv, const void *q, const void *k, const void *v, const float *g,
-                                 const float *beta, const int32_t *n_accept, float *state, void *o, int N, int K,
-                                 int H, hipStream_t s) {
+                                 const float *beta, const int32_t *n_accept, float *state, void *o, float *u_out,
+                                 int N, int K, int H, hipStream_t s) {
 #define KDA_MUL(DK_, DV_)                                                                                          \
     if (dk == DK_ && dv == DV_)                                                                                    \
-        return VERIFY ? launch_wave_t<T, DK_, DV_, kVerify>(q, k, v, g, beta, n_accept, state, o, N, K, H, s,      \
-                                                            "kda_decode_verify")                                   \
-                      : launch_wave_t<T, DK_, DV_, kCommit>(q, k, v, g, beta, n_accept, state, o, N, K, H, s,      \
-                                                            "kda_decode_commit");
+        return VERIFY ? launch_wave_t<T, DK_, DV_, kVerify>(q, k, v, g, beta, n_accept, state, o, u_out, N, K, H, \
+                                                            s, "kda_decode_verify")                                \
+                      : launch_wave_t<T, DK_, DV_, kCommit>(q, k, v, g, beta, n_accept, state, o, nullptr, N, K,   \
+                                                            H, s, "kda_decode_commit");
     KDA_MUL(32, 32) KDA_MUL(32, 64) KDA_MUL(32, 128)
     KDA_MUL(64, 32) KDA_MUL(64, 64) KDA_MUL(64, 128)
     KDA_MUL(128, 32) KDA_MUL(128, 64) KDA_MUL(128, 128)
@@ -382,19 +384,121 @@ static hipError_t multi_dispatch(int dk, int dv, const void *q, const void *k, c
 }
 
 hipError_t launch_decode_verify(int dtype, const void *q, const void *k, const void *v, const float *g,
-                                const float *beta, const float *state, void *o, int N, int K, int H, int dk,
-                                int dv, hipStream_t s) {
+                                const float *beta, const float *state, void *o, float *u_out, int N, int K, int H,
+                                int dk, int dv, hipStream_t s) {
     float *st = const_cast<float *>(state);  // read only in this mode
-    if (dtype == 1) return multi_dispatch<bf16, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, N, K, H, s);
-    return multi_dispatch<float, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, N, K, H, s);
+    if (dtype == 1) return multi_dispatch<bf16, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, u_out, N, K, H, s);
+    return multi_dispatch<float, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, u_out, N, K, H, s);
 }
 
 hipError_t launch_decode_commit(int dtype, const void *k, const void *v, const float *g, const float *beta,
                                 const int32_t *n_accept, float *state, int N, int K, int H, int dk, int dv,
                                 hipStream_t s) {
-    if (dtype == 1) return multi_dispatch<bf16, false>(dk, dv, nullptr, k, v, g, beta, n_accept, state, nullptr, N,
-                                                       K, H, s);
-    return multi_dispatch<float, false>(dk, dv, nullptr, k, v, g, beta, n_accept, state, nullptr, N, K, H, s);
+    if (dtype == 1) return multi_dispatch<bf16, false>(dk, dv, nullptr, k, v, g, beta, n_accept, state, nullptr,
+                                                       nullptr, N, K, H, s);
+    return multi_dispatch<float, false>(dk, dv, nullptr, k, v, g, beta, n_accept, state, nullptr, nullptr, N, K, H,
+                                        s);
+}
+
+// Commit from the update vectors a verify kept (same committed state, same
+// drafts).  Unrolling the recurrence S_t = Diag(e^{g_t}) S_{t-1} + k_t u_t^T
+// over the first n drafts gives
+//   S_n = Diag(D_0) S_0 + sum_{t<n} Diag(D_{t+1}) k_t u_t^T,
+// where D_t is the per-row product of e^g over drafts t .. n-1 (D_n = 1), so
+// with u_t known no reduction over dk is left: per group of up to KG drafts
+// the factors D_{t+1} k_t and D_0 of each row are formed in LDS, and every
+// thread updates its 4 x 4 blocks (the single-step layout) with one multiply
+// and one FMA per draft.  The state is read and written once.
+template <class T, int DK, int DV, int NTH>
+__global__ __launch_bounds__(NTH) void kda_decode_commit_kept_kernel(const T *__restrict__ k,
+                                                                     const float *__restrict__ g,
+                                                                     const float *__restrict__ u,
+                                                                     const int32_t *__restrict__ n_accept,
+                                                                     float *__restrict__ state, int K, int H) {
+    constexpr int CG = DV / 4;    // float4 column groups
+    constexpr int RG = NTH / CG;  // row groups
+    constexpr int RPT = DK / RG;  // rows per thread
+    constexpr int KG = 8;         // drafts per staged group
+    static_assert(RG * CG == NTH && RPT * RG == DK && RPT >= 1, "commit thread split");
+    __shared__ float sk[KG][DK], se[KG][DK], sf[KG][DK], sd[DK];
+    __shared__ floatx4 su[KG][CG];
+
+    const int ch = blockIdx.x;  // sequence * H + head
+    const int n = ch / H, h = ch - n * H;
+    const int na0 = n_accept[n];
+    const int na = na0 < 0 ? 0 : (na0 > K ? K : na0);
+    if (na == 0) return;  // the whole workgroup leaves: nothing accepted
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    float *S = state + size_t(ch) * DK * DV;
+    floatx4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)  // rows i * RG + rg
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
+    for (int g0 = 0; g0 < na; g0 += KG) {
+        const int ng = min(KG, na - g0);
+        if (g0 > 0) __syncthreads();  // the previous group's factors are read
+        for (int e = tid; e < ng * DK; e += NTH) {
+            const int t = e / DK, c = e - t * DK;
+            const size_t row = (size_t(n) * K + g0 + t) * H + h;
+            sk[t][c] = to_f32(k[row * DK + c]);
+            se[t][c] = exp_e(g[row * DK + c]);
+        }
+        for (int e = tid; e < ng * CG; e += NTH) {
+            const int t = e / CG, c4 = e - t * CG;
+            su[t][c4] = reinterpret_cast<const floatx4 *>(u + ((size_t(n) * K + g0 + t) * H + h) * DV)[c4];
+        }
+        __syncthreads();
+        for (int r = tid; r < DK; r += NTH) {
+            float p = 1.f;
+            for (int t = ng - 1; t >= 0; --t) {
+                sf[t][r] = sk[t][r] * p;
+                p *= se[t][r];
+            }
+            sd[r] = p;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = i * RG + rg;
+            floatx4 acc = sd[r] * s[i];
+            for (int t = 0; t < ng; ++t) acc += sf[t][r] * su[t][cg];
+            s[i] = acc;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4 *>(S + size_t(i * RG + rg) * DV) + cg);
+}
+
+template <class T, int DK, int DV>
+static hipError_t launch_commit_kept_t(const void *k, const float *g, const float *u, const int32_t *n_accept,
+                                       float *state, int N, int K, int H, hipStream_t s) {
+    if (N == 0 || K == 0) return hipSuccess;
+    constexpr int NTH = decode_threads<DK, DV>();
+    prof_begin(s);
+    hipLaunchKernelGGL((kda_decode_commit_kept_kernel<T, DK, DV, NTH>), dim3(N * H), dim3(NTH), 0, s,
+                       static_cast<const T *>(k), g, u, n_accept, state, K, H);
+    prof_end(s, "kda_decode_commit_kept");
+    return hipGetLastError();
+}
+
+template <class T>
+static hipError_t commit_kept_dispatch(int dk, int dv, const void *k, const float *g, const float *u,
+                                       const int32_t *n_accept, float *state, int N, int K, int H, hipStream_t s) {
+#define KDA_CK(DK_, DV_) \
+    if (dk == DK_ && dv == DV_) return launch_commit_kept_t<T, DK_, DV_>(k, g, u, n_accept, state, N, K, H, s);
+    KDA_CK(32, 32) KDA_CK(32, 64) KDA_CK(32, 128)
+    KDA_CK(64, 32) KDA_CK(64, 64) KDA_CK(64, 128)
+    KDA_CK(128, 32) KDA_CK(128, 64) KDA_CK(128, 128)
+#undef KDA_CK
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_commit_kept(int dtype, const void *k, const float *g, const float *u,
+                                     const int32_t *n_accept, float *state, int N, int K, int H, int dk, int dv,
+                                     hipStream_t s) {
+    if (dtype == 1) return commit_kept_dispatch<bf16>(dk, dv, k, g, u, n_accept, state, N, K, H, s);
+    return commit_kept_dispatch<float>(dk, dv, k, g, u, n_accept, state, N, K, H, s);
 }
 
 template <class T, int DK, int DV>

@@ -154,13 +154,19 @@ hipError_t launch_decode(int dtype, const void *q, const void *k,
                          const void *v, const float *g, const float *beta,
                          float *state, void *o, int N, int H, int dk, int dv,
                          hipStream_t s);
-// K decode tokens per sequence from one state read: outputs only (verify),
-// or the first n_accept[n] tokens folded into the state (commit).
+// K decode tokens per sequence from one state read: outputs only (verify;
+// u_out non-null also keeps each draft's update vector, fp32 [N][K][H][dv]),
+// or the first n_accept[n] tokens folded into the state (commit), or folded
+// from the kept update vectors (commit_kept).
 hipError_t launch_decode_verify(int dtype, const void *q, const void *k,
                                 const void *v, const float *g,
                                 const float *beta, const float *state,
-                                void *o, int N, int K, int H, int dk, int dv,
-                                hipStream_t s);
+                                void *o, float *u_out, int N, int K, int H,
+                                int dk, int dv, hipStream_t s);
+hipError_t launch_decode_commit_kept(int dtype, const void *k, const float *g,
+                                     const float *u, const int32_t *n_accept,
+                                     float *state, int N, int K, int H, int dk,
+                                     int dv, hipStream_t s);
 hipError_t launch_decode_commit(int dtype, const void *k, const void *v,
                                 const float *g, const float *beta,
                                 const int32_t *n_accept, float *state, int N,

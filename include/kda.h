@@ -222,10 +222,12 @@ int kda_decode_step(const void *q, const void *k, const void *v,
  * Speculative decoding (the serving-stack section of the blog post: K
  * drafted tokens are checked in one pass from the committed recurrent
  * state, rebuilt on chip from the cached per-token inputs, then the
- * accepted prefix is committed).  Both calls read each (sequence, head)
- * state from HBM once and apply the decode step's arithmetic token by token
- * with the state held on chip.  Token t of sequence n is row n * K + t of
- * the [N, K, H, d] inputs.
+ * accepted prefix is committed).  Every call reads each (sequence, head)
+ * state from HBM once; verify, verify_keep and commit apply the decode
+ * step's arithmetic token by token with the state held on chip, and
+ * commit_kept applies the accepted drafts in closed form from the update
+ * vectors verify_keep kept.  Token t of sequence n is row n * K + t of the
+ * [N, K, H, d] inputs.
  *
  * kda_decode_verify: outputs of all K tokens; the state is only read.
  *   q, k  [N, K, H, dk] dtype   v [N, K, H, dv] dtype
@@ -251,6 +253,39 @@ int kda_decode_commit(const void *k, const void *v, const float *g,
                       const float *beta, const int32_t *n_accept,
                       float *state, int N, int K, int H, int dk, int dv,
                       kda_dtype dtype, unsigned flags, hipStream_t stream);
+
+/*
+ * kda_decode_verify_keep: kda_decode_verify that also keeps, for every draft
+ * token, its update vector u_t = beta_t (v_t - S'^T k_t) (the value the
+ * recurrence adds along k_t, S' the state decayed by e^{g_t} after drafts
+ * 0..t-1), so that a commit need not recompute it.
+ *   inputs and o as in kda_decode_verify
+ *   u     [N, K, H, dv] float32, written; must not overlap any input or o
+ * o is bit-identical to kda_decode_verify's.
+ */
+int kda_decode_verify_keep(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           const float *state, void *o, float *u, int N,
+                           int K, int H, int dk, int dv, kda_dtype dtype,
+                           unsigned flags, hipStream_t stream);
+
+/*
+ * kda_decode_commit_kept: kda_decode_commit from the update vectors that
+ * kda_decode_verify_keep kept on the same committed state and drafts: with
+ * D_t the per-row product of e^g over drafts t .. n-1, the state after the
+ * first n drafts is Diag(D_0) S + sum_{t<n} Diag(D_{t+1}) k_t u_t^T, one
+ * streaming pass over the state with no reduction over dk (same result as
+ * kda_decode_commit up to rounding order).  If the state changed since the
+ * verify, the result is not that of the drafts.
+ *   k [N, K, H, dk] dtype; g [N, K, H, dk] float32; u [N, K, H, dv] float32
+ *   n_accept device int32 [N], clamped to [0, K] (0 leaves the state as is)
+ *   state [N, H, dk, dv] float32, read and written in place; it must not
+ *   overlap any input.
+ */
+int kda_decode_commit_kept(const void *k, const float *g, const float *u,
+                           const int32_t *n_accept, float *state, int N, int K,
+                           int H, int dk, int dv, kda_dtype dtype,
+                           unsigned flags, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(int status);

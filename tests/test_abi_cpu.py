@@ -262,10 +262,54 @@ def test_commit_validation(kw, status):
     assert _commit(**kw) == status
 
 
+def _verify_keep(**kw):
+    args = dict(q=A, k=A + (1 << 24), v=A + (2 << 24), g=A + (3 << 24), beta=A + (4 << 24),
+                state=A + (5 << 24), o=A + (6 << 24), u=A + (8 << 24), N=4, K=3, H=2, dk=128, dv=128, dtype=BF16,
+                flags=0, stream=0)
+    args.update(kw)
+    return kda.kda_decode_verify_keep(**args)
+
+
+def _commit_kept(**kw):
+    args = dict(k=A + (1 << 24), g=A + (3 << 24), u=A + (8 << 24), n_accept=A + (7 << 24), state=A + (5 << 24),
+                N=4, K=3, H=2, dk=128, dv=128, dtype=BF16, flags=0, stream=0)
+    args.update(kw)
+    return kda.kda_decode_commit_kept(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dv=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(u=0), kda.KDA_ERR_NULL),
+    (dict(o=0), kda.KDA_ERR_NULL),
+    (dict(u=A + (8 << 24) + 4), kda.KDA_ERR_ALIGN),
+    (dict(u=A + (5 << 24) + 4096), kda.KDA_ERR_ALIAS),                # u inside the state
+    (dict(u=A + (6 << 24) + 512), kda.KDA_ERR_ALIAS),                 # u overlaps o
+    (dict(u=A + 256), kda.KDA_ERR_ALIAS),                             # u overlaps q
+])
+def test_verify_keep_validation(kw, status):
+    assert _verify_keep(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(K=-1), kda.KDA_ERR_SHAPE),
+    (dict(u=0), kda.KDA_ERR_NULL),
+    (dict(n_accept=0), kda.KDA_ERR_NULL),
+    (dict(u=A + (8 << 24) + 8), kda.KDA_ERR_ALIGN),
+    (dict(n_accept=A + (7 << 24) + 2), kda.KDA_ERR_ALIGN),
+    (dict(state=A + (8 << 24) + 1024), kda.KDA_ERR_ALIAS),            # state overlaps u
+    (dict(state=A + (3 << 24) + 1024), kda.KDA_ERR_ALIAS),            # state overlaps g
+])
+def test_commit_kept_validation(kw, status):
+    assert _commit_kept(**kw) == status
+
+
 def test_verify_commit_empty():
     assert _verify(N=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
     assert _verify(K=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
     assert _commit(N=0, k=0, v=0, g=0, beta=0, n_accept=0, state=0) == kda.KDA_OK
+    assert _verify_keep(K=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0, u=0) == kda.KDA_OK
+    assert _commit_kept(N=0, k=0, g=0, u=0, n_accept=0, state=0) == kda.KDA_OK
 
 
 def _noalloc(**kw):

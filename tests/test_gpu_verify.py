@@ -165,3 +165,75 @@ def test_verify_and_commit_span_staging_groups(K, dtype):
             assert torch.equal(st[n].cpu(), state0[n])
         else:
             assert rel_l2(got[n], s_ref[n]) <= tol, f"sequence {n} ({a} accepted)"
+
+
+@pytest.mark.parametrize("dk,dv,dtype,K,n_acc", [
+    (128, 128, "bf16", 4, [0, 1, 2, 4, 3, -2, 9, 4]),
+    (64, 32, "bf16", 7, [7, 0, 3, 5, 1, 6, 2, 8]),
+    (32, 128, "fp32", 3, [3, 1, 0, 2, 3, 3, -1, 2]),
+    (128, 64, "fp32", 12, [12, 8, 9, 0, 1, 7, 11, 15]),  # two staging groups of 8
+])
+def test_commit_from_kept_updates(dk, dv, dtype, K, n_acc):
+    """verify with keep_u gives verify's outputs bit for bit and each draft's
+    update vector; the commit from those vectors reaches the oracle's state
+    after the accepted drafts (clamped to [0, K]), agrees with the token-by-
+    token commit up to rounding order, and leaves sequences that accepted
+    nothing exactly as they were."""
+    import gated_delta_rule_97_amd as kda
+    N = len(n_acc)
+    spec = workloads.DecodeSpec(N=N, H=3, dk=dk, dv=dv, steps=K, dtype=dtype, state_std=1.0, g_mode="slow",
+                                seed=66)
+    state0 = workloads.make_decode_state(spec)
+    x = workloads.make_decode_drafts(spec, K)
+    d = {key: val.cuda() for key, val in x.items()}
+    st = state0.cuda()
+    o1 = kda.decode_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], st)
+    o2, u = kda.decode_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], st, keep_u=True)
+    acc = torch.tensor(n_acc, dtype=torch.int32).cuda()
+    kept = st.clone()
+    kda.decode_commit(d["k"], None, d["g"], None, acc, kept, u=u)
+    plain = st.clone()
+    kda.decode_commit(d["k"], d["v"], d["g"], d["beta"], acc, plain)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "verify_keep's outputs must be verify's"
+    assert torch.equal(st.cpu(), state0), "verify must not write the state"
+    assert torch.isfinite(u).all()
+    clamped = [min(max(a, 0), K) for a in n_acc]
+    _, s_ref = oracle_drafts(x, state0, clamped)
+    tol = TOL_FP32 if dtype == "fp32" else TOL_BF16
+    got, gp = kept.double().cpu().numpy(), plain.double().cpu().numpy()
+    worst = 0.0
+    for n, a in enumerate(clamped):
+        if a == 0:
+            assert torch.equal(kept[n].cpu(), state0[n]), f"sequence {n} accepted nothing"
+            continue
+        e = rel_l2(got[n], s_ref[n])
+        worst = max(worst, e)
+        assert e <= tol, f"sequence {n} ({a} accepted): {e:.2e}"
+        assert rel_l2(got[n], gp[n]) <= 1e-5, f"sequence {n}: kept vs token-by-token commit"
+    print(f"[verify] commit from kept updates dk={dk} dv={dv} {dtype} K={K}: worst state {worst:.2e}", flush=True)
+
+
+def test_commit_from_kept_updates_headline_batch():
+    """The 256 x 32 batch with 4 drafts, every sequence accepting a different
+    count: the kept commit against the oracle's states."""
+    import gated_delta_rule_97_amd as kda
+    K = 4
+    spec = workloads.DECODE
+    state0 = workloads.make_decode_state(spec)
+    x = workloads.make_decode_drafts(spec, K)
+    d = {key: val.cuda() for key, val in x.items()}
+    st = state0.cuda()
+    _, u = kda.decode_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], st, keep_u=True)
+    n_acc = [n % (K + 1) for n in range(spec.N)]
+    kda.decode_commit(d["k"], None, d["g"], None, torch.tensor(n_acc, dtype=torch.int32).cuda(), st, u=u)
+    torch.cuda.synchronize()
+    _, s_ref = oracle_drafts(x, state0, n_acc)
+    got = st.double().cpu().numpy()
+    sel = [n for n in range(spec.N) if n_acc[n] > 0]
+    e = rel_l2(got[sel], s_ref[sel])
+    print(f"[verify] headline batch, commit from kept updates: state {e:.2e}", flush=True)
+    assert e <= TOL_BF16
+    for n in range(spec.N):
+        if n_acc[n] == 0:
+            assert torch.equal(st[n].cpu(), state0[n])

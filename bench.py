@@ -22,7 +22,8 @@ Also measured and reported in the same JSON line: decode (256 sequences x 32
 heads, d = 128, 128 consecutive in-place steps); packed variable-length
 prefill (64 sequences of U[256, 4096] tokens, H = 16); under "next":
 speculative verify/commit of 4 draft tokens on the decode batch (token by
-token, and from the update vectors a verify kept), the
+token, from the update vectors a verify kept, and a whole round of commit and
+verify in one pass over the states), the
 headline prefill with a state checkpoint every 512 tokens, and the 1M-token
 x 8-head prefill (segment-parallel chain, and the single chain for
 comparison); roofline fractions against MI355X peaks (HBM 8 TB/s; bf16 MFMA
@@ -404,19 +405,29 @@ def main():
                                                       drafts["beta"], st_v, o=ov, u=uk), 20)
             st_k = state0.clone()
             t_ckept = timed(lambda: kda.decode_commit(drafts["k"], None, drafts["g"], None, nacc, st_k, u=uk), 20)
-            del uk, st_k
+            # one round in one pass: the accepted drafts committed from their
+            # kept u, then the next drafts verified from the committed state
+            uk2, st_f = torch.empty_like(uk), state0.clone()
+            t_round = timed(lambda: kda.decode_commit_verify((drafts["k"], drafts["g"], uk, nacc), drafts["q"],
+                                                             drafts["k"], drafts["v"], drafts["g"], drafts["beta"],
+                                                             st_f, o=ov, u=uk2), 20)
+            del uk, uk2, st_k, st_f
         else:
-            t_vkeep = t_ckept = float("nan")
+            t_vkeep = t_ckept = t_round = float("nan")
         nh = dspec.N * dspec.H
         vbytes = nh * (dspec.dk * dspec.dv * 4 + K * 1540)            # state read once + K tokens' vectors
         cbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * 1284)        # state read + written, no q or o
         # state read + written; k (bf16), g (fp32) and the kept u (fp32) of K tokens
         kbytes = nh * (2 * dspec.dk * dspec.dv * 4 + K * (dspec.dk * 2 + dspec.dk * 4 + dspec.dv * 4))
+        # a round in one pass: the state read + written, the accepted drafts' k, g, u, the new drafts'
+        # vectors and outputs, and their kept u
+        rbytes = kbytes + nh * K * (1540 + dspec.dv * 4)
         vgbs = vbytes / (t_verify * 1e-3) / 1e9
         cgbs = cbytes / (t_commit * 1e-3) / 1e9
         kgbs = kbytes / (t_ckept * 1e-3) / 1e9
         log(f"verify K={K}: {t_verify * 1e3:.1f} us ({vgbs:.0f} GB/s); commit {t_commit * 1e3:.1f} us ({cgbs:.0f} GB/s); "
-            f"keeping u: verify {t_vkeep * 1e3:.1f} us, commit from u {t_ckept * 1e3:.1f} us ({kgbs:.0f} GB/s)")
+            f"keeping u: verify {t_vkeep * 1e3:.1f} us, commit from u {t_ckept * 1e3:.1f} us ({kgbs:.0f} GB/s); "
+            f"fused round {t_round * 1e3:.1f} us")
         r = lambda x, nd: None if x != x else round(x, nd)  # NaN (not measured) -> null
         verify = {"workload": f"decode batch N={dspec.N} H={dspec.H} d=128 bf16, {K} draft tokens",
                   "verify_us": round(t_verify * 1e3, 2), "commit_us": r(t_commit * 1e3, 2),
@@ -433,6 +444,16 @@ def main():
                   # verify keeping each draft's update vector, then the commit from them
                   "verify_keep_us": r(t_vkeep * 1e3, 2), "commit_kept_us": r(t_ckept * 1e3, 2),
                   "vs_k_decode_steps_kept": r(K * dec_launch_us / (t_vkeep * 1e3 + t_ckept * 1e3), 3),
+                  # a speculative round (commit of K accepted drafts + verify of K new ones) three ways
+                  "round_us": {"commit_then_verify": r((t_commit + t_verify) * 1e3, 2),
+                               "kept_commit_then_verify": r((t_ckept + t_vkeep) * 1e3, 2),
+                               "commit_verify_one_pass": r(t_round * 1e3, 2)},
+                  "commit_verify_roofline": {"kernel": "kda_decode_commit_verify", "bound": "hbm",
+                                             "achieved": r(rbytes / (t_round * 1e-3) / 1e9, 1),
+                                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                             "frac": r(rbytes / (t_round * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                             "avg_launch_us": r(t_round * 1e3, 2),
+                                             "algorithmic_bytes_per_launch": rbytes},
                   "commit_kept_roofline": {"kernel": "kda_decode_commit_kept", "bound": "hbm", "achieved": r(kgbs, 1),
                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                            "frac": r(kgbs / HBM_PEAK_GBS, 4), "avg_launch_us": r(t_ckept * 1e3, 2),

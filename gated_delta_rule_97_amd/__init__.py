@@ -81,6 +81,9 @@ _lib.kda_decode_verify_keep.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, 
 _lib.kda_decode_verify_keep.restype = _i
 _lib.kda_decode_commit_kept.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _u, _vp]
 _lib.kda_decode_commit_kept.restype = _i
+_lib.kda_decode_commit_verify.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                          _i, _i, _i, _u, _vp]
+_lib.kda_decode_commit_verify.restype = _i
 _lib.kda_status_string.argtypes = [_i]
 _lib.kda_status_string.restype = ctypes.c_char_p
 _lib.kda_profile_start.argtypes = [_i]
@@ -164,6 +167,14 @@ def kda_decode_commit_kept(k, g, u, n_accept, state, N, K, H, dk, dv, dtype, fla
     """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
     return _lib.kda_decode_commit_kept(k or None, g or None, u or None, n_accept or None, state or None, N, K, H,
                                        dk, dv, dtype, flags, stream or None)
+
+
+def kda_decode_commit_verify(prev_k, prev_g, prev_u, n_accept, Kp, q, k, v, g, beta, state, o, u, N, K, H, dk, dv,
+                             dtype, flags, stream) -> int:
+    """Raw call; pointers are ints (0 = NULL).  Returns the status code."""
+    return _lib.kda_decode_commit_verify(prev_k or None, prev_g or None, prev_u or None, n_accept or None, Kp,
+                                         q or None, k or None, v or None, g or None, beta or None, state or None,
+                                         o or None, u or None, N, K, H, dk, dv, dtype, flags, stream or None)
 
 
 def kda_profile_start(max_launches: int) -> None:
@@ -320,6 +331,41 @@ def decode_verify(q, k, v, g, beta, state, o=None, *, keep_u=False, u=None, flag
         st = kda_decode_verify(*args, N, K, H, dk, dv, dt, flags, _stream(stream))
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_verify_keep" if keep else "kda_decode_verify")
+    return (o, u) if keep else o
+
+
+def decode_commit_verify(prev, q, k, v, g, beta, state, o=None, *, keep_u=True, u=None, flags=0, stream=None):
+    """One round of a speculative loop in one pass over the states: commits
+    the previous round's accepted drafts, prev = (k, g, u, n_accept) with u
+    the update vectors that round's verify kept (None: nothing to commit),
+    writes the committed state, and verifies the new drafts q, k, v, g, beta
+    [N, K, H, .] from it.  Returns (o, u) with u the new drafts' update
+    vectors for the next round (o only when keep_u is False and no u is
+    given)."""
+    torch = _torch()
+    N, K, H, dk = q.shape
+    dv = state.shape[-1]
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
+    keep = keep_u or u is not None
+    if keep and u is None:
+        u = torch.empty((N, K, H, dv), dtype=torch.float32, device=q.device)
+    if prev is None:
+        pk = pg = pu = pa = None
+        Kp = 0
+    else:
+        pk, pg, pu, pa = prev
+        Kp = pk.shape[1]
+    st = kda_decode_commit_verify(_ptr(pk, q.dtype, "prev k"), _ptr(pg, torch.float32, "prev g"),
+                                  _ptr(pu, torch.float32, "prev u"), _ptr(pa, torch.int32, "n_accept"), Kp,
+                                  _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
+                                  _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+                                  _ptr(state, torch.float32, "state"), _ptr(o, q.dtype, "o"),
+                                  _ptr(u, torch.float32, "u") if keep else 0, N, K, H, dk, dv, dt, flags,
+                                  _stream(stream))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_commit_verify")
     return (o, u) if keep else o
 
 

@@ -629,6 +629,47 @@ int kda_decode_commit_kept(const void *k, const float *g, const float *u, const 
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int kda_decode_commit_verify(const void *prev_k, const float *prev_g, const float *prev_u,
+                             const int32_t *n_accept, int Kp, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, float *state, void *o, float *u, int N, int K, int H,
+                             int dk, int dv, kda_dtype dtype, unsigned flags, hipStream_t stream) {
+    int st = decode_multi_shape(N, K, H, dk, dv, dtype);
+    if (st != KDA_OK) return st;
+    if (Kp < 0 || int64_t(N) * Kp * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0 || (K == 0 && Kp == 0)) return KDA_OK;
+    if (!state) return KDA_ERR_NULL;
+    if (Kp > 0 && (!prev_k || !prev_g || !prev_u || !n_accept)) return KDA_ERR_NULL;
+    if (K > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    const size_t eb = dtype_bytes(dtype), prows = size_t(N) * Kp * H, rows = size_t(N) * K * H;
+    const size_t nstate = size_t(N) * H * dk * dv * 4, no = rows * dv * eb, nu = rows * dv * 4;
+    struct Buf { const void *p; size_t n; };
+    const Buf ins[] = {{prev_k, prows * dk * eb}, {prev_g, prows * dk * 4}, {prev_u, prows * dv * 4},
+                       {n_accept, size_t(N) * 4}, {q, rows * dk * eb}, {k, rows * dk * eb}, {v, rows * dv * eb},
+                       {g, rows * dk * 4}, {beta, rows * 4}};
+    for (const Buf &b : ins) {
+        if (!b.p || b.n == 0) continue;
+        if (misaligned(b.p, b.p == n_accept ? 4 : 16)) return KDA_ERR_ALIGN;
+        if (overlap(state, nstate, b.p, b.n) || overlap(o, no, b.p, b.n) || overlap(u, nu, b.p, b.n))
+            return KDA_ERR_ALIAS;
+    }
+    if (misaligned(state, 16) || misaligned(o, 16) || misaligned(u, 16)) return KDA_ERR_ALIGN;
+    if (overlap(state, nstate, o, no) || overlap(state, nstate, u, nu) || overlap(o, no, u, nu)) return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_CHECK_DECAY) {  // both rounds' decays (each check reports its own flag)
+        unsigned fp = 0, fn = 0;
+        if (prows && run_checks(prev_g, prows * dk, nullptr, 0, 0, nullptr, stream, &fp) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+        if (rows && run_checks(g, rows * dk, nullptr, 0, 0, nullptr, stream, &fn) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+        if ((fp | fn) & 1u) return KDA_ERR_DECAY_BOUND;
+    }
+    const int dt = dtype == KDA_DTYPE_BF16 ? 1 : 0;
+    hipError_t e = (K == 0) ? launch_decode_commit_kept(dt, prev_k, prev_g, prev_u, n_accept, state, N, Kp, H, dk,
+                                                        dv, stream)
+                            : launch_decode_commit_verify(dt, prev_k, prev_g, prev_u, n_accept, Kp, q, k, v, g, beta,
+                                                          state, o, u, N, K, H, dk, dv, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 int kda_profile_start(int max_launches) {
     if (max_launches <= 0) return KDA_ERR_SHAPE;
     if (g_prof.active) return KDA_ERR_SHAPE;

@@ -9,6 +9,8 @@
 // loads its float4 slices of S, the two reductions over dk go through LDS,
 // and the updated slices are written back from registers.  This kernel is
 // bound by HBM bandwidth (about 0.86 flop per byte at dk = dv = 128).
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(NTH) void kda_decode_kernel(const T *__restrict__ q
 // rows of one float4 of columns, and the reductions over dk sum a lane's
 // rows and then its row groups by cross-lane moves.  No barrier.
 // ---------------------------------------------------------------------------
-enum DecodeMode { kVerify = 0, kCommit = 1, kStep = 2 };
+enum DecodeMode { kVerify = 0, kCommit = 1, kStep = 2, kCommitVerify = 3 };
 
 template <int DV>
 constexpr int wave_columns() { return DV < 32 ? DV : 32; }
@@ -222,13 +224,14 @@ template <class T, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ n_accept, float *__restrict__ state,
-    T *__restrict__ o, float *__restrict__ u_out, int K, int H, int nwaves) {
+    T *__restrict__ o, float *__restrict__ u_out, int K, int H, int nwaves, const T *__restrict__ pk,
+    const float *__restrict__ pg, const float *__restrict__ pu, const int32_t *__restrict__ pacc, int Kp) {
     constexpr int CW = wave_columns<DV>();  // value columns of one wave
     constexpr int CG = CW / 4;              // float4 column groups: lanes cg = lane % CG
     constexpr int RG = kWave / CG;          // row groups: lanes rg = lane / CG
     constexpr int RPT = DK / RG;            // consecutive rows per lane
     constexpr int NB = DV / CW;             // waves per (sequence, head)
-    constexpr bool OUT = MODE != kCommit, WRITE = MODE != kVerify;
+    constexpr bool OUT = MODE != kCommit, WRITE = MODE == kCommit || MODE == kStep;
     static_assert(CG * RG == kWave && RPT * RG == DK && RPT % 4 == 0 && DV % CW == 0, "decode wave split");
     static_assert(CG == 8, "row groups are lane bits 3..5");
     constexpr int NVEC = OUT ? 3 : 2;                   // staged per token: k, e^g (, q), as fp32
@@ -260,27 +263,31 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     for (int i = 0; i < RPT; ++i)
         s[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(S + size_t(r0 + i) * DV));
 
-    for (int t0 = 0; t0 < ntok; t0 += kWaveKG) {
-        const int nt = min(kWaveKG, ntok - t0);
-        // ---- stage the group's k, e^g (and q): unit j of token tt ----
-        u32x4 raw[ITER];
+    // Stage k, e^g (and q, for WQ) of tokens t0 .. t0 + nt - 1 of an [N][Kx][H]
+    // input into the wave's LDS region (k in vector 0, e^g in 1, q in 2):
+    // unit j of token tt, one 16-byte unit per lane and load
+    auto stage = [&](auto wq, const T *kp, const T *qp, const float *gp, int Kx, int t0, int nt) {
+        constexpr bool WQ = decltype(wq)::value;
+        constexpr int UTx = KU * (WQ ? 2 : 1) + GU;  // units per token
+        constexpr int ITx = (kWaveKG * UTx + kWave - 1) / kWave;
+        u32x4 raw[ITx];
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
-            const int u = min(lane + kWave * it, nt * UT - 1);  // past the group: a repeated (unused) load
-            const int tt = u / UT, j = u - tt * UT;
-            const size_t row = (size_t(n) * K + t0 + tt) * H + h;
-            const char *src = (j < KU) ? reinterpret_cast<const char *>(k + row * DK) + 16 * j
-                              : (OUT && j < 2 * KU) ? reinterpret_cast<const char *>(q + row * DK) + 16 * (j - KU)
-                                                    : reinterpret_cast<const char *>(g + row * DK) +
-                                                          16 * (j - (OUT ? 2 : 1) * KU);
+        for (int it = 0; it < ITx; ++it) {
+            const int u = min(lane + kWave * it, nt * UTx - 1);  // past the group: a repeated (unused) load
+            const int tt = u / UTx, j = u - tt * UTx;
+            const size_t row = (size_t(n) * Kx + t0 + tt) * H + h;
+            const char *src = (j < KU) ? reinterpret_cast<const char *>(kp + row * DK) + 16 * j
+                              : (WQ && j < 2 * KU) ? reinterpret_cast<const char *>(qp + row * DK) + 16 * (j - KU)
+                                                   : reinterpret_cast<const char *>(gp + row * DK) +
+                                                         16 * (j - (WQ ? 2 : 1) * KU);
             raw[it] = *reinterpret_cast<const u32x4 *>(src);
         }
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) {
+        for (int it = 0; it < ITx; ++it) {
             const int u = lane + kWave * it;
-            if (u < nt * UT) {
-                const int tt = u / UT, j = u - tt * UT;
-                if (j < (OUT ? 2 : 1) * KU) {  // k or q: EPU values of T
+            if (u < nt * UTx) {
+                const int tt = u / UTx, j = u - tt * UTx;
+                if (j < (WQ ? 2 : 1) * KU) {  // k or q: EPU values of T
                     const int vi = j < KU ? 0 : 2, c0 = EPU * (j < KU ? j : j - KU);
                     float *d = &my[tt][vi][wave_vec_idx<DK>(c0)];
                     if constexpr (sizeof(T) == 2) {
@@ -296,13 +303,59 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
                         *reinterpret_cast<u32x4 *>(d) = raw[it];
                     }
                 } else {  // g: four values, stored as e^g
-                    const int c0 = 4 * (j - (OUT ? 2 : 1) * KU);
+                    const int c0 = 4 * (j - (WQ ? 2 : 1) * KU);
                     *reinterpret_cast<floatx4 *>(&my[tt][1][wave_vec_idx<DK>(c0)]) =
                         floatx4{exp_e(__uint_as_float(raw[it][0])), exp_e(__uint_as_float(raw[it][1])),
                                 exp_e(__uint_as_float(raw[it][2])), exp_e(__uint_as_float(raw[it][3]))};
                 }
             }
         }
+    };
+
+    if constexpr (MODE == kCommitVerify) {
+        // the previous round's accepted drafts first, from the update vectors
+        // its verify kept: per token S' = Diag(e^g) S, then S = S' + k u^T, the
+        // commit's own two steps with u known (no reduction over dk); the
+        // committed state is written once, then verified from
+        const int pa = pacc ? pacc[n] : 0;
+        const int np = pa < 0 ? 0 : (pa > Kp ? Kp : pa);
+        static_assert(NVEC == 3 && CW <= DKP, "the q slot of the staging region holds u");
+        for (int t0 = 0; t0 < np; t0 += kWaveKG) {
+            const int nt = min(kWaveKG, np - t0);
+            // u of the wave's CW columns, staged in the (here unused) q slot
+            if (lane < CG * nt) {
+                const int tt = lane / CG, c4 = lane - tt * CG;
+                const size_t prow = (size_t(n) * Kp + t0 + tt) * H + h;
+                *reinterpret_cast<floatx4 *>(&my[tt][2][4 * c4]) =
+                    *reinterpret_cast<const floatx4 *>(pu + prow * DV + cb * CW + 4 * c4);
+            }
+            stage(std::integral_constant<bool, false>{}, pk, nullptr, pg, Kp, t0, nt);
+            for (int tt = 0; tt < nt; ++tt) {
+                const float *kv = &my[tt][0][wave_vec_idx<DK>(r0)];
+                const float *ev = &my[tt][1][wave_vec_idx<DK>(r0)];
+                const floatx4 ut = *reinterpret_cast<const floatx4 *>(&my[tt][2][4 * cg]);
+#pragma unroll
+                for (int i = 0; i < RPT; i += 4) {
+                    const floatx4 k4 = *reinterpret_cast<const floatx4 *>(kv + i);
+                    const floatx4 e4 = *reinterpret_cast<const floatx4 *>(ev + i);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        s[i + j] *= e4[j];
+                        s[i + j] += k4[j] * ut;
+                    }
+                }
+            }
+        }
+        if (np > 0) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+                __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4 *>(S + size_t(r0 + i) * DV));
+        }
+    }
+
+    for (int t0 = 0; t0 < ntok; t0 += kWaveKG) {
+        const int nt = min(kWaveKG, ntok - t0);
+        stage(std::integral_constant<bool, OUT>{}, k, q, g, K, t0, nt);
         // ---- the group's tokens, one after the other ----
         for (int tt = 0; tt < nt; ++tt) {
             const size_t row = (size_t(n) * K + t0 + tt) * H + h;  // token row of [N][K][H]
@@ -327,7 +380,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
             const floatx4 u = rg_gather(uj, b4, b5);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) s[i] += kf[i] * u;
-            if constexpr (MODE == kVerify)  // the update vector, kept for a commit from it
+            if constexpr (MODE == kVerify || MODE == kCommitVerify)  // kept for a commit from it
                 if (u_out && !(lane & CG)) u_out[row * DV + col + cj] = uj;
             if constexpr (OUT) {  // o = S^T q of the updated state
                 const float *qv = &my[tt][2][wave_vec_idx<DK>(r0)];
@@ -350,10 +403,17 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     }
 }
 
+struct PrevRound {  // the previous round's drafts, for a commit in front of a verify
+    const void *k = nullptr;
+    const float *g = nullptr, *u = nullptr;
+    const int32_t *n_accept = nullptr;
+    int K = 0;
+};
+
 template <class T, int DK, int DV, int MODE>
 static hipError_t launch_wave_t(const void *q, const void *k, const void *v, const float *g, const float *beta,
                                 const int32_t *n_accept, float *state, void *o, float *u_out, int N, int K, int H,
-                                hipStream_t s, const char *name) {
+                                hipStream_t s, const char *name, const PrevRound &pr = PrevRound{}) {
     if (N == 0 || K == 0) return hipSuccess;
     constexpr int NB = DV / wave_columns<DV>();
     const int nwaves = N * H * NB;
@@ -361,7 +421,8 @@ static hipError_t launch_wave_t(const void *q, const void *k, const void *v, con
     prof_begin(s);
     hipLaunchKernelGGL((kda_decode_wave_kernel<T, DK, DV, MODE>), dim3((nwaves + WPB - 1) / WPB), dim3(WPB * kWave),
                        0, s, static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), g, beta,
-                       n_accept, state, static_cast<T *>(o), u_out, K, H, nwaves);
+                       n_accept, state, static_cast<T *>(o), u_out, K, H, nwaves, static_cast<const T *>(pr.k), pr.g,
+                       pr.u, pr.n_accept, pr.K);
     prof_end(s, name);
     return hipGetLastError();
 }
@@ -389,6 +450,31 @@ hipError_t launch_decode_verify(int dtype, const void *q, const void *k, const v
     float *st = const_cast<float *>(state);  // read only in this mode
     if (dtype == 1) return multi_dispatch<bf16, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, u_out, N, K, H, s);
     return multi_dispatch<float, true>(dk, dv, q, k, v, g, beta, nullptr, st, o, u_out, N, K, H, s);
+}
+
+template <class T>
+static hipError_t commit_verify_dispatch(int dk, int dv, const void *q, const void *k, const void *v,
+                                         const float *g, const float *beta, float *state, void *o, float *u_out,
+                                         int N, int K, int H, const PrevRound &pr, hipStream_t s) {
+#define KDA_CV(DK_, DV_)                                                                                          \
+    if (dk == DK_ && dv == DV_)                                                                                   \
+        return launch_wave_t<T, DK_, DV_, kCommitVerify>(q, k, v, g, beta, nullptr, state, o, u_out, N, K, H, s,  \
+                                                         "kda_decode_commit_verify", pr);
+    KDA_CV(32, 32) KDA_CV(32, 64) KDA_CV(32, 128)
+    KDA_CV(64, 32) KDA_CV(64, 64) KDA_CV(64, 128)
+    KDA_CV(128, 32) KDA_CV(128, 64) KDA_CV(128, 128)
+#undef KDA_CV
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_commit_verify(int dtype, const void *pk, const float *pg, const float *pu,
+                                       const int32_t *pacc, int Kp, const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta, float *state, void *o, float *u_out,
+                                       int N, int K, int H, int dk, int dv, hipStream_t s) {
+    PrevRound pr;
+    pr.k = pk; pr.g = pg; pr.u = pu; pr.n_accept = pacc; pr.K = Kp;
+    if (dtype == 1) return commit_verify_dispatch<bf16>(dk, dv, q, k, v, g, beta, state, o, u_out, N, K, H, pr, s);
+    return commit_verify_dispatch<float>(dk, dv, q, k, v, g, beta, state, o, u_out, N, K, H, pr, s);
 }
 
 hipError_t launch_decode_commit(int dtype, const void *k, const void *v, const float *g, const float *beta,

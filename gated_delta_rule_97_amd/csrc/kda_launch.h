@@ -163,6 +163,15 @@ hipError_t launch_decode_verify(int dtype, const void *q, const void *k,
                                 const float *beta, const float *state,
                                 void *o, float *u_out, int N, int K, int H,
                                 int dk, int dv, hipStream_t s);
+// The previous round's accepted drafts folded in from its kept update
+// vectors (pk, pg, pu [N][Kp][H][..], pacc [N]), the committed state written,
+// then K new drafts verified from it (o, and u_out when non-null).
+hipError_t launch_decode_commit_verify(int dtype, const void *pk, const float *pg,
+                                       const float *pu, const int32_t *pacc, int Kp,
+                                       const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta, float *state,
+                                       void *o, float *u_out, int N, int K, int H, int dk,
+                                       int dv, hipStream_t s);
 hipError_t launch_decode_commit_kept(int dtype, const void *k, const float *g,
                                      const float *u, const int32_t *n_accept,
                                      float *state, int N, int K, int H, int dk,

@@ -224,9 +224,10 @@ int kda_decode_step(const void *q, const void *k, const void *v,
  * state, rebuilt on chip from the cached per-token inputs, then the
  * accepted prefix is committed).  Every call reads each (sequence, head)
  * state from HBM once; verify, verify_keep and commit apply the decode
- * step's arithmetic token by token with the state held on chip, and
+ * step's arithmetic token by token with the state held on chip,
  * commit_kept applies the accepted drafts in closed form from the update
- * vectors verify_keep kept.  Token t of sequence n is row n * K + t of the
+ * vectors verify_keep kept, and commit_verify folds one round's commit into
+ * the next round's verify.  Token t of sequence n is row n * K + t of the
  * [N, K, H, d] inputs.
  *
  * kda_decode_verify: outputs of all K tokens; the state is only read.
@@ -286,6 +287,35 @@ int kda_decode_commit_kept(const void *k, const float *g, const float *u,
                            const int32_t *n_accept, float *state, int N, int K,
                            int H, int dk, int dv, kda_dtype dtype,
                            unsigned flags, hipStream_t stream);
+
+/*
+ * kda_decode_commit_verify: one round of a speculative loop in one pass over
+ * the states: the previous round's accepted drafts are committed from the
+ * update vectors its verify kept (as kda_decode_commit_kept would, token by
+ * token with u known), the committed state is written, and K new drafts are
+ * verified from it (as kda_decode_verify_keep would).  Each state is read
+ * once and, when its sequence accepted a draft, written once.
+ *   prev_k [N, Kp, H, dk] dtype; prev_g [N, Kp, H, dk] float32;
+ *   prev_u [N, Kp, H, dv] float32 (kept by the previous round's verify on
+ *   this same state); n_accept device int32 [N], clamped to [0, Kp]; all
+ *   may be null when Kp == 0 (nothing to commit)
+ *   q, k, v, g, beta, o as in kda_decode_verify (may be null when K == 0:
+ *   commit only)
+ *   u     [N, K, H, dv] float32 or null: the new drafts' update vectors, for
+ *         the next round
+ *   state [N, H, dk, dv] float32, read and written in place; state, o and u
+ *         must not overlap each other or any input.
+ * The committed state equals kda_decode_commit's bit for bit when the
+ * previous round's u was kept from the same state, and o (and u) then equal
+ * kda_decode_verify_keep's from that committed state.
+ */
+int kda_decode_commit_verify(const void *prev_k, const float *prev_g,
+                             const float *prev_u, const int32_t *n_accept,
+                             int Kp, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta,
+                             float *state, void *o, float *u, int N, int K,
+                             int H, int dk, int dv, kda_dtype dtype,
+                             unsigned flags, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(int status);

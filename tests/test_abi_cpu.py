@@ -304,6 +304,39 @@ def test_commit_kept_validation(kw, status):
     assert _commit_kept(**kw) == status
 
 
+def _commit_verify(**kw):
+    args = dict(prev_k=A + (1 << 24), prev_g=A + (3 << 24), prev_u=A + (8 << 24), n_accept=A + (7 << 24), Kp=3,
+                q=A + (9 << 24), k=A + (10 << 24), v=A + (11 << 24), g=A + (12 << 24), beta=A + (13 << 24),
+                state=A + (5 << 24), o=A + (6 << 24), u=A + (14 << 24), N=4, K=3, H=2, dk=128, dv=128, dtype=BF16,
+                flags=0, stream=0)
+    args.update(kw)
+    return kda.kda_decode_commit_verify(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(Kp=-1), kda.KDA_ERR_SHAPE),
+    (dict(prev_u=0), kda.KDA_ERR_NULL),                              # a previous round needs its kept u
+    (dict(n_accept=0), kda.KDA_ERR_NULL),
+    (dict(q=0), kda.KDA_ERR_NULL),
+    (dict(state=0), kda.KDA_ERR_NULL),
+    (dict(prev_u=A + (8 << 24) + 4), kda.KDA_ERR_ALIGN),
+    (dict(n_accept=A + (7 << 24) + 2), kda.KDA_ERR_ALIGN),
+    (dict(u=A + (5 << 24) + 4096), kda.KDA_ERR_ALIAS),               # new u inside the state
+    (dict(state=A + (8 << 24) + 1024), kda.KDA_ERR_ALIAS),           # state overlaps the kept u
+    (dict(o=A + (9 << 24) + 512), kda.KDA_ERR_ALIAS),                # o overlaps q
+])
+def test_commit_verify_validation(kw, status):
+    assert _commit_verify(**kw) == status
+
+
+def test_commit_verify_optional_parts():
+    # nothing to commit (Kp = 0, no previous buffers) and nothing to verify (K = 0, no draft buffers)
+    assert _commit_verify(N=0) == kda.KDA_OK
+    assert _commit_verify(Kp=0, K=0, prev_k=0, prev_g=0, prev_u=0, n_accept=0, q=0, k=0, v=0, g=0, beta=0, o=0,
+                          u=0) == kda.KDA_OK
+
+
 def test_verify_commit_empty():
     assert _verify(N=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK
     assert _verify(K=0, q=0, k=0, v=0, g=0, beta=0, state=0, o=0) == kda.KDA_OK

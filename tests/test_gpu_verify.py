@@ -237,3 +237,82 @@ def test_commit_from_kept_updates_headline_batch():
     for n in range(spec.N):
         if n_acc[n] == 0:
             assert torch.equal(st[n].cpu(), state0[n])
+
+
+@pytest.mark.parametrize("dk,dv,dtype,Kp,K,n_acc", [
+    (128, 128, "bf16", 4, 4, [0, 1, 2, 4, 3, -2, 9, 4]),
+    (64, 32, "bf16", 7, 3, [7, 0, 3, 5, 1, 6, 2, 8]),
+    (32, 128, "fp32", 3, 6, [3, 1, 0, 2, 3, 3, -1, 2]),
+    (128, 64, "fp32", 9, 5, [9, 8, 5, 0, 1, 4, 7, 12]),  # two staging groups of the commit
+])
+def test_commit_verify_round(dk, dv, dtype, Kp, K, n_acc):
+    """One speculative round in one pass: the previous drafts' accepted
+    prefix committed from the update vectors their verify kept (the state
+    equal to the token-by-token commit's bit for bit), then the new drafts
+    verified from it (o and u equal to verify with kept u on that state)."""
+    import gated_delta_rule_97_amd as kda
+    N = len(n_acc)
+    spec = workloads.DecodeSpec(N=N, H=3, dk=dk, dv=dv, steps=Kp + K, dtype=dtype, state_std=1.0, g_mode="slow",
+                                seed=67)
+    state0 = workloads.make_decode_state(spec)
+    xa = workloads.make_decode_drafts(spec, Kp)
+    xb = workloads.make_decode_drafts(spec, K, first_step=Kp)
+    a = {key: val.cuda() for key, val in xa.items()}
+    b = {key: val.cuda() for key, val in xb.items()}
+    acc = torch.tensor(n_acc, dtype=torch.int32).cuda()
+    st0 = state0.cuda()
+    _, ua = kda.decode_verify(a["q"], a["k"], a["v"], a["g"], a["beta"], st0, keep_u=True)
+    # reference path: token-by-token commit, then verify keeping u
+    s_ref = st0.clone()
+    kda.decode_commit(a["k"], a["v"], a["g"], a["beta"], acc, s_ref)
+    ob_ref, ub_ref = kda.decode_verify(b["q"], b["k"], b["v"], b["g"], b["beta"], s_ref, keep_u=True)
+    # fused round
+    st = st0.clone()
+    ob, ub = kda.decode_commit_verify((a["k"], a["g"], ua, acc), b["q"], b["k"], b["v"], b["g"], b["beta"], st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s_ref), "the committed state must be the token-by-token commit's"
+    assert torch.equal(ob, ob_ref) and torch.equal(ub, ub_ref), "o and u must be verify's on the committed state"
+    # and against the oracle: the state after each sequence's accepted prefix,
+    # then the new drafts' outputs from there
+    clamped = [min(max(x, 0), Kp) for x in n_acc]
+    _, s_or = oracle_drafts(xa, state0, clamped)
+    o_or, _ = oracle_drafts(xb, torch.from_numpy(s_or.astype(np.float32)))
+    tol = TOL_FP32 if dtype == "fp32" else TOL_BF16
+    e_s = rel_l2(st.double().cpu().numpy(), s_or)
+    e_o = rel_l2(ob.double().cpu().numpy(), o_or)
+    print(f"[verify] commit+verify round dk={dk} dv={dv} {dtype} Kp={Kp} K={K}: state {e_s:.2e} o {e_o:.2e}",
+          flush=True)
+    assert e_s <= tol and e_o <= tol
+
+
+def test_commit_verify_edges():
+    """No previous round (a verify keeping u), no new drafts (a commit from
+    kept u), and a round in which no sequence accepted anything (the state is
+    left as it was)."""
+    import gated_delta_rule_97_amd as kda
+    K = 4
+    spec = workloads.DecodeSpec(N=5, H=2, dk=128, dv=128, steps=2 * K, dtype="bf16", state_std=1.0, g_mode="slow",
+                                seed=68)
+    state0 = workloads.make_decode_state(spec).cuda()
+    a = {key: val.cuda() for key, val in workloads.make_decode_drafts(spec, K).items()}
+    b = {key: val.cuda() for key, val in workloads.make_decode_drafts(spec, K, first_step=K).items()}
+    st = state0.clone()
+    o1, u1 = kda.decode_commit_verify(None, a["q"], a["k"], a["v"], a["g"], a["beta"], st)
+    o2, u2 = kda.decode_verify(a["q"], a["k"], a["v"], a["g"], a["beta"], state0, keep_u=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(u1, u2) and torch.equal(st, state0)
+    acc = torch.tensor([4, 0, 2, 1, 3], dtype=torch.int32).cuda()
+    s_commit = state0.clone()
+    kda.decode_commit(a["k"], None, a["g"], None, acc, s_commit, u=u2)
+    s_fused = state0.clone()
+    empty = {key: val[:, :0].contiguous() for key, val in b.items()}
+    kda.decode_commit_verify((a["k"], a["g"], u2, acc), empty["q"], empty["k"], empty["v"], empty["g"],
+                             empty["beta"], s_fused)
+    torch.cuda.synchronize()
+    assert torch.equal(s_fused, s_commit), "K = 0: a commit from kept u"
+    none = torch.zeros(5, dtype=torch.int32).cuda()
+    st = state0.clone()
+    ob, _ = kda.decode_commit_verify((a["k"], a["g"], u2, none), b["q"], b["k"], b["v"], b["g"], b["beta"], st)
+    ob_ref = kda.decode_verify(b["q"], b["k"], b["v"], b["g"], b["beta"], state0)
+    torch.cuda.synchronize()
+    assert torch.equal(st, state0) and torch.equal(ob, ob_ref), "nothing accepted: the state stays as it was"

@@ -1083,7 +1083,8 @@ __device__ __forceinline__ void inter_ckpt(const PrefillArgs &a, const floatx4 (
         if (item < Cfg::NSI) {
             const int m = item % Cfg::NRT, nn = item / Cfg::NRT;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
+            for (int r = 0; r < 4; ++r)  // non-temporal: read by no later step of this call
+                __builtin_nontemporal_store(S[i][r], dst + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16);
         }
     }
 }
@@ -1214,7 +1215,8 @@ __global__ __launch_bounds__(kThreads) void kda_inter_kernel(PrefillArgs a) {
             if (item < NSI) {
                 const int m = item % NRT, nn = item / NRT;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
+                for (int r = 0; r < 4; ++r)  // non-temporal: read by no later step of this call
+                __builtin_nontemporal_store(S[i][r], dst + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16);
             }
         }
     }
@@ -1605,7 +1607,8 @@ __global__ __launch_bounds__(kThreads + kWave * NLW) void kda_inter_ws_kernel(Pr
             if (item < NSI) {
                 const int m = item % NRT, nn = item / NRT;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16] = S[i][r];
+                for (int r = 0; r < 4; ++r)  // non-temporal: read by no later step of this call
+                __builtin_nontemporal_store(S[i][r], dst + size_t(kTile * m + 4 * grp + r) * DV + jb + kTile * nn + l16);
             }
         }
     }

@@ -238,8 +238,6 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
     constexpr int DKP = DK + DK / 4;                    // padded row of one vector
     constexpr int EPU = 16 / int(sizeof(T));            // values of T per 16-byte unit
     constexpr int KU = DK / EPU, GU = DK / 4;           // 16-byte units of k (and q), of g
-    constexpr int UT = KU * (OUT ? 2 : 1) + GU;         // units per token
-    constexpr int ITER = (kWaveKG * UT + kWave - 1) / kWave;
     __shared__ __align__(16) float sv[kWavePB][kWaveKG][NVEC][DKP];
 
     const int wv = blockIdx.x * kWavePB + int(threadIdx.x / kWave);

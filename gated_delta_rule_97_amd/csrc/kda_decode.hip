@@ -213,7 +213,10 @@ constexpr int wave_columns() { return DV < 32 ? DV : 32; }
 // per element) and each lane reads its rows from there: read by every lane
 // straight from memory they would cost one load per 16-byte unit per lane,
 // and eight lanes share each row group.  The region belongs to one wave, and
-// a wave's LDS accesses complete in order, so no barrier is needed.
+// a wave's LDS accesses complete in order, so no workgroup barrier is needed;
+// wave_lds_sync() marks each point where lanes start reading what other lanes
+// wrote, or overwrite what other lanes read, so that the compiler keeps every
+// LDS access on its side of that point.
 constexpr int kWaveKG = 4;   // tokens staged at once
 constexpr int kWavePB = 4;   // waves per workgroup
 
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
                                                          16 * (j - (WQ ? 2 : 1) * KU);
             raw[it] = *reinterpret_cast<const u32x4 *>(src);
         }
+        wave_lds_sync();  // the previous group's reads of the region are behind
 #pragma unroll
         for (int it = 0; it < ITx; ++it) {
             const int u = lane + kWave * it;
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
                 }
             }
         }
+        wave_lds_sync();  // the group is staged
     };
 
     if constexpr (MODE == kCommitVerify) {
@@ -320,6 +325,7 @@ __global__ __launch_bounds__(kWavePB * kWave, 4) void kda_decode_wave_kernel(
         static_assert(NVEC == 3 && CW <= DKP, "the q slot of the staging region holds u");
         for (int t0 = 0; t0 < np; t0 += kWaveKG) {
             const int nt = min(kWaveKG, np - t0);
+            wave_lds_sync();  // the previous group's reads of u are behind
             // u of the wave's CW columns, staged in the (here unused) q slot
             if (lane < CG * nt) {
                 const int tt = lane / CG, c4 = lane - tt * CG;

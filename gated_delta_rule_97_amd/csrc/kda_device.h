@@ -29,6 +29,17 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kTile = 16;  // MFMA tile edge, and the 16-token decay tile
 
+// Lanes of one wave that exchange values through LDS with no workgroup
+// barrier: a wave's LDS accesses execute in program order, and this point
+// (wavefront-scope release and acquire around a wave barrier) keeps the
+// compiler from moving any of the wave's memory accesses across it.  It
+// emits no instruction that waits.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
 

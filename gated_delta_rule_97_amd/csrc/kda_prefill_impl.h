@@ -769,8 +769,10 @@ __global__ __launch_bounds__(kIThreads) void kda_intra_kernel(PrefillArgs a) {
                         *reinterpret_cast<floatx4 *>(t + i) = floatx4{X[i], X[i + 1], X[i + 2], X[i + 3]};
                 }
             }
-            // off-diagonal blocks of column Jw, top to bottom
+            // off-diagonal blocks of column Jw, top to bottom (they read the
+            // diagonal blocks other lanes of this wave wrote)
             if constexpr (NT > 1) {
+                wave_lds_sync();
                 if (Jw == 0) inverse_column<0, NT, A_LD, Y_LD>(sA, sL, sY, grp, l16);
                 if constexpr (NT > 2) if (Jw == 1) inverse_column<1, NT, A_LD, Y_LD>(sA, sL, sY, grp, l16);
                 if constexpr (NT > 3) if (Jw == 2) inverse_column<2, NT, A_LD, Y_LD>(sA, sL, sY, grp, l16);

@@ -221,6 +221,21 @@ def _ptr(t, dtype=None, name="tensor"):
     return t.data_ptr()
 
 
+def _shapes(*checks):
+    """Every given tensor has the shape the sizes passed to the library
+    imply: (tensor or None, expected shape, name); a None entry in the
+    expected shape matches any extent.  Checked before anything is launched,
+    so a mismatched tensor is an error here rather than an out-of-bounds
+    access on the device."""
+    for t, shape, name in checks:
+        if t is None:
+            continue
+        got = tuple(t.shape)
+        if len(got) != len(shape) or any(e is not None and g != e for g, e in zip(got, shape)):
+            want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+            raise ValueError(f"{name} has shape {list(got)}, expected {want}")
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -254,6 +269,9 @@ def chunk_prefill(q, k, v, g, beta, h0=None, cu_seqlens=None, *, chunk_size=64, 
     dv = v.shape[-1]
     dt = _dtype_code(q)
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    _shapes((k, (B, T, H, dk), "k"), (v, (B, T, H, dv), "v"), (g, (B, T, H, dk), "g"), (beta, (B, T, H), "beta"),
+            (h0, (N, H, dk, dv), "h0"), (o, (B, T, H, dv), "o"), (ht, (N, H, dk, dv), "ht"),
+            (ckpt, (None, H, dk, dv), "ckpt"))
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
     if ht is None and output_final_state:
@@ -297,6 +315,8 @@ def decode_step(q, k, v, g, beta, state, o=None, *, flags=0, stream=None):
     N, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
+    _shapes((k, (N, H, dk), "k"), (v, (N, H, dv), "v"), (g, (N, H, dk), "g"), (beta, (N, H), "beta"),
+            (state, (N, H, dk, dv), "state"), (o, (N, H, dv), "o"))
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     st = kda_decode_step(_ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
@@ -318,6 +338,8 @@ def decode_verify(q, k, v, g, beta, state, o=None, *, keep_u=False, u=None, flag
     N, K, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
+    _shapes((k, (N, K, H, dk), "k"), (v, (N, K, H, dv), "v"), (g, (N, K, H, dk), "g"), (beta, (N, K, H), "beta"),
+            (state, (N, H, dk, dv), "state"), (o, (N, K, H, dv), "o"), (u, (N, K, H, dv), "u"))
     if o is None:
         o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
     keep = keep_u or u is not None
@@ -346,17 +368,21 @@ def decode_commit_verify(prev, q, k, v, g, beta, state, o=None, *, keep_u=True, 
     N, K, H, dk = q.shape
     dv = state.shape[-1]
     dt = _dtype_code(q)
-    if o is None:
-        o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
-    keep = keep_u or u is not None
-    if keep and u is None:
-        u = torch.empty((N, K, H, dv), dtype=torch.float32, device=q.device)
     if prev is None:
         pk = pg = pu = pa = None
         Kp = 0
     else:
         pk, pg, pu, pa = prev
         Kp = pk.shape[1]
+    _shapes((k, (N, K, H, dk), "k"), (v, (N, K, H, dv), "v"), (g, (N, K, H, dk), "g"), (beta, (N, K, H), "beta"),
+            (state, (N, H, dk, dv), "state"), (o, (N, K, H, dv), "o"), (u, (N, K, H, dv), "u"),
+            (pk, (N, Kp, H, dk), "prev k"), (pg, (N, Kp, H, dk), "prev g"), (pu, (N, Kp, H, dv), "prev u"),
+            (pa, (N,), "n_accept"))
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=q.dtype, device=q.device)
+    keep = keep_u or u is not None
+    if keep and u is None:
+        u = torch.empty((N, K, H, dv), dtype=torch.float32, device=q.device)
     st = kda_decode_commit_verify(_ptr(pk, q.dtype, "prev k"), _ptr(pg, torch.float32, "prev g"),
                                   _ptr(pu, torch.float32, "prev u"), _ptr(pa, torch.int32, "n_accept"), Kp,
                                   _ptr(q, q.dtype, "q"), _ptr(k, q.dtype, "k"), _ptr(v, q.dtype, "v"),
@@ -379,6 +405,10 @@ def decode_commit(k, v, g, beta, n_accept, state, *, u=None, flags=0, stream=Non
     N, K, H, dk = k.shape
     dv = state.shape[-1]
     dt = _dtype_code(k)
+    _shapes((g, (N, K, H, dk), "g"), (n_accept, (N,), "n_accept"), (state, (N, H, dk, dv), "state"),
+            (u, (N, K, H, dv), "u"))
+    if u is None:
+        _shapes((v, (N, K, H, dv), "v"), (beta, (N, K, H), "beta"))
     if u is not None:
         st = kda_decode_commit_kept(_ptr(k, k.dtype, "k"), _ptr(g, torch.float32, "g"), _ptr(u, torch.float32, "u"),
                                     _ptr(n_accept, torch.int32, "n_accept"), _ptr(state, torch.float32, "state"),

@@ -373,3 +373,59 @@ def test_noalloc_limit_matches_the_workspace_size():
     assert kda.kda_chunk_prefill_workspace_size(1, 2048, 32, 128, 128, 1, 64, BF16) <= lim
     assert kda.kda_chunk_prefill_workspace_size(1, 4096, 32, 128, 128, 1, 64, BF16) > lim
 
+
+
+# The Python binding checks every tensor against the sizes it passes to the
+# library before anything reaches the device (host tensors suffice: the shape
+# check comes first, so a mismatch raises ValueError, never a device call).
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float32)
+
+
+def test_binding_rejects_mismatched_prefill_tensors():
+    import torch
+    B, T, H, dk, dv = 1, 70, 2, 64, 32
+    q = _t(B, T, H, dk, dtype=torch.bfloat16)
+    good = dict(k=_t(B, T, H, dk, dtype=torch.bfloat16), v=_t(B, T, H, dv, dtype=torch.bfloat16),
+                g=_t(B, T, H, dk), beta=_t(B, T, H), h0=_t(B, H, dk, dv))
+    bad = [("k", _t(B, T - 1, H, dk, dtype=torch.bfloat16)), ("g", _t(B, T, H, dv)), ("beta", _t(B, T, H, 1)),
+           ("h0", _t(B, H, dv, dk))]
+    for name, t in bad:
+        a = dict(good, **{name: t})
+        with pytest.raises(ValueError, match=f"^{name} has shape"):
+            kda.chunk_prefill(q, a["k"], a["v"], a["g"], a["beta"], a["h0"])
+    for name, t in [("o", _t(B, T, H, dk, dtype=torch.bfloat16)), ("ht", _t(2, H, dk, dv)),
+                    ("ckpt", _t(3, H, dv, dk))]:
+        with pytest.raises(ValueError, match=f"^{name} has shape"):
+            kda.chunk_prefill(q, *good.values(), **{name: t}, **({"ckpt_stride": 64} if name == "ckpt" else {}))
+
+
+def test_binding_rejects_mismatched_decode_tensors():
+    import torch
+    N, K, H, dk, dv = 3, 4, 2, 64, 32
+    bf = torch.bfloat16
+    q1, k1, v1 = _t(N, H, dk, dtype=bf), _t(N, H, dk, dtype=bf), _t(N, H, dv, dtype=bf)
+    st = _t(N, H, dk, dv)
+    with pytest.raises(ValueError, match="^state has shape"):
+        kda.decode_step(q1, k1, v1, _t(N, H, dk), _t(N, H), _t(N, H, dv, dk))
+    with pytest.raises(ValueError, match="^beta has shape"):
+        kda.decode_step(q1, k1, v1, _t(N, H, dk), _t(N, 1), st)
+    q, k, v, g, b = _t(N, K, H, dk, dtype=bf), _t(N, K, H, dk, dtype=bf), _t(N, K, H, dv, dtype=bf), \
+        _t(N, K, H, dk), _t(N, K, H)
+    with pytest.raises(ValueError, match="^v has shape"):
+        kda.decode_verify(q, k, _t(N, K - 1, H, dv, dtype=bf), g, b, st)
+    with pytest.raises(ValueError, match="^u has shape"):
+        kda.decode_verify(q, k, v, g, b, st, u=_t(N, K, H, dk))
+    acc = torch.zeros(N, dtype=torch.int32)
+    with pytest.raises(ValueError, match="^n_accept has shape"):
+        kda.decode_commit(k, v, g, b, torch.zeros(N + 1, dtype=torch.int32), st)
+    with pytest.raises(ValueError, match="^u has shape"):
+        kda.decode_commit(k, None, g, None, acc, st, u=_t(N, K + 1, H, dv))
+    prev = (k, g, _t(N, K, H, dv), acc)
+    with pytest.raises(ValueError, match="^prev u has shape"):
+        kda.decode_commit_verify((k, g, _t(N, K, H, dk), acc), q, k, v, g, b, st)
+    with pytest.raises(ValueError, match="^prev g has shape"):
+        kda.decode_commit_verify((k, _t(N, K - 1, H, dk), prev[2], acc), q, k, v, g, b, st)
+    with pytest.raises(ValueError, match="^o has shape"):
+        kda.decode_commit_verify(prev, q, k, v, g, b, st, o=_t(N, K, H, dk, dtype=bf))
